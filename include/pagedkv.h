@@ -1,0 +1,290 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv: a block-paged KV cache and PagedAttention
+ * decode for AMD Instinct MI355X (gfx950).
+ *
+ * Sources.  The method is the one described on these pages:
+ *   [P5] "PagedAttention por dentro: bloques, tabla de paginas, eviccion y el
+ *        estado del arte del KV cache en 2026" (blog.lo0.es/posts/
+ *        pagedattention-deep-dive): sections "El modelo de bloques",
+ *        "La tabla de paginas (block table)" with its figure, "El pool de
+ *        bloques", "Copy-on-write para sampling paralelo", "El kernel CUDA".
+ *   [P3] "Como funciona realmente vLLM (y por que lo necesitas)"
+ *        (alexanderzelada.com): "Que es el mecanismo de atencion",
+ *        "PagedAttention: la paginacion del sistema operativo aplicada a la
+ *        GPU" and its box "Que guarda cada entrada de la tabla de bloques".
+ *   [P1] "KV cache: la memoria de trabajo que sostiene la inferencia LLM"
+ *        (blog.lo0.es): "El mecanismo en si", "El precio", "Trucos para que
+ *        el cuaderno sea mas fino" (grouped-query attention).
+ *
+ * Conventions for every call:
+ *   - Calls return pkv_status (0 = PKV_OK) and never throw or abort.
+ *   - "device" pointers are HIP device memory owned by the caller; the
+ *     library only borrows them for the duration of the enqueued work.
+ *     "host" pointers are ordinary host memory, read or written before the
+ *     call returns.
+ *   - Device work is enqueued asynchronously on `stream` (0 = null stream);
+ *     the call returns once the kernels are launched.  Launch failures map
+ *     to PKV_ERR_HIP.
+ *   - The library never allocates device memory.
+ *
+ * ---------------------------------------------------------------------------
+ * Cache layout (the contract between paged_kv_write, paged_kv_copy_blocks and
+ * paged_attention_decode).
+ *
+ * A physical block holds the K and V of 16 consecutive tokens of one sequence
+ * for one layer [P5 "El modelo de bloques"].  k_cache and v_cache are two
+ * separate device buffers of num_blocks * num_kv_heads tiles each.  The tile
+ * of (block b, kv head h) starts at element (b * num_kv_heads + h) * 16 * D,
+ * where D = head_dim, so one block of all heads is one contiguous run of
+ * num_kv_heads * 16 * D elements.  Inside a tile, the element of token slot t
+ * (0..15) and channel d (0..D-1) sits at
+ *
+ *   K:  (d / 8) * 128 + t * 8 + (d % 8)
+ *       -- channel groups of 8: for each group, 16 tokens x 8 channels
+ *   V:  (d / 32) * 512 + (t / 4) * 128 + (d % 16) * 8 + ((d / 16) % 2) * 4 + (t % 4)
+ *       -- channel groups of 32: for each, 4 token quads, and inside a quad
+ *          16 channel columns, each holding 2 channels x 4 tokens
+ *
+ * (integer division).  D must be a multiple of 32.  Both orders are chosen
+ * so that one wavefront reads a whole tile as 64 lanes x 16 contiguous bytes
+ * per load instruction and each lane's bytes are already the operand
+ * fragment the gfx950 matrix instructions consume; the element type (fp32 or
+ * bf16) does not change the order.
+ *
+ * Token position p of sequence s (0-based) lives in physical block
+ * block_tables[s * max_blocks_per_seq + p / 16] at slot p % 16
+ * [P5 "La tabla de paginas": token 200 is found at table position 200/16 = 12].
+ * A flat slot index is block * 16 + slot.
+ *
+ * Other tensors (row-major):
+ *   q, out           [num_seqs][num_q_heads][D]; q in the cache dtype, out fp32
+ *   k_new, v_new     [num_tokens][num_kv_heads][D] in the cache dtype
+ *   slot_mapping     int64 [num_tokens]
+ *   block_tables     int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens     int32 [num_seqs]
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads): query heads
+ * share kv heads in contiguous groups [P1 "Trucos ...", grouped-query
+ * attention].
+ * ---------------------------------------------------------------------------
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_BLOCK_SIZE 16
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = 1,     /* bad argument, id out of range, double free, ... */
+  PKV_ERR_OOM = 2,         /* not enough free blocks (state left unchanged) */
+  PKV_ERR_UNSUPPORTED = 3, /* head_dim / dtype / group size without a kernel */
+  PKV_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} pkv_status;
+
+typedef enum pkv_dtype {
+  PKV_F32 = 0,
+  PKV_BF16 = 1
+} pkv_dtype;
+
+typedef struct pkv_pool pkv_pool;
+
+typedef struct pkv_stats {
+  int32_t num_blocks;
+  int32_t num_free;       /* refcount 0, on the free list */
+  int32_t num_used;       /* refcount >= 1 */
+  int32_t num_shared;     /* refcount >= 2 */
+  int64_t num_refs;       /* sum of refcounts = table entries pointing into the pool */
+  double usage_percent;   /* 100 * num_used / num_blocks */
+} pkv_stats;
+
+/* Human-readable name of a status code (static storage). */
+const char* pkv_status_string(pkv_status status);
+
+/* ===== Host block pool ======================================================
+ * [P5 "El pool de bloques"]: one global pool of fixed-size blocks, sized once
+ * when the engine starts; allocation is O(1) and a finished sequence returns
+ * its blocks, which another sequence may take at the next step [P5 figure in
+ * "La tabla de paginas"].  [P5 "Copy-on-write para sampling paralelo"]:
+ * sequences share prefix blocks through their tables, with reference counts;
+ * a shared block is copied only when a sequence is about to modify it.
+ *
+ * The free list is a LIFO stack.  With init_order == NULL the first
+ * allocations return 0, 1, 2, ...; otherwise they return init_order[0],
+ * init_order[1], ... (init_order must be a permutation of 0..num_blocks-1).
+ * A block freed last is handed out first.  The pool is host memory owned by
+ * the library; it is not thread-safe (one caller at a time).
+ */
+/* block_size must be 16 (else PKV_ERR_UNSUPPORTED); num_blocks >= 1. */
+pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size,
+                           const int32_t* init_order /* host, nullable */,
+                           pkv_pool** out_pool /* host */);
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* Pop n ids (refcount 1 each) into out_ids[0..n).  All or nothing: fewer
+ * than n free blocks -> PKV_ERR_OOM with the pool unchanged.  n >= 0. */
+pkv_status kv_block_alloc(pkv_pool* pool, int32_t n, int32_t* out_ids /* host */);
+
+/* Add one reference to each id (a sequence forked, or a prefix reused).
+ * Any id out of range or free -> PKV_ERR_INVALID, pool unchanged. */
+pkv_status kv_block_share(pkv_pool* pool, int32_t n, const int32_t* ids /* host */);
+
+/* Drop one reference from each id; an id whose count reaches 0 is pushed on
+ * the free list (in array order).  Validated first: an id out of range, or
+ * more drops of one id than it has references -> PKV_ERR_INVALID, pool
+ * unchanged. */
+pkv_status kv_block_free(pkv_pool* pool, int32_t n, const int32_t* ids /* host */);
+
+/* Make block `id` private to the caller before a write [P5 copy-on-write].
+ * refcount 1: *out_id = id, *needs_copy = 0.  refcount > 1: pops a new id
+ * (refcount 1), drops one reference of `id`, *out_id = new id,
+ * *needs_copy = 1; the caller must copy id -> new id on the device
+ * (paged_kv_copy_blocks) before writing into it.  Free or out-of-range id
+ * -> PKV_ERR_INVALID; no free block -> PKV_ERR_OOM (pool unchanged). */
+pkv_status kv_block_cow(pkv_pool* pool, int32_t id, int32_t* out_id, int32_t* needs_copy);
+
+/* Current reference count of `id` (0 = free). */
+pkv_status kv_block_refcount(const pkv_pool* pool, int32_t id, int32_t* out_refcount);
+
+/* Pool occupancy counters. */
+pkv_status kv_pool_stats(const pkv_pool* pool, pkv_stats* out_stats);
+
+/* Snapshot of the free list, next id to be allocated first.  Writes
+ * min(capacity, num_free) ids and the full count to *out_n. */
+pkv_status kv_pool_free_list(const pkv_pool* pool, int32_t capacity, int32_t* out_ids,
+                             int32_t* out_n);
+
+/* ===== Slot planning for appended tokens (host) =============================
+ * [P5 "La tabla de paginas"]: when a sequence produces a token at position
+ * p (p = tokens already cached), it is written into the last block if that
+ * block still has room (p % 16 != 0); otherwise a block is taken from the
+ * global pool and appended to the table, and the token goes to its slot 0.
+ * [P5 copy-on-write]: if the last block is shared (refcount > 1), it is
+ * first replaced by a private copy.
+ *
+ * For s = 0..num_seqs-1 in order, and for each of its num_new[s] tokens
+ * (num_new == NULL means 1 each), with p = context_lens[s]:
+ *   p % 16 == 0           -> allocate a block, table[s][p/16] = it
+ *   refcount(table[s][p/16]) > 1 -> copy-on-write: table[s][p/16] = new id,
+ *                            the pair (old, new) is appended to cow_pairs
+ *   slot_mapping[k++] = table[s][p/16] * 16 + p % 16;  context_lens[s] = p + 1
+ * Every table entry written is also appended to table_updates as the pair
+ * (s * max_blocks_per_seq + p/16, id), for paged_block_table_update.
+ *
+ *   block_tables   host int32 [num_seqs][max_blocks_per_seq], updated in place
+ *   context_lens   host int32 [num_seqs], updated in place
+ *   slot_mapping   host int64 [slot_capacity]; receives sum(num_new) slots
+ *   table_updates  host int32 [update_capacity][2]
+ *   cow_pairs      host int32 [cow_capacity][2]  (src block, dst block)
+ * All or nothing: too few free blocks -> PKV_ERR_OOM; a position beyond
+ * max_blocks_per_seq * 16, a capacity too small, or a table entry that is
+ * not a live block -> PKV_ERR_INVALID; in both cases tables, lengths and pool
+ * are left unchanged.  num_seqs * max_blocks_per_seq must be < 2^31. */
+pkv_status paged_kv_append_slots(pkv_pool* pool, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                 int32_t* block_tables, int32_t* context_lens,
+                                 const int32_t* num_new, int64_t* slot_mapping,
+                                 int64_t slot_capacity, int32_t* table_updates,
+                                 int32_t update_capacity, int32_t* num_updates,
+                                 int32_t* cow_pairs, int32_t cow_capacity, int32_t* num_cow);
+
+/* ===== Device calls ========================================================= */
+
+/* The block tables live in device memory next to the cache, not on the host
+ * [P5 "La tabla de paginas": a host-side table would cost a PCIe round trip
+ * per decode step].  Applies `updates` (device int32 [num_updates][2] of
+ * (flat index, block id)) to block_tables (device int32 [table_elems]).
+ * Pairs whose index is outside [0, table_elems) are skipped. */
+pkv_status paged_block_table_update(int32_t* block_tables, int64_t table_elems,
+                                    const int32_t* updates, int32_t num_updates,
+                                    hipStream_t stream);
+
+/* Store the K and V of new tokens into the cache through a slot mapping
+ * [P1 "El mecanismo en si": the cache keeps K and V of every processed token;
+ * P5: the new token's K,V go to its slot].  For every i < num_tokens with
+ * 0 <= slot_mapping[i] < num_blocks * 16, the row k_new[i][h][:] (and
+ * v_new[i][h][:]) becomes token slot (slot % 16) of tile (slot / 16, h),
+ * in the layout above.  Negative slots are padding and skipped; slots at or
+ * beyond num_blocks * 16 are skipped as well (and reported as
+ * PKV_ERR_INVALID when the environment variable PKV_DEBUG=1, which also
+ * checks uniqueness; that check synchronizes the stream).  Slots must be
+ * unique: two rows for one slot race.  Bytes are copied unchanged.
+ * k_new, v_new, slot_mapping, k_cache, v_cache: device. */
+pkv_status paged_kv_write(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                          void* k_cache, void* v_cache, int32_t num_tokens,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                          pkv_dtype dtype, hipStream_t stream);
+
+/* Copy whole blocks (all kv heads, all 16 slots, K and V) for copy-on-write
+ * [P5 "Copy-on-write para sampling paralelo": only the last affected block
+ * is copied].  pairs: device int32 [num_pairs][2] = (src block, dst block).
+ * Pairs with an id outside [0, num_blocks) are skipped.  Destinations must
+ * be distinct and must not be sources of other pairs in the same call.
+ * Enqueue before paged_kv_write on the same stream so the copy sees the
+ * block as it was before the new tokens arrive. */
+pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
+                                int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t num_blocks, pkv_dtype dtype, hipStream_t stream);
+
+/* Bytes of scratch paged_attention_decode needs for these sizes (0 when
+ * every context fits one partition).  partition_size 0 = default (512). */
+size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                      int32_t max_context_len, int32_t partition_size);
+
+/* Decode attention: one query token per sequence attends over its whole
+ * context, gathering K and V block by block through its table and never
+ * copying them into a contiguous buffer [P3 "PagedAttention ..." ; P5 "El
+ * kernel CUDA": block-aligned chunks, each located through the table].  The
+ * mathematics is plain attention [P3 "Que es el mecanismo de atencion";
+ * P1 "El mecanismo en si"]: for query head h of sequence s, with
+ * kvh = h / (num_q_heads / num_kv_heads) and L = context_lens[s],
+ *   score_t = scale * sum_d q[s][h][d] * K_t[d],   t = 0..L-1
+ *   w_t     = exp(score_t - max score) / sum_j exp(score_j - max score)
+ *   out[s][h][:] = sum_t w_t * V_t[:]
+ * (L = 0 gives a zero row).  Contexts longer than partition_size tokens are
+ * split into partitions whose partial results (running max, sum of weights,
+ * unnormalised output) are merged by a log-sum-exp reduction; the result
+ * does not depend on the partitioning beyond rounding.
+ *
+ *   q, k_cache, v_cache, block_tables, context_lens, workspace: device, read
+ *   out: device fp32, written
+ *   max_context_len: host-side upper bound of context_lens (sizes the grid)
+ *   partition_size: tokens per partition, a multiple of 32; 0 = 512
+ *   workspace_bytes >= paged_attention_workspace_size(...) (may be NULL/0
+ *   when that is 0)
+ * Errors: num_q_heads % num_kv_heads != 0, non-positive sizes, a
+ * partition_size that is not a multiple of 32, a short workspace ->
+ * PKV_ERR_INVALID.  head_dim not in {64, 128}, or more than 16 query heads
+ * per kv head with bf16 -> PKV_ERR_UNSUPPORTED.  On the device, a sequence
+ * whose length exceeds max_context_len or max_blocks_per_seq * 16, or whose
+ * table holds an id outside [0, num_blocks), gets NaN in all its output rows
+ * instead of reading out of bounds.  Table entries at or beyond
+ * ceil(L / 16) are never read. */
+pkv_status paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  float scale, int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, pkv_dtype kv_dtype, float* out,
+                                  hipStream_t stream);
+
+/* ===== Measurement ==========================================================
+ * While profiling is on, every paged_attention_decode call records a pair of
+ * HIP events around its main (block-walking) kernel on the caller's stream.
+ * pkv_profile_end synchronizes on the recorded events and returns how many
+ * launches were timed and their total duration in milliseconds.  At most
+ * 65536 launches are kept per session.  Not thread-safe. */
+pkv_status pkv_profile_begin(void);
+pkv_status pkv_profile_end(int32_t* num_launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

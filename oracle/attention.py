@@ -1,0 +1,82 @@
+"""Decode attention, by its definition, in float64.
+
+"Como funciona realmente vLLM" (alexanderzelada.com), "Que es el mecanismo
+de atencion": the current token's query is compared with the keys of the
+previous tokens, a softmax turns the affinities into weights that add up to
+100 %, and the output is the weighted sum of the value vectors.  "KV cache:
+la memoria de trabajo ...", "El mecanismo en si": to predict token N only
+the new Q and the cached K, V of the earlier tokens are needed.  "Trucos
+para que el cuaderno sea mas fino": with grouped-query attention the query
+heads share K, V in groups (Llama 3 8B: 32 query heads in groups of 4).
+"PagedAttention: ..." (same lesson): paging changes how the cache is
+addressed, not the mathematics of attention.
+
+Readings where the pages are silent: the softmax is scaled by ``scale``
+(1/sqrt(head_dim) in every workload) and stabilised by subtracting the
+maximum (equal in exact arithmetic); query head h uses kv head
+h // (num_q_heads // num_kv_heads); there is no mask beyond the context
+length and no positional term; an empty context gives a zero row.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .cache import CacheModel, widen
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """One query vector q [D] over keys k [L][D] and values v [L][D], float64."""
+    if k.shape[0] == 0:
+        return np.zeros(v.shape[1], dtype=np.float64)
+    s = scale * (k @ q)
+    e = np.exp(s - s.max())
+    w = e / e.sum()
+    return w @ v
+
+
+def decode(q_stored: np.ndarray, cache: CacheModel, tables: np.ndarray, lens: np.ndarray,
+           num_q_heads: int, num_kv_heads: int, scale: float, seqs=None) -> np.ndarray:
+    """out [B][Hq][D] float64 for the sequences in ``seqs`` (default all;
+    rows of other sequences stay zero).  Each sequence's K/V are gathered
+    block by block through its table."""
+    B = q_stored.shape[0]
+    D = q_stored.shape[2]
+    group = num_q_heads // num_kv_heads
+    q = widen(q_stored, cache.dtype)
+    out = np.zeros((B, num_q_heads, D), dtype=np.float64)
+    for b in (range(B) if seqs is None else seqs):
+        L = int(lens[b])
+        for kvh in range(num_kv_heads):
+            k, v = cache.gather(tables[b], L, kvh)
+            for h in range(kvh * group, (kvh + 1) * group):
+                out[b, h] = attend(q[b, h], k, v, scale)
+    return out
+
+
+def partial_state(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
+    """Partial softmax state of one chunk of tokens: (m, l, o) with
+    m = max score, l = sum exp(score - m), o = sum exp(score - m) * v."""
+    s = scale * (k @ q)
+    m = s.max()
+    e = np.exp(s - m)
+    return m, e.sum(), e @ v
+
+
+def merge_states(states):
+    """Log-sum-exp merge of partial states into the normalised output:
+    m = max m_p, l = sum l_p e^(m_p - m), out = sum o_p e^(m_p - m) / l."""
+    m = max(st[0] for st in states)
+    l = sum(st[1] * np.exp(st[0] - m) for st in states)
+    o = sum(st[2] * np.exp(st[0] - m) for st in states)
+    return o / l
+
+
+def attend_partitioned(q, k, v, scale, partition_tokens: int) -> np.ndarray:
+    """Same result as ``attend`` computed as independent partitions of
+    ``partition_tokens`` tokens merged by ``merge_states``."""
+    L = k.shape[0]
+    if L == 0:
+        return np.zeros(v.shape[1], dtype=np.float64)
+    states = [partial_state(q, k[a:a + partition_tokens], v[a:a + partition_tokens], scale)
+              for a in range(0, L, partition_tokens)]
+    return merge_states(states)

@@ -1,0 +1,80 @@
+"""The cache tensors on the host: write, block copy, gather.
+
+"KV cache: la memoria de trabajo ..." (blog.lo0.es), "El mecanismo en si":
+the cache keeps the K and V of every token already processed, in every
+layer.  "PagedAttention por dentro", "La tabla de paginas": a token is
+found through its sequence's block table; "Copy-on-write para sampling
+paralelo": a whole block is copied when a shared block diverges.
+"Como funciona realmente vLLM", "PagedAttention: ...": the kernel reads the
+scattered blocks through the table without copying them into a contiguous
+buffer -- the gather below exists only to state the result, it is not a
+step of the GPU path.
+
+Values are kept exactly as stored (float32, or bf16 as raw uint16 bits);
+gathers widen them exactly to float64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .layout import BLOCK_SIZE, offset_tables
+
+
+def widen(stored: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values -> float64, exactly (bf16 bits shift into float32)."""
+    if dtype == "f32":
+        return np.asarray(stored, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        f = (np.asarray(stored, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+        return f.astype(np.float64)
+    raise ValueError(dtype)
+
+
+class CacheModel:
+    """k, v: arrays [num_blocks][num_kv_heads][16 * D] of stored elements."""
+
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
+                 fill=None):
+        self.num_blocks, self.num_kv_heads, self.head_dim, self.dtype = (
+            num_blocks, num_kv_heads, head_dim, dtype)
+        store = np.float32 if dtype == "f32" else np.uint16
+        shape = (num_blocks, num_kv_heads, BLOCK_SIZE * head_dim)
+        self.k = np.zeros(shape, dtype=store)
+        self.v = np.zeros(shape, dtype=store)
+        if fill is not None:
+            self.k[...] = fill
+            self.v[...] = fill
+        self.koff, self.voff = offset_tables(head_dim)
+
+    def write(self, k_new: np.ndarray, v_new: np.ndarray, slots: np.ndarray):
+        """k_new, v_new [T][Hkv][D] stored values; slots int64 [T].  A slot
+        outside [0, num_blocks * 16) is skipped (negative = padding)."""
+        slots = np.asarray(slots, dtype=np.int64)
+        keep = (slots >= 0) & (slots < self.num_blocks * BLOCK_SIZE)
+        idx = np.nonzero(keep)[0]
+        blk = slots[idx] // BLOCK_SIZE
+        t = slots[idx] % BLOCK_SIZE
+        heads = np.arange(self.num_kv_heads)
+        # self.k[blk, h, koff[t, d]] = k_new[i, h, d]  for all kept i, all h, d
+        self.k[blk[:, None, None], heads[None, :, None], self.koff[t][:, None, :]] = k_new[idx]
+        self.v[blk[:, None, None], heads[None, :, None], self.voff[t][:, None, :]] = v_new[idx]
+
+    def copy_blocks(self, pairs):
+        """Copy whole blocks (every head and slot, K and V), src -> dst, in order."""
+        for src, dst in pairs:
+            if 0 <= src < self.num_blocks and 0 <= dst < self.num_blocks:
+                self.k[dst] = self.k[src]
+                self.v[dst] = self.v[src]
+
+    def gather(self, table_row, length: int, kv_head: int):
+        """K and V of tokens 0..length-1 of one sequence and kv head, as
+        float64 [length][D], read block by block through the table."""
+        t = np.arange(length)
+        blk = np.asarray(table_row, dtype=np.int64)[t // BLOCK_SIZE]
+        slot = t % BLOCK_SIZE
+        k = self.k[blk[:, None], kv_head, self.koff[slot]]
+        v = self.v[blk[:, None], kv_head, self.voff[slot]]
+        return widen(k, self.dtype), widen(v, self.dtype)
+
+    def stored_bytes(self):
+        return self.k.tobytes(), self.v.tobytes()

@@ -1,0 +1,120 @@
+"""Plants plausible mistakes in the oracle (on the CPU, by monkeypatching)
+and checks that at least one pin in test_oracle_pins fails for each."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention, layout, pool, slots
+from tests import test_oracle_pins as pins
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except (AssertionError, Exception):
+        return True
+    return False
+
+
+def test_mutation_gqa_head_map(monkeypatch):
+    def bad_decode(q_stored, cache, tables, lens, num_q_heads, num_kv_heads, scale, seqs=None):
+        B, D = q_stored.shape[0], q_stored.shape[2]
+        q = attention.widen(q_stored, cache.dtype)
+        out = np.zeros((B, num_q_heads, D))
+        for b in range(B):
+            for h in range(num_q_heads):
+                k, v = cache.gather(tables[b], int(lens[b]), h % num_kv_heads)   # wrong map
+                out[b, h] = attention.attend(q[b, h], k, v, scale)
+        return out
+    monkeypatch.setattr(attention, "decode", bad_decode)
+    assert _fails(pins.test_paged_equals_contiguous_sdpa, 8, 2, "f32")
+
+
+def test_mutation_dropped_scale(monkeypatch):
+    orig = attention.attend
+    monkeypatch.setattr(attention, "attend", lambda q, k, v, scale: orig(q, k, v, 1.0))
+    assert _fails(pins.test_paged_equals_contiguous_sdpa, 4, 4, "f32")
+    assert _fails(pins.test_closed_forms)
+
+
+def test_mutation_unnormalised_weights(monkeypatch):
+    def bad(q, k, v, scale):
+        if k.shape[0] == 0:
+            return np.zeros(v.shape[1])
+        s = scale * (k @ q)
+        return np.exp(s - s.max()) @ v
+    monkeypatch.setattr(attention, "attend", bad)
+    assert _fails(pins.test_closed_forms)
+
+
+def test_mutation_lse_merge(monkeypatch):
+    def bad_merge(states):
+        m = max(st[0] for st in states)
+        l = sum(st[1] * np.exp(st[0] - m) for st in states)
+        o = sum(st[2] for st in states)                # forgot the rescale
+        return o / l
+    monkeypatch.setattr(attention, "merge_states", bad_merge)
+    assert _fails(pins.test_partitioned_lse_equals_single_pass, 2000, 512)
+
+
+def test_mutation_layout_transposed(monkeypatch):
+    monkeypatch.setattr(layout, "k_offset", lambda t, d: t * 128 + d)
+    assert _fails(pins.test_layout_golden_offsets)
+
+
+def test_mutation_layout_v_swapped_halves(monkeypatch):
+    monkeypatch.setattr(layout, "v_offset", lambda t, d: (d // 32) * 512 + (t // 4) * 128
+                        + (d % 16) * 8 + ((d // 16) % 2) + (t % 4) * 2)
+    assert _fails(pins.test_layout_golden_offsets)
+
+
+def test_mutation_slot_off_by_one(monkeypatch):
+    monkeypatch.setattr(slots, "slot_of", lambda row, p: int(row[p // 16]) * 16 + (p + 1) % 16)
+    assert _fails(pins.test_token_200_position_12)
+
+
+def test_mutation_alloc_on_wrong_boundary(monkeypatch):
+    orig = slots.plan_append
+
+    def bad_plan(pool_, tables, lens, num_new=None):
+        # allocates one token late: p % 16 == 1 instead of 0
+        lens[...] = lens - 0
+        B = tables.shape[0]
+        num_new = np.ones(B, np.int64) if num_new is None else num_new
+        out = []
+        for s in range(B):
+            for _ in range(int(num_new[s])):
+                p = int(lens[s])
+                if p % 16 == 1 or p == 0:
+                    (blk,) = pool_.alloc(1)
+                    tables[s, (p + 15) // 16 if p else 0] = blk
+                out.append(0)
+                lens[s] = p + 1
+        return np.array(out), [], []
+    monkeypatch.setattr(slots, "plan_append", bad_plan)
+    assert _fails(pins.test_session_273_blocks)
+    monkeypatch.setattr(slots, "plan_append", orig)
+
+
+def test_mutation_fifo_free_list(monkeypatch):
+    orig_free = pool.PoolModel.free
+
+    def fifo_free(self, ids):
+        orig_free(self, ids)
+        # move freed ids to the bottom of the stack (FIFO reuse)
+        freed = [i for i in ids if self.refcount[i] == 0]
+        self._free = freed + [i for i in self._free if i not in freed]
+    monkeypatch.setattr(pool.PoolModel, "free", fifo_free)
+    assert _fails(pins.test_figure_pool_and_reuse)
+
+
+def test_mutation_cow_copies_always(monkeypatch):
+    def bad_cow(self, i):
+        self._check_live(i)
+        new = self._free.pop()
+        self.refcount[new] = 1
+        self.refcount[i] -= 1
+        return new, True
+    monkeypatch.setattr(pool.PoolModel, "cow", bad_cow)
+    assert _fails(pins.test_cow_beam_fork)
