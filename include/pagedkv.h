@@ -182,9 +182,10 @@ pkv_status kv_pool_free_list(const pkv_pool* pool, int32_t capacity, int32_t* ou
  *   slot_mapping   host int64 [slot_capacity]; receives sum(num_new) slots
  *   table_updates  host int32 [update_capacity][2]
  *   cow_pairs      host int32 [cow_capacity][2]  (src block, dst block)
- * All or nothing: too few free blocks -> PKV_ERR_OOM; a position beyond
- * max_blocks_per_seq * 16, a capacity too small, or a table entry that is
- * not a live block -> PKV_ERR_INVALID; in both cases tables, lengths and pool
+ * All or nothing: a position beyond max_blocks_per_seq * 16, a negative
+ * count, a capacity too small, or a partly filled last block that is not a
+ * live block -> PKV_ERR_INVALID (checked for all sequences first); otherwise
+ * too few free blocks -> PKV_ERR_OOM; in both cases tables, lengths and pool
  * are left unchanged.  num_seqs * max_blocks_per_seq must be < 2^31. */
 pkv_status paged_kv_append_slots(pkv_pool* pool, int32_t num_seqs, int32_t max_blocks_per_seq,
                                  int32_t* block_tables, int32_t* context_lens,
@@ -279,7 +280,8 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
  * HIP events around its main (block-walking) kernel on the caller's stream.
  * pkv_profile_end synchronizes on the recorded events and returns how many
  * launches were timed and their total duration in milliseconds.  At most
- * 65536 launches are kept per session.  Not thread-safe. */
+ * 8192 launches are kept per session (later ones are not timed).  Not
+ * thread-safe. */
 pkv_status pkv_profile_begin(void);
 pkv_status pkv_profile_end(int32_t* num_launches, double* total_ms);
 

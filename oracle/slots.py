@@ -38,10 +38,22 @@ def plan_append(pool: PoolModel, tables: np.ndarray, lens: np.ndarray, num_new=N
     (updated in place); num_new: tokens appended per sequence (default 1).
     Returns (slots int64 [sum num_new], updates [(flat index, id)],
     cow_pairs [(src, dst)]).  All or nothing: on error, pool, tables and
-    lens are restored and the PoolError is re-raised."""
+    lens are restored and the PoolError is re-raised; "invalid" (a position
+    beyond the table, a dead table entry) takes precedence over "oom"."""
     B, max_blocks = tables.shape
     if num_new is None:
         num_new = np.ones(B, dtype=np.int64)
+    # Argument errors are reported before pool exhaustion: every sequence's
+    # new positions must fit its table, and a partly filled last block that
+    # receives tokens must be a live block.
+    for s in range(B):
+        add, p0 = int(num_new[s]), int(lens[s])
+        if add < 0 or p0 < 0 or p0 + add > max_blocks * BLOCK_SIZE:
+            raise PoolError("invalid", f"sequence {s}: positions beyond the table")
+        if add > 0 and p0 % BLOCK_SIZE != 0:
+            blk = int(tables[s, p0 // BLOCK_SIZE])
+            if not (0 <= blk < pool.num_blocks) or pool.refcount[blk] == 0:
+                raise PoolError("invalid", f"sequence {s}: table entry {blk} is not live")
     snap = pool.snapshot()
     tables_before = tables.copy()
     lens_before = lens.copy()

@@ -1,0 +1,270 @@
+"""ctypes binding of libpagedkv (include/pagedkv.h), same names as the C ABI.
+
+Argument marshalling only: host arrays are numpy, device buffers are torch
+CUDA tensors (their data pointers are passed through), streams default to
+torch's current stream.  A non-zero status raises PkvError.  The library
+must be built (``__graft_entry__.build()``); importing this module without
+it raises ImportError -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+_lib = C.CDLL(LIB_PATH)
+
+PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP = range(5)
+PKV_F32, PKV_BF16 = 0, 1
+BLOCK_SIZE = 16
+
+_i32p = C.POINTER(C.c_int32)
+_i64p = C.POINTER(C.c_int64)
+_vp = C.c_void_p
+
+
+class pkv_stats(C.Structure):
+    _fields_ = [("num_blocks", C.c_int32), ("num_free", C.c_int32), ("num_used", C.c_int32),
+                ("num_shared", C.c_int32), ("num_refs", C.c_int64), ("usage_percent", C.c_double)]
+
+
+_SIGS = {
+    "pkv_status_string": (C.c_char_p, [C.c_int]),
+    "pkv_pool_create": (C.c_int, [C.c_int32, C.c_int32, _i32p, C.POINTER(_vp)]),
+    "pkv_pool_destroy": (None, [_vp]),
+    "kv_block_alloc": (C.c_int, [_vp, C.c_int32, _i32p]),
+    "kv_block_share": (C.c_int, [_vp, C.c_int32, _i32p]),
+    "kv_block_free": (C.c_int, [_vp, C.c_int32, _i32p]),
+    "kv_block_cow": (C.c_int, [_vp, C.c_int32, _i32p, _i32p]),
+    "kv_block_refcount": (C.c_int, [_vp, C.c_int32, _i32p]),
+    "kv_pool_stats": (C.c_int, [_vp, C.POINTER(pkv_stats)]),
+    "kv_pool_free_list": (C.c_int, [_vp, C.c_int32, _i32p, _i32p]),
+    "paged_kv_append_slots": (C.c_int, [_vp, C.c_int32, C.c_int32, _i32p, _i32p, _i32p, _i64p,
+                                        C.c_int64, _i32p, C.c_int32, _i32p, _i32p, C.c_int32,
+                                        _i32p]),
+    "paged_block_table_update": (C.c_int, [_vp, C.c_int64, _vp, C.c_int32, _vp]),
+    "paged_kv_write": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32, C.c_int32,
+                                 C.c_int32, C.c_int, _vp]),
+    "paged_kv_copy_blocks": (C.c_int, [_vp, _vp, _vp, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                       C.c_int, _vp]),
+    "paged_attention_workspace_size": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                                    C.c_int32]),
+    "paged_attention_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32, C.c_int32,
+                                         C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_float,
+                                         C.c_int32, _vp, C.c_size_t, C.c_int, _vp, _vp]),
+    "pkv_profile_begin": (C.c_int, []),
+    "pkv_profile_end": (C.c_int, [_i32p, C.POINTER(C.c_double)]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.pkv_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+def _check(st: int, where: str):
+    if st != PKV_OK:
+        raise PkvError(st, where)
+
+
+def pkv_status_string(status: int) -> str:
+    return _lib.pkv_status_string(status).decode()
+
+
+def _i32(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(_i32p)
+
+
+# --------------------------------------------------------------------------- pool
+class Pool:
+    """Owns a pkv_pool handle."""
+
+    def __init__(self, handle):
+        self.handle = handle
+
+    def __del__(self):
+        h, self.handle = getattr(self, "handle", None), None
+        if h:
+            _lib.pkv_pool_destroy(h)
+
+
+def pkv_pool_create(num_blocks: int, block_size: int = BLOCK_SIZE, init_order=None) -> Pool:
+    h = _vp()
+    if init_order is None:
+        st = _lib.pkv_pool_create(num_blocks, block_size, None, C.byref(h))
+    else:
+        arr, ptr = _i32(init_order)
+        st = _lib.pkv_pool_create(num_blocks, block_size, ptr, C.byref(h))
+    _check(st, "pkv_pool_create")
+    return Pool(h)
+
+
+def kv_block_alloc(pool: Pool, n: int) -> np.ndarray:
+    out = np.empty(max(n, 0), dtype=np.int32)
+    _check(_lib.kv_block_alloc(pool.handle, n, out.ctypes.data_as(_i32p)), "kv_block_alloc")
+    return out
+
+
+def kv_block_share(pool: Pool, ids) -> None:
+    arr, ptr = _i32(ids)
+    _check(_lib.kv_block_share(pool.handle, arr.size, ptr), "kv_block_share")
+
+
+def kv_block_free(pool: Pool, ids) -> None:
+    arr, ptr = _i32(ids)
+    _check(_lib.kv_block_free(pool.handle, arr.size, ptr), "kv_block_free")
+
+
+def kv_block_cow(pool: Pool, block_id: int):
+    out, copy = C.c_int32(), C.c_int32()
+    _check(_lib.kv_block_cow(pool.handle, block_id, C.byref(out), C.byref(copy)), "kv_block_cow")
+    return out.value, bool(copy.value)
+
+
+def kv_block_refcount(pool: Pool, block_id: int) -> int:
+    out = C.c_int32()
+    _check(_lib.kv_block_refcount(pool.handle, block_id, C.byref(out)), "kv_block_refcount")
+    return out.value
+
+
+def kv_pool_stats(pool: Pool) -> dict:
+    s = pkv_stats()
+    _check(_lib.kv_pool_stats(pool.handle, C.byref(s)), "kv_pool_stats")
+    return {f: getattr(s, f) for f, _ in pkv_stats._fields_}
+
+
+def kv_pool_free_list(pool: Pool) -> np.ndarray:
+    n = C.c_int32()
+    _check(_lib.kv_pool_free_list(pool.handle, 0, None, C.byref(n)), "kv_pool_free_list")
+    out = np.empty(n.value, dtype=np.int32)
+    _check(_lib.kv_pool_free_list(pool.handle, n.value, out.ctypes.data_as(_i32p), C.byref(n)),
+           "kv_pool_free_list")
+    return out
+
+
+def paged_kv_append_slots(pool: Pool, block_tables: np.ndarray, context_lens: np.ndarray,
+                          num_new=None):
+    """block_tables int32 [B][max_blocks] and context_lens int32 [B] are
+    updated in place.  Returns (slot_mapping int64, table_updates int32 [n][2],
+    cow_pairs int32 [n][2])."""
+    assert block_tables.dtype == np.int32 and block_tables.flags.c_contiguous
+    assert context_lens.dtype == np.int32 and context_lens.flags.c_contiguous
+    B, mb = block_tables.shape
+    if num_new is None:
+        nn, nn_ptr, total = None, None, B
+    else:
+        nn, nn_ptr = _i32(num_new)
+        total = int(nn.sum())
+    upd_cap = total + B
+    slots = np.empty(max(total, 1), dtype=np.int64)
+    upd = np.empty((upd_cap, 2), dtype=np.int32)
+    cows = np.empty((max(B, 1), 2), dtype=np.int32)
+    nu, nc = C.c_int32(), C.c_int32()
+    st = _lib.paged_kv_append_slots(pool.handle, B, mb, block_tables.ctypes.data_as(_i32p),
+                                    context_lens.ctypes.data_as(_i32p), nn_ptr,
+                                    slots.ctypes.data_as(_i64p), total,
+                                    upd.ctypes.data_as(_i32p), upd_cap, C.byref(nu),
+                                    cows.ctypes.data_as(_i32p), B, C.byref(nc))
+    _check(st, "paged_kv_append_slots")
+    return slots[:total], upd[:nu.value], cows[:nc.value]
+
+
+# --------------------------------------------------------------------------- device calls
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t, name):
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    return t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return PKV_BF16
+    raise ValueError(f"unsupported cache dtype {t.dtype}")
+
+
+def paged_block_table_update(block_tables, updates, stream=None) -> None:
+    n = updates.shape[0]
+    if n == 0:
+        return
+    _check(_lib.paged_block_table_update(_dev(block_tables, "block_tables"), block_tables.numel(),
+                                         _dev(updates, "updates"), n, _stream(stream)),
+           "paged_block_table_update")
+
+
+def paged_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache, num_kv_heads: int,
+                   head_dim: int, num_blocks: int, stream=None) -> None:
+    n = slot_mapping.shape[0]
+    if n == 0:
+        return
+    _check(_lib.paged_kv_write(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                               _dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"),
+                               _dev(v_cache, "v_cache"), n, num_kv_heads, head_dim, num_blocks,
+                               _dtype_code(k_cache), _stream(stream)), "paged_kv_write")
+
+
+def paged_kv_copy_blocks(k_cache, v_cache, pairs, num_kv_heads: int, head_dim: int,
+                         num_blocks: int, stream=None) -> None:
+    n = pairs.shape[0]
+    if n == 0:
+        return
+    _check(_lib.paged_kv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                     _dev(pairs, "pairs"), n, num_kv_heads, head_dim, num_blocks,
+                                     _dtype_code(k_cache), _stream(stream)),
+           "paged_kv_copy_blocks")
+
+
+def paged_attention_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                   partition_size=0) -> int:
+    return int(_lib.paged_attention_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                   max_context_len, partition_size))
+
+
+def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, out, *,
+                           num_kv_heads: int, num_blocks: int, max_context_len: int,
+                           scale: float, partition_size: int = 0, workspace=None,
+                           stream=None) -> None:
+    B, Hq, D = q.shape
+    mb = block_tables.shape[1]
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.paged_attention_decode(_dev(q, "q"), _dev(k_cache, "k_cache"),
+                                       _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+                                       _dev(context_lens, "context_lens"), B, Hq, num_kv_heads, D,
+                                       num_blocks, mb, max_context_len, scale, partition_size,
+                                       ws_ptr, ws_bytes, _dtype_code(k_cache), _dev(out, "out"),
+                                       _stream(stream)), "paged_attention_decode")
+
+
+def pkv_profile_begin() -> None:
+    _check(_lib.pkv_profile_begin(), "pkv_profile_begin")
+
+
+def pkv_profile_end():
+    n, ms = C.c_int32(), C.c_double()
+    _check(_lib.pkv_profile_end(C.byref(n), C.byref(ms)), "pkv_profile_end")
+    return n.value, ms.value

@@ -1,0 +1,247 @@
+// Host block pool and slot planner of libpagedkv.
+//
+// "PagedAttention por dentro" (blog.lo0.es): "El pool de bloques" -- one
+// global pool of fixed 16-token blocks, sized at start, O(1) allocation;
+// the figure in "La tabla de paginas (block table)" -- blocks of a finished
+// session return to the pool; the same section's append rule (write into
+// the last block while it has room, otherwise take a new block and append
+// it to the table); "Copy-on-write para sampling paralelo" -- shared blocks
+// carry reference counts and are copied only when a sequence is about to
+// write into one.
+//
+// The free list is a LIFO stack (std::vector, top at the back).  Every call
+// validates before it mutates, so a failing call leaves the pool unchanged.
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pagedkv.h"
+
+struct pkv_pool {
+  int32_t num_blocks = 0;
+  std::vector<int32_t> free_stack;  // back() is handed out next
+  std::vector<int32_t> ref;         // 0 = free
+};
+
+namespace {
+
+bool live(const pkv_pool* p, int32_t id) {
+  return id >= 0 && id < p->num_blocks && p->ref[id] > 0;
+}
+
+int32_t pop_block(pkv_pool* p) {
+  int32_t id = p->free_stack.back();
+  p->free_stack.pop_back();
+  p->ref[id] = 1;
+  return id;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID: return "invalid argument";
+    case PKV_ERR_OOM: return "out of free blocks";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* init_order,
+                           pkv_pool** out_pool) {
+  if (!out_pool) return PKV_ERR_INVALID;
+  *out_pool = nullptr;
+  if (block_size != PKV_BLOCK_SIZE) return PKV_ERR_UNSUPPORTED;
+  if (num_blocks < 1) return PKV_ERR_INVALID;
+  if (init_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t id = init_order[i];
+      if (id < 0 || id >= num_blocks || seen[id]) return PKV_ERR_INVALID;
+      seen[id] = 1;
+    }
+  }
+  pkv_pool* p = new (std::nothrow) pkv_pool;
+  if (!p) return PKV_ERR_OOM;
+  p->num_blocks = num_blocks;
+  p->ref.assign(num_blocks, 0);
+  p->free_stack.resize(num_blocks);
+  // The first allocation returns order[0]: it sits at the top (back).
+  for (int32_t i = 0; i < num_blocks; ++i)
+    p->free_stack[num_blocks - 1 - i] = init_order ? init_order[i] : i;
+  *out_pool = p;
+  return PKV_OK;
+}
+
+void pkv_pool_destroy(pkv_pool* pool) { delete pool; }
+
+pkv_status kv_block_alloc(pkv_pool* p, int32_t n, int32_t* out_ids) {
+  if (!p || n < 0 || (n > 0 && !out_ids)) return PKV_ERR_INVALID;
+  if (static_cast<size_t>(n) > p->free_stack.size()) return PKV_ERR_OOM;
+  for (int32_t i = 0; i < n; ++i) out_ids[i] = pop_block(p);
+  return PKV_OK;
+}
+
+pkv_status kv_block_share(pkv_pool* p, int32_t n, const int32_t* ids) {
+  if (!p || n < 0 || (n > 0 && !ids)) return PKV_ERR_INVALID;
+  for (int32_t i = 0; i < n; ++i)
+    if (!live(p, ids[i])) return PKV_ERR_INVALID;
+  for (int32_t i = 0; i < n; ++i) ++p->ref[ids[i]];
+  return PKV_OK;
+}
+
+pkv_status kv_block_free(pkv_pool* p, int32_t n, const int32_t* ids) {
+  if (!p || n < 0 || (n > 0 && !ids)) return PKV_ERR_INVALID;
+  std::unordered_map<int32_t, int32_t> drops;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t id = ids[i];
+    if (id < 0 || id >= p->num_blocks) return PKV_ERR_INVALID;
+    if (++drops[id] > p->ref[id]) return PKV_ERR_INVALID;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t id = ids[i];
+    if (--p->ref[id] == 0) p->free_stack.push_back(id);
+  }
+  return PKV_OK;
+}
+
+pkv_status kv_block_cow(pkv_pool* p, int32_t id, int32_t* out_id, int32_t* needs_copy) {
+  if (!p || !out_id || !needs_copy || !live(p, id)) return PKV_ERR_INVALID;
+  if (p->ref[id] == 1) {
+    *out_id = id;
+    *needs_copy = 0;
+    return PKV_OK;
+  }
+  if (p->free_stack.empty()) return PKV_ERR_OOM;
+  int32_t fresh = pop_block(p);
+  --p->ref[id];
+  *out_id = fresh;
+  *needs_copy = 1;
+  return PKV_OK;
+}
+
+pkv_status kv_block_refcount(const pkv_pool* p, int32_t id, int32_t* out_refcount) {
+  if (!p || !out_refcount || id < 0 || id >= p->num_blocks) return PKV_ERR_INVALID;
+  *out_refcount = p->ref[id];
+  return PKV_OK;
+}
+
+pkv_status kv_pool_stats(const pkv_pool* p, pkv_stats* s) {
+  if (!p || !s) return PKV_ERR_INVALID;
+  int32_t used = 0, shared = 0;
+  int64_t refs = 0;
+  for (int32_t r : p->ref) {
+    used += r > 0;
+    shared += r > 1;
+    refs += r;
+  }
+  s->num_blocks = p->num_blocks;
+  s->num_free = static_cast<int32_t>(p->free_stack.size());
+  s->num_used = used;
+  s->num_shared = shared;
+  s->num_refs = refs;
+  s->usage_percent = 100.0 * used / p->num_blocks;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_free_list(const pkv_pool* p, int32_t capacity, int32_t* out_ids,
+                             int32_t* out_n) {
+  if (!p || !out_n || capacity < 0 || (capacity > 0 && !out_ids)) return PKV_ERR_INVALID;
+  const int32_t n = static_cast<int32_t>(p->free_stack.size());
+  const int32_t k = std::min(n, capacity);
+  for (int32_t i = 0; i < k; ++i) out_ids[i] = p->free_stack[n - 1 - i];
+  *out_n = n;
+  return PKV_OK;
+}
+
+pkv_status paged_kv_append_slots(pkv_pool* p, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                 int32_t* tables, int32_t* lens, const int32_t* num_new,
+                                 int64_t* slot_mapping, int64_t slot_capacity,
+                                 int32_t* table_updates, int32_t update_capacity,
+                                 int32_t* num_updates, int32_t* cow_pairs, int32_t cow_capacity,
+                                 int32_t* num_cow) {
+  if (!p || num_seqs < 0 || max_blocks_per_seq < 1 || !num_updates || !num_cow)
+    return PKV_ERR_INVALID;
+  if (num_seqs > 0 && (!tables || !lens)) return PKV_ERR_INVALID;
+  if (static_cast<int64_t>(num_seqs) * max_blocks_per_seq >= (int64_t(1) << 31))
+    return PKV_ERR_INVALID;
+  const int64_t cap_tokens = int64_t(max_blocks_per_seq) * PKV_BLOCK_SIZE;
+
+  // Dry run: count what the real pass will need and validate every table
+  // entry it will read, without touching the pool.  Only copy-on-write
+  // changes existing refcounts inside one call (it drops one reference of
+  // the shared block), tracked in `dropped`.
+  int64_t slots = 0, allocs = 0, cows = 0;
+  std::unordered_map<int32_t, int32_t> dropped;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t add = num_new ? num_new[s] : 1;
+    const int64_t p0 = lens[s];
+    if (add < 0 || p0 < 0 || p0 + add > cap_tokens) return PKV_ERR_INVALID;
+    if (add == 0) continue;
+    slots += add;
+    // tokens p0 .. p0+add-1: a block starts at every p % 16 == 0
+    const int64_t first_new = (p0 + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;  // first block index >= p0 boundary
+    const int64_t last_blk = (p0 + add - 1) / PKV_BLOCK_SIZE;
+    allocs += std::max<int64_t>(0, last_blk - first_new + 1);
+    if (p0 % PKV_BLOCK_SIZE != 0) {
+      // the first token lands in the existing, possibly shared, last block
+      const int32_t old = tables[int64_t(s) * max_blocks_per_seq + p0 / PKV_BLOCK_SIZE];
+      if (!live(p, old)) return PKV_ERR_INVALID;
+      auto it = dropped.find(old);
+      const int32_t refs = p->ref[old] - (it == dropped.end() ? 0 : it->second);
+      if (refs > 1) {
+        ++cows;
+        ++allocs;
+        ++dropped[old];
+      }
+    }
+  }
+  if (allocs > static_cast<int64_t>(p->free_stack.size())) return PKV_ERR_OOM;
+  if (slots > slot_capacity || allocs > update_capacity || cows > cow_capacity)
+    return PKV_ERR_INVALID;
+  if ((slots > 0 && !slot_mapping) || (allocs > 0 && !table_updates) || (cows > 0 && !cow_pairs))
+    return PKV_ERR_INVALID;
+
+  // Real pass: cannot fail any more.
+  int64_t k = 0;
+  int32_t nu = 0, nc = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t add = num_new ? num_new[s] : 1;
+    int32_t* row = tables + int64_t(s) * max_blocks_per_seq;
+    for (int32_t a = 0; a < add; ++a) {
+      const int32_t pos = lens[s];
+      const int32_t ti = pos / PKV_BLOCK_SIZE;
+      if (pos % PKV_BLOCK_SIZE == 0) {
+        const int32_t id = pop_block(p);
+        row[ti] = id;
+        table_updates[2 * nu] = s * max_blocks_per_seq + ti;
+        table_updates[2 * nu + 1] = id;
+        ++nu;
+      } else if (p->ref[row[ti]] > 1) {
+        const int32_t old = row[ti];
+        const int32_t id = pop_block(p);
+        --p->ref[old];
+        row[ti] = id;
+        table_updates[2 * nu] = s * max_blocks_per_seq + ti;
+        table_updates[2 * nu + 1] = id;
+        ++nu;
+        cow_pairs[2 * nc] = old;
+        cow_pairs[2 * nc + 1] = id;
+        ++nc;
+      }
+      slot_mapping[k++] = int64_t(row[ti]) * PKV_BLOCK_SIZE + pos % PKV_BLOCK_SIZE;
+      lens[s] = pos + 1;
+    }
+  }
+  *num_updates = nu;
+  *num_cow = nc;
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+"""Host driver for one layer's paged KV cache on one GPU.
+
+Holds the device cache tensors, the device-resident block tables and
+lengths (with their host mirrors), the host pool and a decode workspace, and
+sequences the C-ABI calls of one decode step:
+
+  1. plan the appended tokens' slots on the host (paged_kv_append_slots);
+  2. upload slots, table deltas, copy-on-write pairs and lengths (one
+     host-to-device copy from pinned staging memory);
+  3. apply the table deltas (paged_block_table_update);
+  4. copy shared blocks that are about to be written (paged_kv_copy_blocks);
+  5. write the new K/V (paged_kv_write);
+  6. attend (paged_attention_decode).
+
+Every step runs in libpagedkv; this module only moves arguments.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _capi as capi
+
+BLOCK = capi.BLOCK_SIZE
+
+
+class _Staging:
+    """A ring of pinned host buffers so that uploads stay asynchronous."""
+
+    def __init__(self, nbytes: int, depth: int = 4):
+        self.bufs = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(depth)]
+        self.events = [None] * depth
+        self.i = 0
+
+    def put(self, arrays, device, stream):
+        """Packs numpy arrays (8-byte aligned pieces) into the next pinned
+        buffer and copies them to ``device``; returns device views."""
+        k = self.i
+        self.i = (self.i + 1) % len(self.bufs)
+        if self.events[k] is not None:
+            self.events[k].synchronize()
+        buf = self.bufs[k]
+        host = buf.numpy()
+        offs, off = [], 0
+        for a in arrays:
+            offs.append(off)
+            n = a.nbytes
+            host[off:off + n] = np.ascontiguousarray(a).view(np.uint8).ravel()
+            off += (n + 7) & ~7
+        with torch.cuda.stream(stream):
+            dev = buf[:max(off, 8)].to(device, non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(stream)
+        self.events[k] = ev
+        views = []
+        for a, o in zip(arrays, offs):
+            t = dev[o:o + a.nbytes]
+            dt = {np.dtype(np.int64): torch.int64, np.dtype(np.int32): torch.int32}[a.dtype]
+            views.append(t.view(dt).view(*a.shape) if a.size else t.view(dt))
+        return views
+
+
+class PagedKV:
+    def __init__(self, *, num_blocks: int, num_seqs: int, max_blocks_per_seq: int,
+                 num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
+                 device="cuda", init_order=None, fill=None, partition_size: int = 0):
+        self.num_blocks, self.num_seqs, self.max_blocks = num_blocks, num_seqs, max_blocks_per_seq
+        self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.partition_size = partition_size
+        self.pool = capi.pkv_pool_create(num_blocks, BLOCK, init_order)
+        tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+        n = num_blocks * num_kv_heads * BLOCK * head_dim
+        self.k_cache = torch.empty(n, dtype=tdt, device=self.device)
+        self.v_cache = torch.empty(n, dtype=tdt, device=self.device)
+        if fill is None:
+            self.k_cache.zero_()
+            self.v_cache.zero_()
+        else:
+            self.k_cache.fill_(fill)
+            self.v_cache.fill_(fill)
+        self.tables = np.full((num_seqs, max_blocks_per_seq), -1, dtype=np.int32)
+        self.lens = np.zeros(num_seqs, dtype=np.int32)
+        self.tables_d = torch.from_numpy(self.tables).to(self.device)
+        self.lens_d = torch.from_numpy(self.lens).to(self.device)
+        ws = capi.paged_attention_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                 max_blocks_per_seq * BLOCK, partition_size)
+        self.workspace = torch.empty(max(ws // 4, 1), dtype=torch.float32, device=self.device)
+        self._staging = None
+
+    # ------------------------------------------------------------------ host helpers
+    def _upload(self, arrays, stream):
+        need = sum((a.nbytes + 7) & ~7 for a in arrays) + 8
+        if self._staging is None or self._staging.bufs[0].numel() < need:
+            self._staging = _Staging(max(need, 1 << 16))
+        return self._staging.put(arrays, self.device, stream)
+
+    def share_prefix(self, src: int, dsts, num_blocks: int):
+        """Sequences ``dsts`` take the first ``num_blocks`` blocks of ``src``
+        by reference (refcount + 1 each) and the same length."""
+        ids = self.tables[src, :num_blocks].copy()
+        for d in dsts:
+            capi.kv_block_share(self.pool, ids)
+            self.tables[d, :num_blocks] = ids
+            self.lens[d] = self.lens[src]
+        self.tables_d.copy_(torch.from_numpy(self.tables))
+        self.lens_d.copy_(torch.from_numpy(self.lens))
+
+    # ------------------------------------------------------------------ a step
+    def append(self, k_new, v_new, num_new=None, stream=None):
+        """Appends tokens (k_new, v_new device [T][Hkv][D], rows in order of
+        sequence) and returns (slots, table updates, cow pairs) as numpy."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        slots, upd, cows = capi.paged_kv_append_slots(self.pool, self.tables, self.lens, num_new)
+        d_slots, d_upd, d_cows, d_lens = self._upload([slots, upd, cows, self.lens], stream)
+        s = stream.cuda_stream
+        capi.paged_block_table_update(self.tables_d, d_upd, s)
+        with torch.cuda.stream(stream):
+            self.lens_d.copy_(d_lens)
+        capi.paged_kv_copy_blocks(self.k_cache, self.v_cache, d_cows, self.num_kv_heads,
+                                  self.head_dim, self.num_blocks, s)
+        capi.paged_kv_write(k_new, v_new, d_slots, self.k_cache, self.v_cache, self.num_kv_heads,
+                            self.head_dim, self.num_blocks, s)
+        return slots, upd, cows
+
+    def decode(self, q, scale: float, out=None, stream=None, partition_size=None):
+        stream = stream or torch.cuda.current_stream(self.device)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        ps = self.partition_size if partition_size is None else partition_size
+        max_ctx = int(self.lens.max()) if self.lens.size else 0
+        ws = self.workspace
+        need = capi.paged_attention_workspace_size(self.num_seqs, self.num_q_heads, self.head_dim,
+                                                   max_ctx, ps)
+        if need > ws.numel() * 4:
+            ws = self.workspace = torch.empty(need // 4, dtype=torch.float32, device=self.device)
+        capi.paged_attention_decode(q, self.k_cache, self.v_cache, self.tables_d, self.lens_d, out,
+                                    num_kv_heads=self.num_kv_heads, num_blocks=self.num_blocks,
+                                    max_context_len=max_ctx, scale=scale, partition_size=ps,
+                                    workspace=ws, stream=stream.cuda_stream)
+        return out
+
+    def free_sequence(self, s: int):
+        """Returns sequence s's blocks to the pool (one reference each)."""
+        n = -(-int(self.lens[s]) // BLOCK)
+        capi.kv_block_free(self.pool, self.tables[s, :n])
+        self.tables[s, :] = -1
+        self.lens[s] = 0
+        self.tables_d[s].fill_(-1)
+        self.lens_d[s] = 0
+
+
+def replay_prefill(kv: PagedKV, w, to_device):
+    """Builds the prefill state of a synthetic workload ``w`` (attributes as
+    in workloads.synth.Workload): optional shared prefix appended by sequence
+    0 and shared by the others, then every sequence's own tokens.
+    ``to_device`` turns a host row array into a device tensor of the cache
+    dtype."""
+    s = w.spec
+    row = 0
+    if s.prefix_len > 0:
+        first = np.zeros(s.num_seqs, dtype=np.int32)
+        first[0] = s.prefix_len
+        kv.append(to_device(w.k_rows[:s.prefix_len]), to_device(w.v_rows[:s.prefix_len]), first)
+        row = s.prefix_len
+        kv.share_prefix(0, range(1, s.num_seqs), -(-s.prefix_len // BLOCK))
+    if int(w.own_lens.sum()) > 0:
+        kv.append(to_device(w.k_rows[row:]), to_device(w.v_rows[row:]), w.own_lens)
