@@ -39,11 +39,8 @@ class CacheModel:
             num_blocks, num_kv_heads, head_dim, dtype)
         store = np.float32 if dtype == "f32" else np.uint16
         shape = (num_blocks, num_kv_heads, BLOCK_SIZE * head_dim)
-        self.k = np.zeros(shape, dtype=store)
-        self.v = np.zeros(shape, dtype=store)
-        if fill is not None:
-            self.k[...] = fill
-            self.v[...] = fill
+        self.k = np.full(shape, 0 if fill is None else fill, dtype=store)
+        self.v = np.full(shape, 0 if fill is None else fill, dtype=store)
         self.koff, self.voff = offset_tables(head_dim)
 
     def write(self, k_new: np.ndarray, v_new: np.ndarray, slots: np.ndarray):
@@ -54,10 +51,14 @@ class CacheModel:
         idx = np.nonzero(keep)[0]
         blk = slots[idx] // BLOCK_SIZE
         t = slots[idx] % BLOCK_SIZE
-        heads = np.arange(self.num_kv_heads)
-        # self.k[blk, h, koff[t, d]] = k_new[i, h, d]  for all kept i, all h, d
-        self.k[blk[:, None, None], heads[None, :, None], self.koff[t][:, None, :]] = k_new[idx]
-        self.v[blk[:, None, None], heads[None, :, None], self.voff[t][:, None, :]] = v_new[idx]
+        tile = BLOCK_SIZE * self.head_dim
+        kf = self.k.reshape(-1)
+        vf = self.v.reshape(-1)
+        for h in range(self.num_kv_heads):
+            # element (blk, h, off[t, d]) <- row i, head h, channel d
+            base = (blk * self.num_kv_heads + h) * tile
+            kf[base[:, None] + self.koff[t]] = k_new[idx, h, :]
+            vf[base[:, None] + self.voff[t]] = v_new[idx, h, :]
 
     def copy_blocks(self, pairs):
         """Copy whole blocks (every head and slot, K and V), src -> dst, in order."""

@@ -60,11 +60,10 @@ def plan_append(pool: PoolModel, tables: np.ndarray, lens: np.ndarray, num_new=N
     slots, updates, cows = [], [], []
     try:
         for s in range(B):
-            for _ in range(int(num_new[s])):
-                p = int(lens[s])
+            p, end = int(lens[s]), int(lens[s]) + int(num_new[s])
+            # the new tokens p .. end-1, one block's run at a time
+            while p < end:
                 pos = p // BLOCK_SIZE
-                if pos >= max_blocks:
-                    raise PoolError("invalid", f"sequence {s}: position {p} beyond the table")
                 if p % BLOCK_SIZE == 0:
                     (blk,) = pool.alloc(1)
                     tables[s, pos] = blk
@@ -76,8 +75,10 @@ def plan_append(pool: PoolModel, tables: np.ndarray, lens: np.ndarray, num_new=N
                         tables[s, pos] = new
                         updates.append((s * max_blocks + pos, new))
                         cows.append((old, new))
-                slots.append(slot_of(tables[s], p))
-                lens[s] = p + 1
+                run = min(end, (pos + 1) * BLOCK_SIZE) - p
+                slots.extend(slot_of(tables[s], q) for q in range(p, p + run))
+                p += run
+                lens[s] = p
     except PoolError:
         pool.restore(snap)
         tables[...] = tables_before

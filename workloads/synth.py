@@ -17,10 +17,14 @@ Five workloads follow the shapes of the decode step described on the pages
                    last block is only half full; the append step then adds
                    s_b + 1 tokens per sequence, which forces copy-on-write
 
-Draw order (fixed, one numpy PCG64 generator seeded 1000 + workload number):
-lengths, own-suffix lengths, the pool permutation, Q, K rows, V rows, then
-the appended K rows and V rows.  Values are N(0, 1) float32; bf16 workloads
-round them to bf16 (round to nearest even) and keep the raw 16-bit patterns.
+Draw order (fixed): one numpy PCG64 generator seeded 1000 + workload number
+draws the lengths, the own-suffix lengths, the pool permutation and Q, in
+that order.  The bulk rows (K rows, V rows, appended K rows, appended V rows:
+tags 1, 2, 3, 4) are drawn in chunks of 4096 rows, chunk c of tag k from
+PCG64(SeedSequence([seed, k, c])), so chunks can be drawn in parallel and
+the result does not depend on the number of threads.  Values are N(0, 1)
+float32; bf16 workloads round them to bf16 (round to nearest even) and keep
+the raw 16-bit patterns.
 
 Prefill recipe that both sides replay with their own allocator:
   1. if ``prefix_len > 0``: sequence 0 appends ``prefix_len`` tokens, and
@@ -36,6 +40,7 @@ permutation), so blocks end up scattered over the pool.
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -143,8 +148,8 @@ def _ceil_div(a, b):
 
 
 def _draw_values(rng: np.random.Generator, shape, dtype: str, chunk_rows: int = 1 << 14):
-    """N(0,1) float32 draws, stored as float32 or bf16 bits, drawn row-chunk by
-    row-chunk (same stream as a single draw of the whole array)."""
+    """N(0,1) float32 draws from ``rng``, stored as float32 or bf16 bits,
+    drawn row-chunk by row-chunk (same stream as one draw of the array)."""
     shape = tuple(int(s) for s in shape)
     rows = shape[0]
     inner = int(np.prod(shape[1:])) if len(shape) > 1 else 1
@@ -154,6 +159,37 @@ def _draw_values(rng: np.random.Generator, shape, dtype: str, chunk_rows: int = 
         r1 = min(rows, r0 + chunk_rows)
         x = rng.standard_normal((r1 - r0) * inner, dtype=np.float32).reshape(r1 - r0, inner)
         flat[r0:r1] = x if dtype == "f32" else round_bf16_bits(x)
+    return out
+
+
+BULK_CHUNK = 4096
+
+
+def _draw_rows(seed: int, tag: int, shape, dtype: str, threads: int | None = None):
+    """Bulk rows: chunk c of BULK_CHUNK rows from PCG64(SeedSequence([seed,
+    tag, c])); chunks are independent, so they are drawn on a thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
+    shape = tuple(int(s) for s in shape)
+    rows = shape[0]
+    inner = int(np.prod(shape[1:])) if len(shape) > 1 else 1
+    out = np.empty(shape, dtype=np.float32 if dtype == "f32" else np.uint16)
+    flat = out.reshape(rows, inner)
+
+    def fill(c):
+        r0, r1 = c * BULK_CHUNK, min(rows, (c + 1) * BULK_CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tag, c])))
+        x = g.standard_normal((r1 - r0) * inner, dtype=np.float32).reshape(r1 - r0, inner)
+        flat[r0:r1] = x if dtype == "f32" else round_bf16_bits(x)
+
+    nchunks = -(-rows // BULK_CHUNK)
+    if threads is None:
+        threads = min(16, len(os.sched_getaffinity(0)))
+    if nchunks <= 1 or threads <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out
 
 
@@ -219,12 +255,12 @@ def generate(key: str, *, values: bool = True, extra_tokens: int = 0) -> Workloa
     q = k_rows = v_rows = k_app = v_app = None
     if values:
         H, Hkv, D = s.num_q_heads, s.num_kv_heads, s.head_dim
-        q = _draw_values(rng, (B, H, D), s.dtype)                 # 4. Q
-        k_rows = _draw_values(rng, (total_rows, Hkv, D), s.dtype)  # 5. K rows
-        v_rows = _draw_values(rng, (total_rows, Hkv, D), s.dtype)  # 6. V rows
+        q = _draw_values(rng, (B, H, D), s.dtype)                      # 4. Q
+        k_rows = _draw_rows(s.seed, 1, (total_rows, Hkv, D), s.dtype)   # 5. K rows
+        v_rows = _draw_rows(s.seed, 2, (total_rows, Hkv, D), s.dtype)   # 6. V rows
         n_app = int(append.sum())
-        k_app = _draw_values(rng, (n_app, Hkv, D), s.dtype)        # 7. appended K, V
-        v_app = _draw_values(rng, (n_app, Hkv, D), s.dtype)
+        k_app = _draw_rows(s.seed, 3, (n_app, Hkv, D), s.dtype)         # 7. appended K, V
+        v_app = _draw_rows(s.seed, 4, (n_app, Hkv, D), s.dtype)
     return Workload(spec=s, lens=lens.astype(np.int32), own_lens=own.astype(np.int32),
                     suffix_lens=suffix.astype(np.int32), append_counts=append.astype(np.int32),
                     num_blocks=nb, max_blocks_per_seq=max_blocks, pool_order=order,
@@ -234,14 +270,17 @@ def generate(key: str, *, values: bool = True, extra_tokens: int = 0) -> Workloa
 
 def small_random(seed: int, *, num_seqs: int, num_q_heads: int, num_kv_heads: int,
                  head_dim: int, dtype: str, max_len: int, num_blocks: int | None = None,
-                 min_len: int = 0, append: int = 1) -> Workload:
+                 min_len: int = 0, append: int = 1, fixed=None) -> Workload:
     """A small random workload for edge-case tests (not one of the named ones).
 
-    Lengths uniform in [min_len, max_len]; the pool holds 1.25x the need."""
+    Lengths uniform in [min_len, max_len], the first ones replaced by
+    ``fixed`` if given; the pool holds 1.25x the need."""
     s = WorkloadSpec(f"random-{seed}", 0, num_seqs, num_q_heads, num_kv_heads, head_dim,
                      dtype, "fixed")
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = rng.integers(min_len, max_len, size=num_seqs, endpoint=True).astype(np.int64)
+    if fixed is not None:
+        lens[:len(fixed)] = fixed
     append_c = np.full(num_seqs, append, dtype=np.int64)
     need = int(np.sum(_ceil_div(lens + append_c, BLOCK_SIZE)))
     nb = num_blocks if num_blocks is not None else max(1, int(math.ceil(1.25 * need)))
@@ -249,11 +288,11 @@ def small_random(seed: int, *, num_seqs: int, num_q_heads: int, num_kv_heads: in
     order = rng.permutation(nb).astype(np.int32)
     q = _draw_values(rng, (num_seqs, num_q_heads, head_dim), dtype)
     T = int(lens.sum())
-    k_rows = _draw_values(rng, (T, num_kv_heads, head_dim), dtype)
-    v_rows = _draw_values(rng, (T, num_kv_heads, head_dim), dtype)
+    k_rows = _draw_rows(seed, 1, (T, num_kv_heads, head_dim), dtype)
+    v_rows = _draw_rows(seed, 2, (T, num_kv_heads, head_dim), dtype)
     n_app = int(append_c.sum())
-    k_app = _draw_values(rng, (n_app, num_kv_heads, head_dim), dtype)
-    v_app = _draw_values(rng, (n_app, num_kv_heads, head_dim), dtype)
+    k_app = _draw_rows(seed, 3, (n_app, num_kv_heads, head_dim), dtype)
+    v_app = _draw_rows(seed, 4, (n_app, num_kv_heads, head_dim), dtype)
     return Workload(spec=s, lens=lens.astype(np.int32), own_lens=lens.astype(np.int32),
                     suffix_lens=np.zeros(num_seqs, np.int32), append_counts=append_c.astype(np.int32),
                     num_blocks=nb, max_blocks_per_seq=max_blocks, pool_order=order,
