@@ -1,0 +1,219 @@
+"""Benchmark of the paged decode step on one MI355X.
+
+A step is one pass of the whole hot path for a batch of sequences, each
+gaining one token:
+  host slot planning + block allocation (C++), one pinned host-to-device
+  upload, block-table deltas, copy-on-write copies (when a shared block is
+  hit), the K/V write, and decode attention (split-K partitions + LSE
+  merge).
+Contexts grow by one token per step, exactly as in serving.
+
+Workload: gqa-8b-bf16 -- 256 sequences, 32 query / 8 kv heads, head_dim 128,
+bf16 cache, log-normal lengths (median 1000, sigma 1, clipped to [16, 8192],
+one sequence at 273), scattered 16-token blocks.
+
+Prints ONE JSON line.  value = effective KV GB/s of the whole step (K+V
+bytes the decode reads / step time); roofline = the decode main kernel's
+own average duration (HIP events recorded by the library on the kernel's
+stream) against 8 TB/s; cpu_baseline = the CPU oracle timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "gqa-8b-bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_gqa-8b_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    src = os.path.join(ROOT, "paged_kv_cache_102_amd", "csrc", "kernels.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def kv_bytes(lens, num_kv_heads, head_dim, elem=2) -> int:
+    return int(lens.astype("int64").sum()) * 2 * num_kv_heads * head_dim * elem
+
+
+def cpu_baseline(w, seconds: float = 12.0):
+    """The oracle, as it stands, on this host: decode over the whole batch,
+    repeated until ``seconds`` of CPU work, single-threaded BLAS."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attention, replay
+    st = replay.prefill(w)
+    s = w.spec
+    reps, t0 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            attention.decode(w.q, st.cache, st.tables, st.lens, s.num_q_heads, s.num_kv_heads,
+                             s.scale)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds or reps >= 4:
+                break
+    dt = time.perf_counter() - t0
+    gbs = kv_bytes(st.lens, s.num_kv_heads, s.head_dim) * reps / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seqs_per_s": round(s.num_seqs * reps / dt, 2),
+            "sample": f"full {s.num_seqs}-sequence batch at its prefill lengths, {reps} pass(es), "
+                      f"{dt:.1f} s, numpy float64, 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0 = default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only-steps", type=int, default=50)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path "
+              "is single-GPU in this build.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from paged_kv_cache_102_amd import _capi as capi
+    from paged_kv_cache_102_amd.driver import PagedKV, replay_prefill
+    from workloads import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
+    steps, warm = args.steps, args.warmup
+    w = synth.generate(WORKLOAD, extra_tokens=steps + warm + args.decode_only_steps + 1)
+    s = w.spec
+    log(f"[bench] {WORKLOAD}: B={s.num_seqs} Hq={s.num_q_heads} Hkv={s.num_kv_heads} "
+        f"D={s.head_dim} pool={w.num_blocks} blocks, {int(w.lens.sum())} tokens")
+
+    def to_dev(rows):
+        return torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    kv = PagedKV(num_blocks=w.num_blocks, num_seqs=s.num_seqs,
+                 max_blocks_per_seq=w.max_blocks_per_seq, num_q_heads=s.num_q_heads,
+                 num_kv_heads=s.num_kv_heads, head_dim=s.head_dim, dtype=s.dtype, device=dev,
+                 init_order=w.pool_order, partition_size=args.partition)
+    replay_prefill(kv, w, to_dev)
+    q = to_dev(w.q)
+    k_new, v_new = to_dev(w.k_app), to_dev(w.v_app)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        kv.append(k_new, v_new)
+        kv.decode(q, s.scale, out=out)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    # timed region: K whole steps
+    bytes_total = 0
+    capi.pkv_profile_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+        bytes_total += kv_bytes(kv.lens, s.num_kv_heads, s.head_dim)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    nlaunch, kern_ms = capi.pkv_profile_end()
+    dt = t1 - t0
+    ms_per_step = dt * 1e3 / steps
+    value = bytes_total / dt / 1e9
+    bytes_per_launch = bytes_total / steps
+    avg_kernel_ms = kern_ms / max(nlaunch, 1)
+    achieved = bytes_per_launch / (avg_kernel_ms * 1e-3) / 1e9
+
+    # decode alone, back to back (no appends), for context
+    dec = {}
+    if args.decode_only_steps > 0:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.decode_only_steps):
+            kv.decode(q, s.scale, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / args.decode_only_steps
+        db = kv_bytes(kv.lens, s.num_kv_heads, s.head_dim)
+        dec = {"ms": round(dms, 4), "kv_gb_per_s": round(db / dms / 1e6, 1),
+               "frac_of_peak": round(db / dms / 1e6 / HBM_PEAK_GBS, 4)}
+
+    traffic = committed_traffic()
+    stats = capi.kv_pool_stats(kv.pool)
+    waste = float(np.sum(-(-kv.lens // 16) * 16 - kv.lens) / np.sum(-(-kv.lens // 16) * 16))
+    result = {
+        "metric": "paged decode attn: effective KV GB/s & % of HBM peak; sequences/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "num_seqs": s.num_seqs, "num_q_heads": s.num_q_heads,
+                   "num_kv_heads": s.num_kv_heads, "head_dim": s.head_dim, "block_size": 16,
+                   "mean_context": round(float(kv.lens.mean()), 1),
+                   "partition_tokens": args.partition or 512, "parallelism": "single-gpu"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(s.num_seqs * steps / dt, 1),
+        "decode_only": dec,
+        "kv_waste_fraction": round(waste, 5),
+        "pool_usage_percent": round(stats["usage_percent"], 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_bf16_kernel<128>",
+                     "avg_launch_ms": round(avg_kernel_ms, 5), "launches": nlaunch,
+                     "algorithmic_bytes_per_launch": int(bytes_per_launch)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(w)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
