@@ -93,6 +93,8 @@ def main():
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0 = default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only-steps", type=int, default=50)
+    ap.add_argument("--no-read-ceiling", dest="read_ceiling", action="store_false",
+                    help="skip the streaming-read ceiling measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -176,6 +178,22 @@ def main():
         dec = {"ms": round(dms, 4), "kv_gb_per_s": round(db / dms / 1e6, 1),
                "frac_of_peak": round(db / dms / 1e6 / HBM_PEAK_GBS, 4)}
 
+    # measured streaming-read ceiling on this GPU (2 GiB, 16-byte loads)
+    ceiling = None
+    if args.read_ceiling:
+        buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+        sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+        capi.pkv_stream_read(buf, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            capi.pkv_stream_read(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ceiling = buf.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del buf, sink
+
     traffic = committed_traffic()
     stats = capi.kv_pool_stats(kv.pool)
     waste = float(np.sum(-(-kv.lens // 16) * 16 - kv.lens) / np.sum(-(-kv.lens // 16) * 16))
@@ -206,6 +224,8 @@ def main():
                      "traffic": traffic, "kernel": "decode_bf16_kernel<128>",
                      "avg_launch_ms": round(avg_kernel_ms, 5), "launches": nlaunch,
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
+        "hbm_read_ceiling_gbs": round(ceiling, 1) if ceiling else None,
+        "decode_frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")

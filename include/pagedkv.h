@@ -221,6 +221,18 @@ pkv_status paged_kv_write(const void* k_new, const void* v_new, const int64_t* s
                           int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                           pkv_dtype dtype, hipStream_t stream);
 
+/* One launch doing both paged_block_table_update(block_tables, table_elems,
+ * updates, num_updates) and paged_kv_write(k_new, ..., dtype) above, with
+ * their argument meanings, checks and skipping rules (the two parts touch
+ * different memory, so their order inside the launch does not matter).  A
+ * decode step appends a token per sequence and may grow a table in the same
+ * step [P5 "La tabla de paginas"]; one launch instead of two shortens it. */
+pkv_status paged_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                           void* k_cache, void* v_cache, int32_t num_tokens, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t num_blocks, pkv_dtype dtype,
+                           int32_t* block_tables, int64_t table_elems, const int32_t* updates,
+                           int32_t num_updates, hipStream_t stream);
+
 /* Copy whole blocks (all kv heads, all 16 slots, K and V) for copy-on-write
  * [P5 "Copy-on-write para sampling paralelo": only the last affected block
  * is copied].  pairs: device int32 [num_pairs][2] = (src block, dst block).
@@ -232,8 +244,11 @@ pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pai
                                 int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t num_blocks, pkv_dtype dtype, hipStream_t stream);
 
-/* Bytes of scratch paged_attention_decode needs for these sizes (0 when
- * every context fits one partition).  partition_size 0 = default (512). */
+/* Bytes of scratch paged_attention_decode needs for these sizes.  For
+ * partition_size > 0 it is 0 when every context fits one partition; for
+ * partition_size 0 it covers both the balanced bf16 split (two partial
+ * states per wavefront of the current device's grid) and 512-token fp32
+ * partitions.  Queries the current device (returns 0 if that fails). */
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                       int32_t max_context_len, int32_t partition_size);
 
@@ -247,15 +262,20 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int
  *   score_t = scale * sum_d q[s][h][d] * K_t[d],   t = 0..L-1
  *   w_t     = exp(score_t - max score) / sum_j exp(score_j - max score)
  *   out[s][h][:] = sum_t w_t * V_t[:]
- * (L = 0 gives a zero row).  Contexts longer than partition_size tokens are
- * split into partitions whose partial results (running max, sum of weights,
- * unnormalised output) are merged by a log-sum-exp reduction; the result
- * does not depend on the partitioning beyond rounding.
+ * (L = 0 gives a zero row).  The work is split into pieces whose partial
+ * results (running max, sum of weights, unnormalised output) are merged by a
+ * log-sum-exp reduction; the result does not depend on the split beyond
+ * rounding.  partition_size > 0: every context is cut into partitions of
+ * that many tokens.  partition_size == 0 (bf16): balanced split -- all
+ * (kv head, sequence, block) tiles form one list and every wavefront of a
+ * fixed grid (8 per compute unit) takes an equal contiguous slice of it,
+ * across sequence boundaries; for fp32, 0 means 512-token partitions.
  *
  *   q, k_cache, v_cache, block_tables, context_lens, workspace: device, read
  *   out: device fp32, written
  *   max_context_len: host-side upper bound of context_lens (sizes the grid)
- *   partition_size: tokens per partition, a multiple of 32; 0 = 512
+ *   partition_size: tokens per partition, a multiple of 32; 0 = balanced
+ *   (bf16) / 512 (fp32)
  *   workspace_bytes >= paged_attention_workspace_size(...) (may be NULL/0
  *   when that is 0)
  * Errors: num_q_heads % num_kv_heads != 0, non-positive sizes, a
@@ -284,6 +304,17 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
  * thread-safe. */
 pkv_status pkv_profile_begin(void);
 pkv_status pkv_profile_end(int32_t* num_launches, double* total_ms);
+
+/* Streaming-read reference: reads `bytes` (rounded down to 16) of device
+ * memory `buf` once with 16-byte loads, on `stream`, so the caller can time
+ * the achievable HBM read rate next to the decode kernel (8192 one-wave
+ * workgroups, each streaming its own contiguous chunk with non-temporal
+ * 16-byte loads, as the decode kernel does).  `sink` is device memory of at
+ * least 32 KiB that the kernel may write.  Chunks must stay below 2 GiB
+ * (bytes < 16 TiB) -> else PKV_ERR_UNSUPPORTED.  The decode path reads the whole cache on every token ["KV cache:
+ * la memoria de trabajo ...", "La inferencia es memory-bound"], so this is
+ * its ceiling. */
+pkv_status pkv_stream_read(const void* buf, size_t bytes, void* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -51,6 +51,8 @@ _SIGS = {
     "paged_block_table_update": (C.c_int, [_vp, C.c_int64, _vp, C.c_int32, _vp]),
     "paged_kv_write": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32, C.c_int32,
                                  C.c_int32, C.c_int, _vp]),
+    "paged_kv_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32, C.c_int32,
+                                  C.c_int32, C.c_int, _vp, C.c_int64, _vp, C.c_int32, _vp]),
     "paged_kv_copy_blocks": (C.c_int, [_vp, _vp, _vp, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                        C.c_int, _vp]),
     "paged_attention_workspace_size": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32, C.c_int32,
@@ -60,6 +62,7 @@ _SIGS = {
                                          C.c_int32, _vp, C.c_size_t, C.c_int, _vp, _vp]),
     "pkv_profile_begin": (C.c_int, []),
     "pkv_profile_end": (C.c_int, [_i32p, C.POINTER(C.c_double)]),
+    "pkv_stream_read": (C.c_int, [_vp, C.c_size_t, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -227,6 +230,20 @@ def paged_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache, num_kv_heads: i
                                _dtype_code(k_cache), _stream(stream)), "paged_kv_write")
 
 
+def paged_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, num_kv_heads: int,
+                    head_dim: int, num_blocks: int, block_tables, updates, stream=None) -> None:
+    n = slot_mapping.shape[0]
+    nu = updates.shape[0]
+    if n == 0 and nu == 0:
+        return
+    _check(_lib.paged_kv_append(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                _dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"),
+                                _dev(v_cache, "v_cache"), n, num_kv_heads, head_dim, num_blocks,
+                                _dtype_code(k_cache), _dev(block_tables, "block_tables"),
+                                block_tables.numel(), _dev(updates, "updates") if nu else None,
+                                nu, _stream(stream)), "paged_kv_append")
+
+
 def paged_kv_copy_blocks(k_cache, v_cache, pairs, num_kv_heads: int, head_dim: int,
                          num_blocks: int, stream=None) -> None:
     n = pairs.shape[0]
@@ -268,3 +285,8 @@ def pkv_profile_end():
     n, ms = C.c_int32(), C.c_double()
     _check(_lib.pkv_profile_end(C.byref(n), C.byref(ms)), "pkv_profile_end")
     return n.value, ms.value
+
+
+def pkv_stream_read(buf, sink, stream=None) -> None:
+    _check(_lib.pkv_stream_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                _dev(sink, "sink"), _stream(stream)), "pkv_stream_read")

@@ -59,15 +59,21 @@ __host__ __device__ inline int v_elem(int t, int d) {
 }
 
 // ------------------------------------------------------------------ wave helpers
-__device__ inline float group_max(float x) {  // over lanes l, l^16, l^32, l^48
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Reductions over the four lanes l, l^16, l^32, l^48 (one per 16-lane row)
+// with the gfx950 row-swap permutes: permlane16_swap pairs rows (0,1) and
+// (2,3), permlane32_swap pairs rows (0,2) and (1,3); both results of a swap
+// hold the two partners, so combining them gives the pair's value in every lane.
+__device__ inline float group_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ inline float group_sum(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 __device__ inline float wave_sum(float x) {
   for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
@@ -122,6 +128,48 @@ __global__ void kv_write_kernel(const T* __restrict__ k_new, const T* __restrict
   for (int e = 0; e < 8; ++e) vc[tile + v_elem(t, c * 8 + e)] = vv[e];
 }
 
+// ------------------------------------------------------------------ A2 + A3 fused
+// Workgroups [0, table_wgs) apply table deltas; the rest scatter K/V rows
+// exactly as kv_write_kernel does.
+template <typename T>
+__global__ void append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
+                              const int64_t* __restrict__ slots, T* __restrict__ kc,
+                              T* __restrict__ vc, int64_t total, int num_kv_heads, int head_dim,
+                              int64_t num_slots, int32_t* __restrict__ tables, int64_t elems,
+                              const int32_t* __restrict__ upd, int n_upd, int table_wgs) {
+  if (static_cast<int>(blockIdx.x) < table_wgs) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n_upd) {
+      const int64_t idx = upd[2 * i];
+      if (idx >= 0 && idx < elems) tables[idx] = upd[2 * i + 1];
+    }
+    return;
+  }
+  const int64_t idx = int64_t(blockIdx.x - table_wgs) * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int chunks = head_dim >> 3;
+  const int c = static_cast<int>(idx % chunks);
+  const int64_t ih = idx / chunks;
+  const int h = static_cast<int>(ih % num_kv_heads);
+  const int64_t i = ih / num_kv_heads;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot >> 4;
+  const int t = static_cast<int>(slot & 15);
+  const int64_t src = (i * num_kv_heads + h) * head_dim + c * 8;
+  const int64_t tile = (blk * num_kv_heads + h) * int64_t(kBlock) * head_dim;
+  T kv[8], vv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    kv[e] = k_new[src + e];
+    vv[e] = v_new[src + e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) kc[tile + k_elem(t, c * 8 + e)] = kv[e];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vc[tile + v_elem(t, c * 8 + e)] = vv[e];
+}
+
 // ------------------------------------------------------------------ A4: block copies
 // blockIdx.x = pair, blockIdx.y = 0 (K) / 1 (V); a block of all heads is one
 // contiguous run of `run16` 16-byte words.
@@ -148,9 +196,15 @@ struct DecodeArgs {
   float* ws_o;   // [B][Hq][max_parts][D]   unnormalised partial outputs
   float* ws_m;   // [B][Hq][max_parts]      running max (log2 domain)
   float* ws_l;   // [B][Hq][max_parts]      sum of weights
-  int num_q_heads, num_kv_heads, group;
+  int num_seqs, num_q_heads, num_kv_heads, group;
   int num_blocks, max_blocks, max_ctx, part_tokens, max_parts;
   float scale_log2e;
+  // balanced mode: partial states of each wave's first (slot 0) and last
+  // (slot 1) segment, [grid][2][group][D] and [grid][2][group]
+  float* bw_o;
+  float* bw_m;
+  float* bw_l;
+  int grid_waves;
 };
 
 // Length check shared by the kernels: a bad length poisons the sequence.
@@ -158,16 +212,35 @@ __device__ inline bool len_ok(int L, const DecodeArgs& a) {
   return L >= 0 && L <= a.max_ctx && int64_t(L) <= int64_t(a.max_blocks) * kBlock;
 }
 
-template <int D>
-__global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
+// Buffer resource over one cache tile: loads at byte offsets below `bytes`
+// read memory; with bytes == 0 every load returns zeros without a memory
+// request.  That lets the pipeline issue the same loads on every trip
+// (so the load counter waits are static) while prefetches past the end of
+// a partition cost nothing.
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// AUX is the cache policy of the K/V loads: 2 = non-temporal (the cache is
+// streamed once per step; on MI355X this lifts the read rate by ~12 %),
+// 0 = default, 18 = non-temporal + sc1.
+template <int D, int ST, int AUX>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_bf16_kernel(DecodeArgs a) {
   constexpr int NJ = D / 32;  // 16-byte pieces per lane per tile (K and V each)
   constexpr int NT = D / 16;  // 16-channel output tiles
   constexpr int64_t TILE = int64_t(kBlock) * D;
+  constexpr int TILE_BYTES = static_cast<int>(TILE * 2);
 
   const int lane = threadIdx.x;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // 1D grid, kv head fastest: workgroup i runs on XCD i % 8, so each XCD gets
+  // the same kv heads of every sequence and partition (an equal share of
+  // the work for any length mix, and blocks shared between sequences are
+  // read through one XCD's L2)
+  const int64_t wid = blockIdx.x;
+  const int kvh = static_cast<int>(wid % a.num_kv_heads);
+  const int b = static_cast<int>((wid / a.num_kv_heads) % a.num_seqs);
+  const int part = static_cast<int>(wid / (int64_t(a.num_kv_heads) * a.num_seqs));
   const int hcol = lane & 15;  // query head within the group (B/A operand column/row)
   const int grp = lane >> 4;   // lane group: tokens 4*grp .. 4*grp+3 of a block
   const int g = a.group;
@@ -199,9 +272,10 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
     qf[j] = __builtin_bit_cast(bf16x8, w);
   }
 
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.kc) + kvh * TILE + lane * 8;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.vc) + kvh * TILE + lane * 8;
-  const int64_t block_stride = int64_t(a.num_kv_heads) * TILE;
+  const char* kc = static_cast<const char*>(a.kc) + int64_t(kvh) * TILE_BYTES;
+  const char* vc = static_cast<const char*>(a.vc) + int64_t(kvh) * TILE_BYTES;
+  const int64_t block_bytes = int64_t(a.num_kv_heads) * TILE_BYTES;
+  const int loff = lane * 16;
 
   f32x4 o[NT];
 #pragma unroll
@@ -210,17 +284,26 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
   float lsum = 0.f;     // this lane's share of the sum of weights
   bool bad = false;
 
-  auto load_block = [&](int i, uint4 (&kr)[NJ], uint4 (&vr)[NJ]) {
-    int phys = __builtin_amdgcn_readfirstlane(row[i]);
-    if (phys < 0 || phys >= a.num_blocks) {
+  // physical block of partition block i (clamped into the partition; ids past
+  // its end are fetched but never used for a live load)
+  auto block_id = [&](int i) -> int {
+    return __builtin_amdgcn_readfirstlane(row[min(i, nblk - 1)]);
+  };
+  auto issue = [&](int i, int phys, uint4 (&kr)[NJ], uint4 (&vr)[NJ]) {
+    int bytes = TILE_BYTES;
+    if (i >= nblk) {
+      bytes = 0;
+    } else if (phys < 0 || phys >= a.num_blocks) {
       bad = true;
-      phys = 0;
+      bytes = 0;
     }
-    const int64_t off = int64_t(phys) * block_stride;
+    const int64_t off = int64_t(bytes ? phys : 0) * block_bytes;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + off, bytes);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + off, bytes);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      kr[j] = *reinterpret_cast<const uint4*>(kbase + off + 512 * j);
-      vr[j] = *reinterpret_cast<const uint4*>(vbase + off + 512 * j);
+      kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + 1024 * j, 0, AUX));
+      vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + 1024 * j, 0, AUX));
     }
   };
 
@@ -285,16 +368,23 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
     }
   };
 
-  // two-stage pipeline: the next block's loads are in flight while one computes
-  uint4 ka[NJ], va[NJ], kb[NJ], vb[NJ];
-  load_block(0, ka, va);
-  if (nblk > 1) load_block(1, kb, vb);
-  for (int i = 0; i < nblk; i += 2) {
-    compute_block(i, ka, va);
-    if (i + 2 < nblk) load_block(i + 2, ka, va);
-    if (i + 1 < nblk) {
-      compute_block(i + 1, kb, vb);
-      if (i + 3 < nblk) load_block(i + 3, kb, vb);
+  // ST-stage pipeline: while block i is computed, blocks i+1 .. i+ST-1 are in
+  // flight.  Every trip issues the same loads (past the end they are empty),
+  // and block ids are fetched one trip ahead of the loads that use them.
+  uint4 kr[ST][NJ], vr[ST][NJ];
+  int ids[ST];
+#pragma unroll
+  for (int st = 0; st < ST; ++st) ids[st] = block_id(st);
+#pragma unroll
+  for (int st = 0; st < ST; ++st) issue(st, ids[st], kr[st], vr[st]);
+  for (int i0 = 0; i0 < nblk; i0 += ST) {
+#pragma unroll
+    for (int st = 0; st < ST; ++st) ids[st] = block_id(i0 + ST + st);
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      const int i = i0 + st;
+      if (i < nblk) compute_block(i, kr[st], vr[st]);
+      issue(i + ST, ids[st], kr[st], vr[st]);
     }
   }
 
@@ -329,6 +419,343 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ A5: decode, bf16, balanced
+// Work-balanced form of the same computation.  All (kv head, sequence,
+// block) tiles form one list, kv head slowest, then sequence, then block;
+// wave w of the grid takes an equal contiguous slice of it and walks the
+// slice across sequence boundaries with the same stage pipeline (so there
+// is no per-partition start-up and no ragged tail of unequal partitions).
+// A sequence's blocks that fall entirely inside one wave are finished there
+// (output written directly); at most the first and the last segment of a
+// wave are partial, and their (o, m, l) states go to slots 0 and 1 of that
+// wave for the merge kernel.
+__device__ inline int nblocks_of(const DecodeArgs& a, int L) {
+  return len_ok(L, a) ? (L + kBlock - 1) / kBlock : 0;
+}
+
+// Sum over the wave, returned as a wave-uniform value (scalar register), so
+// that everything derived from it (slice bounds, buffer resources) stays
+// uniform.
+__device__ inline int wave_sum_int(int x) {
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+// Blocks per kv head over all sequences.
+__device__ inline int total_blocks(const DecodeArgs& a) {
+  int total = 0;
+  for (int c = 0; c < a.num_seqs; c += 64) {
+    const int b = c + static_cast<int>(threadIdx.x);
+    total += wave_sum_int(b < a.num_seqs ? nblocks_of(a, a.lens[b]) : 0);
+  }
+  return total;
+}
+
+// Blocks of the sequences before b (per kv head).
+__device__ inline int blocks_before(const DecodeArgs& a, int b) {
+  int sum = 0;
+  for (int c = 0; c < b; c += 64) {
+    const int s = c + static_cast<int>(threadIdx.x);
+    sum += wave_sum_int(s < b ? nblocks_of(a, a.lens[s]) : 0);
+  }
+  return sum;
+}
+
+__device__ inline int64_t balanced_per_wave(int64_t G, int waves) {
+  constexpr int64_t kMinBlocks = 8;
+  const int64_t per = (G + waves - 1) / waves;
+  return per < kMinBlocks ? kMinBlocks : per;
+}
+
+template <int D, int ST, int AUX>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_bf16_balanced_kernel(DecodeArgs a) {
+  constexpr int NJ = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int64_t TILE = int64_t(kBlock) * D;
+  constexpr int TILE_BYTES = static_cast<int>(TILE * 2);
+
+  const int lane = threadIdx.x;
+  const int hcol = lane & 15;
+  const int grp = lane >> 4;
+  const int g = a.group;
+  const int B = a.num_seqs;
+  const int Hkv = a.num_kv_heads;
+  const int64_t wid = blockIdx.x;
+
+  const int total = total_blocks(a);
+  const int64_t G = int64_t(total) * Hkv;
+  const int64_t per = balanced_per_wave(G, a.grid_waves);
+  const int64_t g0 = wid * per;
+  if (g0 >= G) return;
+  const int64_t g1 = min(g0 + per, G);
+
+  // locate the first tile of the slice: kv head, then sequence by a scan of
+  // the per-sequence block counts
+  int c_kvh = static_cast<int>(g0 / total);
+  int rem = static_cast<int>(g0 - int64_t(c_kvh) * total);
+  int c_b = 0, c_blk = 0;
+  for (int c = 0, base = 0; c < B; c += 64) {
+    const int b = c + lane;
+    const int nb = b < B ? nblocks_of(a, a.lens[b]) : 0;
+    int incl = nb;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(incl, d);
+      if (lane >= d) incl += up;
+    }
+    const int chunk_total = __builtin_amdgcn_readlane(incl, 63);
+    if (rem < base + chunk_total) {
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > rem);
+      const int pos = static_cast<int>(__builtin_ctzll(hit));
+      c_b = c + pos;
+      c_blk = rem - (base + __builtin_amdgcn_readlane(incl, pos) - __builtin_amdgcn_readlane(nb, pos));
+      break;
+    }
+    base += chunk_total;
+  }
+  c_b = __builtin_amdgcn_readfirstlane(c_b);
+  c_blk = __builtin_amdgcn_readfirstlane(c_blk);
+  int c_L = a.lens[c_b];
+  int c_nb = nblocks_of(a, c_L);
+
+  // the load cursor starts where the compute cursor starts
+  int l_kvh = c_kvh, l_b = c_b, l_blk = c_blk, l_L = c_L, l_nb = c_nb;
+  auto advance = [&](int& kvh, int& b, int& blk, int& L, int& nb) {
+    ++blk;
+    while (blk >= nb) {  // skips empty sequences
+      blk = 0;
+      if (++b == B) {
+        b = 0;
+        if (++kvh == Hkv) {  // past the list: park (never used for a live load)
+          kvh = 0;
+          nb = 1 << 30;
+          break;
+        }
+      }
+      L = a.lens[b];
+      nb = nblocks_of(a, L);
+    }
+  };
+
+  const int64_t block_bytes = int64_t(Hkv) * TILE_BYTES;
+  const int loff = lane * 16;
+  const int qoff = (hcol * D + grp * 8) * 2;  // >= g*D*2 for padded heads: reads as 0
+  const int qbytes = g * D * 2;
+
+  // stage buffers: K, V and (for the first block of a segment) Q
+  uint4 kr[ST][NJ], vr[ST][NJ], qr[ST][NJ];
+  bool st_bad[ST];
+  int64_t l_idx = g0;
+  auto issue = [&](int st) {
+    const bool live = l_idx < g1;
+    int phys = __builtin_amdgcn_readfirstlane(
+        a.tables[int64_t(l_b) * a.max_blocks + (live ? l_blk : 0)]);
+    bool bad = false;
+    int bytes = live ? TILE_BYTES : 0;
+    if (live && (phys < 0 || phys >= a.num_blocks)) {
+      bad = true;
+      bytes = 0;
+    }
+    const int64_t off = (bytes ? int64_t(phys) * block_bytes : 0) + int64_t(l_kvh) * TILE_BYTES;
+    const char* kc = static_cast<const char*>(a.kc) + off;
+    const char* vc = static_cast<const char*>(a.vc) + off;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc, bytes);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc, bytes);
+    const bool needq = live && (l_blk == 0 || l_idx == g0);
+    const char* qb = static_cast<const char*>(a.q) +
+                     (int64_t(l_b) * a.num_q_heads + int64_t(l_kvh) * g) * D * 2;
+    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(qb, needq ? qbytes : 0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      kr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + 1024 * j, 0, AUX));
+      vr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + 1024 * j, 0, AUX));
+      qr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 64 * j, 0, 0));
+    }
+    st_bad[st] = bad;
+    if (live) advance(l_kvh, l_b, l_blk, l_L, l_nb);
+    ++l_idx;
+  };
+
+  bf16x8 qf[NJ];
+  f32x4 o[NT];
+  float m = -INFINITY, lsum = 0.f;
+  bool seg_bad = false;
+  int seg_first_blk = 0;
+  bool seg_is_first = true;  // the segment that starts the slice
+
+  auto end_segment = [&](bool complete) {
+    const float lt = group_sum(lsum);
+    const int64_t head0 = int64_t(c_b) * a.num_q_heads + int64_t(c_kvh) * g;
+    if (complete) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = grp * 4 + r;
+        const float lr = __shfl(lt, h);
+        const float inv = seg_bad ? __builtin_nanf("") : 1.0f / lr;
+        if (h < g) {
+          float* dst = a.out + (head0 + h) * D + hcol;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) dst[16 * n] = o[n][r] * inv;
+        }
+      }
+    } else {
+      const int64_t slot = wid * 2 + (seg_is_first ? 0 : 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = grp * 4 + r;
+        if (h < g) {
+          float* dst = a.bw_o + (slot * g + h) * D + hcol;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) dst[16 * n] = o[n][r];
+        }
+      }
+      if (lane < g) {
+        a.bw_m[slot * g + lane] = seg_bad ? __builtin_nanf("") : m;
+        a.bw_l[slot * g + lane] = lt;
+      }
+    }
+    seg_is_first = false;
+  };
+
+  auto compute = [&](int st, int64_t idx) {
+    if (c_blk == 0 || idx == g0) {  // a segment starts: its Q came with this block
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) qf[j] = __builtin_bit_cast(bf16x8, qr[st][j]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m = -INFINITY;
+      lsum = 0.f;
+      seg_bad = false;
+      seg_first_blk = c_blk;
+    }
+    seg_bad |= st_bad[st];
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[st][j]), qf[j], s,
+                                                   0, 0, 0);
+    const int tb = c_blk * kBlock + grp * 4;
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = (tb + r < c_L) ? s[r] * a.scale_log2e : -INFINITY;
+    float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mloc = group_max(mloc);
+    const float mnew = fmaxf(m, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sv[r] - mnew);
+    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    m = mnew;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, grp * 4 + r);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) o[n][r] *= ar;
+      }
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hi[r] = bf16_bits_rne(p[r]);
+      lo[r] = bf16_bits_rne(p[r] - __uint_as_float(hi[r] << 16));
+    }
+    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
+    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
+    if (c_blk * kBlock + kBlock > c_L) {
+      const uint32_t m01 = (tb + 0 < c_L ? 0x0000FFFFu : 0u) | (tb + 1 < c_L ? 0xFFFF0000u : 0u);
+      const uint32_t m23 = (tb + 2 < c_L ? 0x0000FFFFu : 0u) | (tb + 3 < c_L ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        vr[st][j].x &= m01;
+        vr[st][j].y &= m23;
+        vr[st][j].z &= m01;
+        vr[st][j].w &= m23;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const s16x4 v0 = __builtin_bit_cast(s16x4, make_uint2(vr[st][j].x, vr[st][j].y));
+      const s16x4 v1 = __builtin_bit_cast(s16x4, make_uint2(vr[st][j].z, vr[st][j].w));
+      o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, v0, o[2 * j], 0, 0, 0);
+      o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, v0, o[2 * j], 0, 0, 0);
+      o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, v1, o[2 * j + 1], 0, 0, 0);
+      o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, v1, o[2 * j + 1], 0, 0, 0);
+    }
+    const bool last_of_seq = (c_blk == c_nb - 1);
+    if (last_of_seq || idx == g1 - 1) end_segment(last_of_seq && seg_first_blk == 0);
+    if (idx + 1 < g1) advance(c_kvh, c_b, c_blk, c_L, c_nb);
+  };
+
+#pragma unroll
+  for (int st = 0; st < ST; ++st) issue(st);
+  for (int64_t i0 = g0; i0 < g1; i0 += ST) {
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      const int64_t i = i0 + st;
+      if (i < g1) compute(st, i);
+      issue(st);
+    }
+  }
+}
+
+// Merge for the balanced form: one wave per (sequence, kv head).  Writes
+// zeros for an empty context and NaN for a bad length; for a sequence whose
+// blocks were split over waves w0..w1, merges their partial states (slot 1
+// of w0 when w0's slice began before the sequence, else slot 0).
+template <int D>
+__global__ __launch_bounds__(64) void balanced_merge_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x;
+  const int kvh = static_cast<int>(blockIdx.x % a.num_kv_heads);
+  const int b = static_cast<int>(blockIdx.x / a.num_kv_heads);
+  const int g = a.group;
+  const int L = a.lens[b];
+  const int64_t head0 = int64_t(b) * a.num_q_heads + int64_t(kvh) * g;
+  if (!len_ok(L, a) || L == 0) {
+    const float fill = (L == 0) ? 0.f : __builtin_nanf("");
+    for (int e = lane; e < g * D; e += 64) a.out[head0 * D + e] = fill;
+    return;
+  }
+  const int total = total_blocks(a);
+  const int64_t G = int64_t(total) * a.num_kv_heads;
+  const int64_t per = balanced_per_wave(G, a.grid_waves);
+  const int64_t s = int64_t(kvh) * total + blocks_before(a, b);
+  const int64_t e = s + (L + kBlock - 1) / kBlock;
+  const int64_t w0 = s / per, w1 = (e - 1) / per;
+  if (w0 == w1) return;  // finished inside one wave
+  const bool split = (64 % g) == 0;
+  const int lanes_per_head = split ? 64 / g : 64;
+  const int h_first = split ? lane / lanes_per_head : 0;
+  const int h_step = split ? g : 1;
+  const int sub = split ? lane % lanes_per_head : lane;
+  for (int h = h_first; h < g; h += h_step) {
+    float M = -INFINITY;
+    bool bad = false;
+    for (int64_t w = w0; w <= w1; ++w) {
+      const int64_t slot = w * 2 + ((w == w0 && w0 * per < s) ? 1 : 0);
+      const float mv = a.bw_m[slot * g + h];
+      bad |= (mv != mv);
+      M = fmaxf(M, mv);
+    }
+    float den = 0.f;
+    for (int64_t w = w0; w <= w1; ++w) {
+      const int64_t slot = w * 2 + ((w == w0 && w0 * per < s) ? 1 : 0);
+      den = fmaf(__builtin_amdgcn_exp2f(a.bw_m[slot * g + h] - M), a.bw_l[slot * g + h], den);
+    }
+    const float inv = bad ? __builtin_nanf("") : 1.0f / den;
+    for (int d = sub; d < D; d += lanes_per_head) {
+      float acc = 0.f;
+      for (int64_t w = w0; w <= w1; ++w) {
+        const int64_t slot = w * 2 + ((w == w0 && w0 * per < s) ? 1 : 0);
+        acc = fmaf(__builtin_amdgcn_exp2f(a.bw_m[slot * g + h] - M),
+                   a.bw_o[(slot * g + h) * D + d], acc);
+      }
+      a.out[(head0 + h) * D + d] = acc * inv;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ A5: decode, fp32
 // One wave per (sequence, query head, partition); lane holds channels lane
 // and lane + 64.  Plain vector-ALU form for the fp32 cache.
@@ -337,9 +764,10 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
   constexpr int NE = D / 64;
   constexpr int64_t TILE = int64_t(kBlock) * D;
   const int lane = threadIdx.x;
-  const int part = blockIdx.x;
-  const int hq = blockIdx.y;
-  const int b = blockIdx.z;
+  const int64_t wid = blockIdx.x;  // query head fastest, then sequence, then partition
+  const int hq = static_cast<int>(wid % a.num_q_heads);
+  const int b = static_cast<int>((wid / a.num_q_heads) % a.num_seqs);
+  const int part = static_cast<int>(wid / (int64_t(a.num_q_heads) * a.num_seqs));
   const int kvh = hq / a.group;
   const int L = a.lens[b];
   const int64_t head = int64_t(b) * a.num_q_heads + hq;
@@ -404,40 +832,73 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ A6: LSE reduce
-// One wave per (sequence, query head) with more than one partition:
+// One wave per (sequence, kv head) -- kv head fastest, like the main kernel --
+// merging the partitions of each of its query heads:
 //   M = max_p m_p,  l = sum_p l_p 2^(m_p - M),  out = sum_p o_p 2^(m_p - M) / l
+// The wave's lanes are split evenly over the group's heads when the group
+// size divides 64 (each lane owns D*g/64 channels of one head); other group
+// sizes take the heads one after another with all 64 lanes.
 template <int D>
 __global__ __launch_bounds__(64) void lse_reduce_kernel(DecodeArgs a) {
-  constexpr int NE = D / 64;
   const int lane = threadIdx.x;
-  const int64_t head = blockIdx.x;  // b * Hq + hq
-  const int b = static_cast<int>(head / a.num_q_heads);
+  const int kvh = static_cast<int>(blockIdx.x % a.num_kv_heads);
+  const int b = static_cast<int>(blockIdx.x / a.num_kv_heads);
   const int L = a.lens[b];
   if (!len_ok(L, a) || L == 0) return;
   const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
   if (nparts <= 1) return;
-  const float* mp = a.ws_m + head * a.max_parts;
-  const float* lp = a.ws_l + head * a.max_parts;
-  const float* op = a.ws_o + head * a.max_parts * D;
-  float M = -INFINITY;
-  bool bad = false;
-  for (int p = 0; p < nparts; ++p) {
-    const float mv = mp[p];
-    bad |= (mv != mv);
-    M = fmaxf(M, mv);
+  const int g = a.group;
+  const bool split = (64 % g) == 0;
+  const int lanes_per_head = split ? 64 / g : 64;
+  const int h_first = split ? lane / lanes_per_head : 0;
+  const int h_step = split ? g : 1;
+  const int sub = split ? lane % lanes_per_head : lane;
+  for (int h = h_first; h < g; h += h_step) {
+    const int64_t head = int64_t(b) * a.num_q_heads + int64_t(kvh) * g + h;
+    const float* mp = a.ws_m + head * a.max_parts;
+    const float* lp = a.ws_l + head * a.max_parts;
+    const float* op = a.ws_o + head * a.max_parts * D;
+    float M = -INFINITY;
+    bool bad = false;
+    for (int p = 0; p < nparts; ++p) {
+      const float mv = mp[p];
+      bad |= (mv != mv);
+      M = fmaxf(M, mv);
+    }
+    float den = 0.f;
+    for (int p = 0; p < nparts; ++p) den = fmaf(__builtin_amdgcn_exp2f(mp[p] - M), lp[p], den);
+    const float inv = bad ? __builtin_nanf("") : 1.0f / den;
+    for (int d = sub; d < D; d += lanes_per_head) {
+      float acc = 0.f;
+      for (int p = 0; p < nparts; ++p)
+        acc = fmaf(__builtin_amdgcn_exp2f(mp[p] - M), op[int64_t(p) * D + d], acc);
+      a.out[head * D + d] = acc * inv;
+    }
   }
-  float acc[NE], den = 0.f;
+}
+
+// ------------------------------------------------------------------ measurement
+// Streaming read: workgroup w (one wavefront) reads its own contiguous chunk
+// with 1 KiB per load instruction and non-temporal 16-byte buffer loads
+// (the same access form as the decode kernel), folding the data into one
+// word per workgroup so the loads are not dead code.
+__global__ __launch_bounds__(64) void stream_read_kernel(const char* __restrict__ src, int64_t bytes,
+                                                         int64_t chunk, uint32_t* __restrict__ sink) {
+  const int64_t begin = int64_t(blockIdx.x) * chunk;
+  if (begin >= bytes) return;
+  const int n = static_cast<int>(min(chunk, bytes - begin));
+  const __amdgpu_buffer_rsrc_t r = tile_rsrc(src + begin, n);
+  uint32_t acc = 0;
+  for (int off = 0; off < n; off += 8 * 1024) {
+    uint4 v[8];
 #pragma unroll
-  for (int e = 0; e < NE; ++e) acc[e] = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = __builtin_amdgcn_exp2f(mp[p] - M);
-    den = fmaf(w, lp[p], den);
+    for (int u = 0; u < 8; ++u)
+      v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           r, off + u * 1024 + threadIdx.x * 16, 0, 2));
 #pragma unroll
-    for (int e = 0; e < NE; ++e) acc[e] = fmaf(w, op[int64_t(p) * D + lane + 64 * e], acc[e]);
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  const float inv = bad ? __builtin_nanf("") : 1.0f / den;
-#pragma unroll
-  for (int e = 0; e < NE; ++e) a.out[head * D + lane + 64 * e] = acc[e] * inv;
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // practically never taken
 }
 
 // ------------------------------------------------------------------ host helpers
@@ -446,14 +907,70 @@ bool debug_checks() {
   return v && v[0] == '1';
 }
 
+// PKV_DEBUG check of a device slot mapping: in range and unique.  Synchronizes.
+pkv_status check_slots(const int64_t* slot_mapping, int32_t num_tokens, int64_t num_slots,
+                       hipStream_t stream) {
+  std::vector<int64_t> host(num_tokens);
+  if (hipStreamSynchronize(stream) != hipSuccess ||
+      hipMemcpy(host.data(), slot_mapping, sizeof(int64_t) * num_tokens, hipMemcpyDeviceToHost) !=
+          hipSuccess)
+    return PKV_ERR_HIP;
+  std::vector<char> seen(num_slots, 0);
+  for (int64_t s : host) {
+    if (s < 0) continue;
+    if (s >= num_slots || seen[s]) return PKV_ERR_INVALID;
+    seen[s] = 1;
+  }
+  return PKV_OK;
+}
+
 pkv_status launch_status() {
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+// Blocks kept in flight per wavefront by the bf16 decode kernel (2..4);
+// PKV_DECODE_STAGES overrides the default for tuning.
+int pipeline_stages() {
+  static int st = [] {
+    const char* v = std::getenv("PKV_DECODE_STAGES");
+    int x = v ? std::atoi(v) : 0;
+    return (x >= 2 && x <= 4) ? x : 3;
+  }();
+  return st;
+}
+
+// Cache policy of the bf16 decode K/V loads (0, 2 = non-temporal, 18);
+// PKV_DECODE_CACHE overrides the default for tuning.
+int decode_cache_policy() {
+  static int aux = [] {
+    const char* v = std::getenv("PKV_DECODE_CACHE");
+    int x = v ? std::atoi(v) : 2;
+    return (x == 0 || x == 2 || x == 18) ? x : 2;
+  }();
+  return aux;
 }
 
 int elem_size(pkv_dtype dt) { return dt == PKV_F32 ? 4 : (dt == PKV_BF16 ? 2 : 0); }
 
 int resolve_partition(int32_t partition_size) {
   return partition_size == 0 ? kDefaultPartition : partition_size;
+}
+
+// Waves of the balanced decode grid: every wave slot of the current device
+// (8 one-wave workgroups per compute unit at the kernel's register use);
+// PKV_BALANCED_WAVES overrides it for tuning.  0 if the device query fails.
+int balanced_waves() {
+  const char* v = std::getenv("PKV_BALANCED_WAVES");
+  if (v && std::atoi(v) > 0) return std::atoi(v);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus * 8;
+}
+
+size_t balanced_workspace_bytes(int waves, int group, int head_dim) {
+  return size_t(waves) * 2 * group * (head_dim + 2) * sizeof(float);
 }
 
 int64_t max_parts_for(int32_t max_context_len, int part) {
@@ -469,6 +986,42 @@ Profiler g_prof;
 constexpr size_t kMaxProfiled = 8192;
 
 }  // namespace
+
+template <int D, int ST>
+void launch_decode_bf16_st(unsigned grid, hipStream_t stream, const DecodeArgs& a) {
+  switch (decode_cache_policy()) {
+    case 0: hipLaunchKernelGGL((decode_bf16_kernel<D, ST, 0>), grid, dim3(64), 0, stream, a); break;
+    case 18: hipLaunchKernelGGL((decode_bf16_kernel<D, ST, 18>), grid, dim3(64), 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_bf16_kernel<D, ST, 2>), grid, dim3(64), 0, stream, a); break;
+  }
+}
+
+void launch_decode_bf16(unsigned grid, hipStream_t stream, const DecodeArgs& a, int head_dim) {
+  const int st = pipeline_stages();
+  if (head_dim == 64) {
+    launch_decode_bf16_st<64, 4>(grid, stream, a);
+  } else if (st == 2) {
+    launch_decode_bf16_st<128, 2>(grid, stream, a);
+  } else if (st == 4) {
+    launch_decode_bf16_st<128, 4>(grid, stream, a);
+  } else {
+    launch_decode_bf16_st<128, 3>(grid, stream, a);
+  }
+}
+
+void launch_decode_bf16_balanced(unsigned grid, hipStream_t stream, const DecodeArgs& a,
+                                 int head_dim) {
+  const int aux = decode_cache_policy();
+  if (head_dim == 64) {
+    hipLaunchKernelGGL((decode_bf16_balanced_kernel<64, 3, 2>), grid, dim3(64), 0, stream, a);
+  } else if (aux == 0) {
+    hipLaunchKernelGGL((decode_bf16_balanced_kernel<128, 3, 0>), grid, dim3(64), 0, stream, a);
+  } else if (pipeline_stages() == 2) {
+    hipLaunchKernelGGL((decode_bf16_balanced_kernel<128, 2, 2>), grid, dim3(64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_bf16_balanced_kernel<128, 3, 2>), grid, dim3(64), 0, stream, a);
+  }
+}
 
 // ============================================================================ C ABI
 extern "C" {
@@ -498,17 +1051,8 @@ pkv_status paged_kv_write(const void* k_new, const void* v_new, const int64_t* s
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_INVALID;
   const int64_t num_slots = int64_t(num_blocks) * kBlock;
   if (debug_checks()) {
-    std::vector<int64_t> host(num_tokens);
-    if (hipStreamSynchronize(stream) != hipSuccess ||
-        hipMemcpy(host.data(), slot_mapping, sizeof(int64_t) * num_tokens,
-                  hipMemcpyDeviceToHost) != hipSuccess)
-      return PKV_ERR_HIP;
-    std::vector<char> seen(num_slots, 0);
-    for (int64_t s : host) {
-      if (s < 0) continue;
-      if (s >= num_slots || seen[s]) return PKV_ERR_INVALID;
-      seen[s] = 1;
-    }
+    pkv_status st = check_slots(slot_mapping, num_tokens, num_slots, stream);
+    if (st != PKV_OK) return st;
   }
   const int64_t total = int64_t(num_tokens) * num_kv_heads * (head_dim / 8);
   const int threads = 256;
@@ -523,6 +1067,44 @@ pkv_status paged_kv_write(const void* k_new, const void* v_new, const int64_t* s
                        static_cast<const float*>(k_new), static_cast<const float*>(v_new),
                        slot_mapping, static_cast<float*>(k_cache), static_cast<float*>(v_cache),
                        total, num_kv_heads, head_dim, num_slots);
+  }
+  return launch_status();
+}
+
+pkv_status paged_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                           void* k_cache, void* v_cache, int32_t num_tokens, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t num_blocks, pkv_dtype dtype,
+                           int32_t* block_tables, int64_t table_elems, const int32_t* updates,
+                           int32_t num_updates, hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
+      num_updates < 0 || table_elems < 0)
+    return PKV_ERR_INVALID;
+  if (head_dim % 32 != 0 || elem_size(dtype) == 0) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens > 0 && (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache))
+    return PKV_ERR_INVALID;
+  if (num_updates > 0 && (!block_tables || !updates)) return PKV_ERR_INVALID;
+  if (num_tokens == 0 && num_updates == 0) return PKV_OK;
+  const int64_t num_slots = int64_t(num_blocks) * kBlock;
+  if (debug_checks() && num_tokens > 0) {
+    pkv_status st = check_slots(slot_mapping, num_tokens, num_slots, stream);
+    if (st != PKV_OK) return st;
+  }
+  const int threads = 256;
+  const int table_wgs = (num_updates + threads - 1) / threads;
+  const int64_t total = int64_t(num_tokens) * num_kv_heads * (head_dim / 8);
+  const int64_t grid = table_wgs + (total + threads - 1) / threads;
+  if (dtype == PKV_BF16) {
+    hipLaunchKernelGGL(append_kernel<uint16_t>, dim3(grid), dim3(threads), 0, stream,
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                       slot_mapping, static_cast<uint16_t*>(k_cache),
+                       static_cast<uint16_t*>(v_cache), total, num_kv_heads, head_dim, num_slots,
+                       block_tables, table_elems, updates, num_updates, table_wgs);
+  } else {
+    hipLaunchKernelGGL(append_kernel<float>, dim3(grid), dim3(threads), 0, stream,
+                       static_cast<const float*>(k_new), static_cast<const float*>(v_new),
+                       slot_mapping, static_cast<float*>(k_cache), static_cast<float*>(v_cache),
+                       total, num_kv_heads, head_dim, num_slots, block_tables, table_elems,
+                       updates, num_updates, table_wgs);
   }
   return launch_status();
 }
@@ -547,8 +1129,13 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || partition_size < 0) return 0;
   const int part = resolve_partition(partition_size);
   const int64_t mp = max_parts_for(max_context_len, part);
-  if (mp <= 1) return 0;
-  return size_t(num_seqs) * num_q_heads * mp * (head_dim + 2) * sizeof(float);
+  size_t fixed = mp <= 1 ? 0 : size_t(num_seqs) * num_q_heads * mp * (head_dim + 2) * sizeof(float);
+  if (partition_size != 0) return fixed;
+  // partition_size 0: the balanced bf16 form (group of at most 16 heads)
+  // or 512-token partitions for fp32 -- room for either
+  const size_t bal = balanced_workspace_bytes(balanced_waves(), num_q_heads < 16 ? num_q_heads : 16,
+                                              head_dim);
+  return fixed > bal ? fixed : bal;
 }
 
 pkv_status paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -564,7 +1151,6 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
     return PKV_ERR_INVALID;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
   if (partition_size % 32 != 0) return PKV_ERR_INVALID;
-  if (num_seqs > 65535 || num_kv_heads > 65535 || num_q_heads > 65535) return PKV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (elem_size(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
   const int group = num_q_heads / num_kv_heads;
@@ -574,9 +1160,16 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
     return PKV_ERR_INVALID;
   const int part = resolve_partition(partition_size);
   const int64_t max_parts = max_parts_for(max_context_len, part);
-  if (max_parts > 65535) return PKV_ERR_UNSUPPORTED;
-  const size_t need = paged_attention_workspace_size(num_seqs, num_q_heads, head_dim,
-                                                     max_context_len, partition_size);
+  // one workgroup per (partition, sequence, head) must fit a 1D grid
+  if (max_parts * num_seqs * num_q_heads > 0x7FFFFFFF) return PKV_ERR_UNSUPPORTED;
+  const bool balanced = kv_dtype == PKV_BF16 && partition_size == 0;
+  const int waves = balanced ? balanced_waves() : 0;
+  if (balanced && waves <= 0) return PKV_ERR_HIP;
+  const size_t need =
+      balanced ? balanced_workspace_bytes(waves, group, head_dim)
+               : paged_attention_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                partition_size == 0 ? kDefaultPartition
+                                                                    : partition_size);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_INVALID;
 
   DecodeArgs a;
@@ -591,6 +1184,7 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
   a.ws_o = ws;
   a.ws_m = ws ? ws + heads * max_parts * head_dim : nullptr;
   a.ws_l = ws ? a.ws_m + heads * max_parts : nullptr;
+  a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.group = group;
@@ -600,17 +1194,33 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
   a.part_tokens = part;
   a.max_parts = static_cast<int>(max_parts);
   a.scale_log2e = scale * 1.4426950408889634f;
+  a.grid_waves = waves;
+  a.bw_o = balanced ? ws : nullptr;
+  a.bw_m = balanced ? ws + size_t(waves) * 2 * group * head_dim : nullptr;
+  a.bw_l = balanced ? a.bw_m + size_t(waves) * 2 * group : nullptr;
 
   const bool prof = g_prof.on && g_prof.used + 2 <= g_prof.pool.size();
   if (prof) (void)hipEventRecord(g_prof.pool[g_prof.used], stream);
-  if (kv_dtype == PKV_BF16) {
-    dim3 grid(static_cast<unsigned>(max_parts), num_kv_heads, num_seqs);
+  if (balanced) {
+    launch_decode_bf16_balanced(static_cast<unsigned>(waves), stream, a, head_dim);
+    if (prof) {
+      (void)hipEventRecord(g_prof.pool[g_prof.used + 1], stream);
+      g_prof.used += 2;
+    }
+    pkv_status st = launch_status();
+    if (st != PKV_OK) return st;
+    const unsigned mgrid = static_cast<unsigned>(int64_t(num_seqs) * num_kv_heads);
     if (head_dim == 128)
-      hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL(balanced_merge_kernel<128>, dim3(mgrid), dim3(64), 0, stream, a);
     else
-      hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL(balanced_merge_kernel<64>, dim3(mgrid), dim3(64), 0, stream, a);
+    return launch_status();
+  }
+  if (kv_dtype == PKV_BF16) {
+    const unsigned grid = static_cast<unsigned>(max_parts * num_seqs * num_kv_heads);
+    launch_decode_bf16(grid, stream, a, head_dim);
   } else {
-    dim3 grid(static_cast<unsigned>(max_parts), num_q_heads, num_seqs);
+    const unsigned grid = static_cast<unsigned>(max_parts * num_seqs * num_q_heads);
     if (head_dim == 128)
       hipLaunchKernelGGL(decode_f32_kernel<128>, grid, dim3(64), 0, stream, a);
     else
@@ -622,11 +1232,23 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
   }
   pkv_status st = launch_status();
   if (st != PKV_OK || max_parts <= 1) return st;
-  const unsigned rgrid = static_cast<unsigned>(heads);
+  const unsigned rgrid = static_cast<unsigned>(int64_t(num_seqs) * num_kv_heads);
   if (head_dim == 128)
     hipLaunchKernelGGL(lse_reduce_kernel<128>, dim3(rgrid), dim3(64), 0, stream, a);
   else
     hipLaunchKernelGGL(lse_reduce_kernel<64>, dim3(rgrid), dim3(64), 0, stream, a);
+  return launch_status();
+}
+
+pkv_status pkv_stream_read(const void* buf, size_t bytes, void* sink, hipStream_t stream) {
+  if (!buf || !sink || bytes < 16) return PKV_ERR_INVALID;
+  constexpr int kGrid = 8192;
+  const int64_t total = static_cast<int64_t>(bytes & ~size_t(15));
+  // per-workgroup chunks of whole KiB, each below 2 GiB
+  const int64_t chunk = ((total + kGrid - 1) / kGrid + 1023) & ~int64_t(1023);
+  if (chunk >= (int64_t(1) << 31)) return PKV_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(kGrid), dim3(64), 0, stream,
+                     static_cast<const char*>(buf), total, chunk, static_cast<uint32_t*>(sink));
   return launch_status();
 }
 

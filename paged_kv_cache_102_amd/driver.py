@@ -115,13 +115,12 @@ class PagedKV:
         slots, upd, cows = capi.paged_kv_append_slots(self.pool, self.tables, self.lens, num_new)
         d_slots, d_upd, d_cows, d_lens = self._upload([slots, upd, cows, self.lens], stream)
         s = stream.cuda_stream
-        capi.paged_block_table_update(self.tables_d, d_upd, s)
-        with torch.cuda.stream(stream):
-            self.lens_d.copy_(d_lens)
+        # the uploaded lengths become the device lengths (no extra copy)
+        self.lens_d = d_lens
         capi.paged_kv_copy_blocks(self.k_cache, self.v_cache, d_cows, self.num_kv_heads,
                                   self.head_dim, self.num_blocks, s)
-        capi.paged_kv_write(k_new, v_new, d_slots, self.k_cache, self.v_cache, self.num_kv_heads,
-                            self.head_dim, self.num_blocks, s)
+        capi.paged_kv_append(k_new, v_new, d_slots, self.k_cache, self.v_cache, self.num_kv_heads,
+                             self.head_dim, self.num_blocks, self.tables_d, d_upd, s)
         return slots, upd, cows
 
     def decode(self, q, scale: float, out=None, stream=None, partition_size=None):
