@@ -153,6 +153,7 @@ def main():
     for _ in range(steps):
         step()
         bytes_total += kv_bytes(kv.lens, s.num_kv_heads, s.head_dim)
+    t_issued = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     nlaunch, kern_ms = capi.pkv_profile_end()
@@ -217,6 +218,7 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(s.num_seqs * steps / dt, 1),
         "decode_only": dec,
+        "host_issue_ms_per_step": round((t_issued - t0) * 1e3 / steps, 4),
         "kv_waste_fraction": round(waste, 5),
         "pool_usage_percent": round(stats["usage_percent"], 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

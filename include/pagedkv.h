@@ -247,8 +247,10 @@ pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pai
 /* Bytes of scratch paged_attention_decode needs for these sizes.  For
  * partition_size > 0 it is 0 when every context fits one partition; for
  * partition_size 0 it covers both the balanced bf16 split (two partial
- * states per wavefront of the current device's grid) and 512-token fp32
- * partitions.  Queries the current device (returns 0 if that fails). */
+ * states per wavefront of the current device's grid, plus one 8-byte arrival
+ * counter per sequence and kv head) and 512-token fp32 partitions.  Queries
+ * the current device (returns 0 if that fails).  The counters carry a tag
+ * of the launch that wrote them, so the workspace never needs clearing. */
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                       int32_t max_context_len, int32_t partition_size);
 
@@ -269,7 +271,10 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int
  * that many tokens.  partition_size == 0 (bf16): balanced split -- all
  * (kv head, sequence, block) tiles form one list and every wavefront of a
  * fixed grid (8 per compute unit) takes an equal contiguous slice of it,
- * across sequence boundaries; for fp32, 0 means 512-token partitions.
+ * across sequence boundaries; a sequence split over several wavefronts is
+ * merged by the last of them to finish, inside the same launch; for fp32,
+ * 0 means 512-token partitions.  Concurrent calls must not share a
+ * workspace.
  *
  *   q, k_cache, v_cache, block_tables, context_lens, workspace: device, read
  *   out: device fp32, written

@@ -204,6 +204,8 @@ struct DecodeArgs {
   float* bw_o;
   float* bw_m;
   float* bw_l;
+  unsigned long long* bw_count;  // [num_seqs * num_kv_heads]: epoch << 32 | arrivals
+  unsigned epoch;                // distinct for every balanced launch
   int grid_waves;
 };
 
@@ -441,26 +443,6 @@ __device__ inline int wave_sum_int(int x) {
   return __builtin_amdgcn_readfirstlane(x);
 }
 
-// Blocks per kv head over all sequences.
-__device__ inline int total_blocks(const DecodeArgs& a) {
-  int total = 0;
-  for (int c = 0; c < a.num_seqs; c += 64) {
-    const int b = c + static_cast<int>(threadIdx.x);
-    total += wave_sum_int(b < a.num_seqs ? nblocks_of(a, a.lens[b]) : 0);
-  }
-  return total;
-}
-
-// Blocks of the sequences before b (per kv head).
-__device__ inline int blocks_before(const DecodeArgs& a, int b) {
-  int sum = 0;
-  for (int c = 0; c < b; c += 64) {
-    const int s = c + static_cast<int>(threadIdx.x);
-    sum += wave_sum_int(s < b ? nblocks_of(a, a.lens[s]) : 0);
-  }
-  return sum;
-}
-
 __device__ inline int64_t balanced_per_wave(int64_t G, int waves) {
   constexpr int64_t kMinBlocks = 8;
   const int64_t per = (G + waves - 1) / waves;
@@ -483,32 +465,69 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
   const int Hkv = a.num_kv_heads;
   const int64_t wid = blockIdx.x;
 
-  const int total = total_blocks(a);
+  // sequences with no work: zeros for an empty context, NaN for a bad length
+  for (int b = static_cast<int>(wid); b < B; b += gridDim.x) {
+    const int L = a.lens[b];
+    if (!len_ok(L, a) || L == 0) {
+      const float fill = (L == 0) ? 0.f : __builtin_nanf("");
+      for (int e = lane; e < a.num_q_heads * D; e += 64)
+        a.out[int64_t(b) * a.num_q_heads * D + e] = fill;
+    }
+  }
+  // Block counts per sequence, 4 sequences per lane and 256 per pass: the
+  // total over all sequences, then the tile where this wave's slice starts
+  // (kv head, then sequence by a prefix scan).  For up to 256 sequences the
+  // counts stay in registers, so this costs one round of length loads.
+  int cnt[4];
+  auto load_counts = [&](int c) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int b = c + lane * 4 + k;
+      cnt[k] = b < B ? nblocks_of(a, a.lens[b]) : 0;
+    }
+  };
+  auto lane_scan = [&](int x) {  // inclusive prefix over lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(x, d);
+      if (lane >= d) x += up;
+    }
+    return x;
+  };
+  int total = 0;
+  for (int c = 0; c < B; c += 256) {
+    load_counts(c);
+    total += wave_sum_int(cnt[0] + cnt[1] + cnt[2] + cnt[3]);
+  }
   const int64_t G = int64_t(total) * Hkv;
   const int64_t per = balanced_per_wave(G, a.grid_waves);
   const int64_t g0 = wid * per;
   if (g0 >= G) return;
   const int64_t g1 = min(g0 + per, G);
 
-  // locate the first tile of the slice: kv head, then sequence by a scan of
-  // the per-sequence block counts
   int c_kvh = static_cast<int>(g0 / total);
   int rem = static_cast<int>(g0 - int64_t(c_kvh) * total);
   int c_b = 0, c_blk = 0;
-  for (int c = 0, base = 0; c < B; c += 64) {
-    const int b = c + lane;
-    const int nb = b < B ? nblocks_of(a, a.lens[b]) : 0;
-    int incl = nb;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int up = __shfl_up(incl, d);
-      if (lane >= d) incl += up;
-    }
+  for (int c = 0, base = 0; c < B; c += 256) {
+    if (B > 256) load_counts(c);  // else still in registers from the total
+    const int mine = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    const int incl = lane_scan(mine);
     const int chunk_total = __builtin_amdgcn_readlane(incl, 63);
     if (rem < base + chunk_total) {
       const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > rem);
       const int pos = static_cast<int>(__builtin_ctzll(hit));
-      c_b = c + pos;
-      c_blk = rem - (base + __builtin_amdgcn_readlane(incl, pos) - __builtin_amdgcn_readlane(nb, pos));
+      int r = rem - (base + __builtin_amdgcn_readlane(incl, pos) - __builtin_amdgcn_readlane(mine, pos));
+      int k = 0;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const int nq = __builtin_amdgcn_readlane(cnt[q], pos);
+        if (k == q && r >= nq) {
+          r -= nq;
+          k = q + 1;
+        }
+      }
+      c_b = c + pos * 4 + k;
+      c_blk = r;
       break;
     }
     base += chunk_total;
@@ -581,7 +600,13 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
   float m = -INFINITY, lsum = 0.f;
   bool seg_bad = false;
   int seg_first_blk = 0;
+  int64_t seg_start_idx = g0;
   bool seg_is_first = true;  // the segment that starts the slice
+  // partial segments left for the merge: item (b * Hkv + kvh) and its start
+  // in the tile list, per slot (-1: none)
+  int part_item[2] = {-1, -1};
+  int64_t part_start[2] = {0, 0};
+  int part_nb[2] = {0, 0};
 
   auto end_segment = [&](bool complete) {
     const float lt = group_sum(lsum);
@@ -599,20 +624,30 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
         }
       }
     } else {
-      const int64_t slot = wid * 2 + (seg_is_first ? 0 : 1);
+      // partial state for the merge, written with device-scope (relaxed
+      // atomic) stores: the wave that merges may run on another XCD, whose
+      // L2 is not coherent with this one
+      const int sl = seg_is_first ? 0 : 1;
+      const int64_t slot = wid * 2 + sl;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = grp * 4 + r;
         if (h < g) {
           float* dst = a.bw_o + (slot * g + h) * D + hcol;
 #pragma unroll
-          for (int n = 0; n < NT; ++n) dst[16 * n] = o[n][r];
+          for (int n = 0; n < NT; ++n)
+            __hip_atomic_store(dst + 16 * n, o[n][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
       if (lane < g) {
-        a.bw_m[slot * g + lane] = seg_bad ? __builtin_nanf("") : m;
-        a.bw_l[slot * g + lane] = lt;
+        __hip_atomic_store(a.bw_m + slot * g + lane, seg_bad ? __builtin_nanf("") : m,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.bw_l + slot * g + lane, lt, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
+      part_item[sl] = c_b * Hkv + c_kvh;
+      part_start[sl] = seg_start_idx - seg_first_blk;
+      part_nb[sl] = c_nb;
     }
     seg_is_first = false;
   };
@@ -627,6 +662,7 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
       lsum = 0.f;
       seg_bad = false;
       seg_first_blk = c_blk;
+      seg_start_idx = idx;
     }
     seg_bad |= st_bad[st];
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -698,60 +734,100 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
       issue(st);
     }
   }
-}
 
-// Merge for the balanced form: one wave per (sequence, kv head).  Writes
-// zeros for an empty context and NaN for a bad length; for a sequence whose
-// blocks were split over waves w0..w1, merges their partial states (slot 1
-// of w0 when w0's slice began before the sequence, else slot 0).
-template <int D>
-__global__ __launch_bounds__(64) void balanced_merge_kernel(DecodeArgs a) {
-  const int lane = threadIdx.x;
-  const int kvh = static_cast<int>(blockIdx.x % a.num_kv_heads);
-  const int b = static_cast<int>(blockIdx.x / a.num_kv_heads);
-  const int g = a.group;
-  const int L = a.lens[b];
-  const int64_t head0 = int64_t(b) * a.num_q_heads + int64_t(kvh) * g;
-  if (!len_ok(L, a) || L == 0) {
-    const float fill = (L == 0) ? 0.f : __builtin_nanf("");
-    for (int e = lane; e < g * D; e += 64) a.out[head0 * D + e] = fill;
-    return;
-  }
-  const int total = total_blocks(a);
-  const int64_t G = int64_t(total) * a.num_kv_heads;
-  const int64_t per = balanced_per_wave(G, a.grid_waves);
-  const int64_t s = int64_t(kvh) * total + blocks_before(a, b);
-  const int64_t e = s + (L + kBlock - 1) / kBlock;
-  const int64_t w0 = s / per, w1 = (e - 1) / per;
-  if (w0 == w1) return;  // finished inside one wave
-  const bool split = (64 % g) == 0;
-  const int lanes_per_head = split ? 64 / g : 64;
-  const int h_first = split ? lane / lanes_per_head : 0;
-  const int h_step = split ? g : 1;
-  const int sub = split ? lane % lanes_per_head : lane;
-  for (int h = h_first; h < g; h += h_step) {
-    float M = -INFINITY;
-    bool bad = false;
-    for (int64_t w = w0; w <= w1; ++w) {
-      const int64_t slot = w * 2 + ((w == w0 && w0 * per < s) ? 1 : 0);
-      const float mv = a.bw_m[slot * g + h];
-      bad |= (mv != mv);
-      M = fmaxf(M, mv);
-    }
-    float den = 0.f;
-    for (int64_t w = w0; w <= w1; ++w) {
-      const int64_t slot = w * 2 + ((w == w0 && w0 * per < s) ? 1 : 0);
-      den = fmaf(__builtin_amdgcn_exp2f(a.bw_m[slot * g + h] - M), a.bw_l[slot * g + h], den);
-    }
-    const float inv = bad ? __builtin_nanf("") : 1.0f / den;
-    for (int d = sub; d < D; d += lanes_per_head) {
-      float acc = 0.f;
-      for (int64_t w = w0; w <= w1; ++w) {
-        const int64_t slot = w * 2 + ((w == w0 && w0 * per < s) ? 1 : 0);
-        acc = fmaf(__builtin_amdgcn_exp2f(a.bw_m[slot * g + h] - M),
-                   a.bw_o[(slot * g + h) * D + d], acc);
+  // Partial segments: once this wave's device-scope stores of its partial
+  // states have completed (vmcnt 0 -- the same ordering the compiler uses
+  // for an agent-scope release of atomic data, without an L2 write-back,
+  // since nothing here is left dirty in L2), count an arrival on the
+  // sequence's counter; the wave that brings the count to the number of
+  // waves sharing the sequence merges, reading the states with device-scope
+  // loads (no L2 invalidate needed for them).
+  if (part_item[0] < 0 && part_item[1] < 0) return;
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int sl = 0; sl < 2; ++sl) {
+    const int item = part_item[sl];
+    if (item < 0) continue;
+    const int64_t s0 = part_start[sl];
+    const int64_t w0 = s0 / per, w1 = (s0 + part_nb[sl] - 1) / per;
+    const unsigned need = static_cast<unsigned>(w1 - w0 + 1);
+    unsigned arrived = 0;
+    if (lane == 0) {
+      unsigned long long* cp = a.bw_count + item;
+      unsigned long long old = __hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned long long nv = 0;
+      for (int tries = 0; tries < (1 << 20); ++tries) {
+        nv = (unsigned(old >> 32) == a.epoch) ? old + 1
+                                              : ((static_cast<unsigned long long>(a.epoch) << 32) | 1ull);
+        if (__hip_atomic_compare_exchange_weak(cp, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+          break;
       }
-      a.out[(head0 + h) * D + d] = acc * inv;
+      arrived = static_cast<unsigned>(nv);
+    }
+    arrived = __builtin_amdgcn_readlane(arrived, 0);
+    if (arrived != need) continue;
+    __asm__ volatile("" ::: "memory");
+    // merge: slot 1 of w0 when w0's slice began before the sequence, else
+    // slot 0; partial states are folded in batches of kMergeBatch waves
+    // (all loads of a batch in flight together), with a running maximum
+    const int b = item / Hkv, kvh = item % Hkv;
+    const int64_t head0 = int64_t(b) * a.num_q_heads + int64_t(kvh) * g;
+    const bool split = (64 % g) == 0;
+    const int lanes_per_head = split ? 64 / g : 64;
+    const int h_first = split ? lane / lanes_per_head : 0;
+    const int h_step = split ? g : 1;
+    const int sub = split ? lane % lanes_per_head : lane;
+    const int nd = D / lanes_per_head;  // channels per lane (<= D / 4)
+    constexpr int kMergeBatch = 4;
+    constexpr int NDMAX = D / 4;
+    for (int h = h_first; h < g; h += h_step) {
+      float M = -INFINITY, den = 0.f;
+      float acc[NDMAX];
+#pragma unroll
+      for (int k = 0; k < NDMAX; ++k) acc[k] = 0.f;
+      bool bad = false;
+      for (int64_t wb = w0; wb <= w1; wb += kMergeBatch) {
+        float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch][NDMAX];
+#pragma unroll
+        for (int c = 0; c < kMergeBatch; ++c) {
+          const int64_t w = wb + c;
+          const bool live = w <= w1;
+          const int64_t slot = w * 2 + ((w == w0 && w0 * per < s0) ? 1 : 0);
+          const int64_t mi = live ? slot * g + h : 0;
+          mv[c] = live ? __hip_atomic_load(a.bw_m + mi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : -INFINITY;
+          lv[c] = live ? __hip_atomic_load(a.bw_l + mi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : 0.f;
+#pragma unroll
+          for (int k = 0; k < NDMAX; ++k)
+            ov[c][k] = (live && k < nd)
+                           ? __hip_atomic_load(a.bw_o + mi * D + sub + k * lanes_per_head,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.f;
+        }
+        float mc = M;
+#pragma unroll
+        for (int c = 0; c < kMergeBatch; ++c) {
+          bad |= (mv[c] != mv[c]);
+          mc = fmaxf(mc, mv[c]);
+        }
+        const float keep = __builtin_amdgcn_exp2f(M - mc);
+        den *= keep;
+#pragma unroll
+        for (int k = 0; k < NDMAX; ++k) acc[k] *= keep;
+#pragma unroll
+        for (int c = 0; c < kMergeBatch; ++c) {
+          const float f = __builtin_amdgcn_exp2f(mv[c] - mc);
+          den = fmaf(f, lv[c], den);
+#pragma unroll
+          for (int k = 0; k < NDMAX; ++k) acc[k] = fmaf(f, ov[c][k], acc[k]);
+        }
+        M = mc;
+      }
+      const float inv = bad ? __builtin_nanf("") : 1.0f / den;
+#pragma unroll
+      for (int k = 0; k < NDMAX; ++k)
+        if (k < nd) a.out[(head0 + h) * D + sub + k * lanes_per_head] = acc[k] * inv;
     }
   }
 }
@@ -969,8 +1045,21 @@ int balanced_waves() {
   return cus * 8;
 }
 
-size_t balanced_workspace_bytes(int waves, int group, int head_dim) {
-  return size_t(waves) * 2 * group * (head_dim + 2) * sizeof(float);
+// Balanced-mode scratch: per wave two partial states (D + 2 floats per head
+// of the group), then one 8-byte arrival counter per (sequence, kv head).
+size_t balanced_states_bytes(int waves, int group, int head_dim) {
+  return (size_t(waves) * 2 * group * (head_dim + 2) * sizeof(float) + 255) & ~size_t(255);
+}
+size_t balanced_workspace_bytes(int waves, int group, int head_dim, int64_t seq_heads) {
+  return balanced_states_bytes(waves, group, head_dim) + size_t(seq_heads) * 8;
+}
+
+// Launch tag for the arrival counters: a counter left by an earlier launch
+// carries an older tag and is read as zero, so counters never need clearing.
+unsigned next_epoch() {
+  static unsigned e = 0x5EED0001u;
+  e = e + 1 == 0 ? 1 : e + 1;
+  return e;
 }
 
 int64_t max_parts_for(int32_t max_context_len, int part) {
@@ -1134,7 +1223,7 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int
   // partition_size 0: the balanced bf16 form (group of at most 16 heads)
   // or 512-token partitions for fp32 -- room for either
   const size_t bal = balanced_workspace_bytes(balanced_waves(), num_q_heads < 16 ? num_q_heads : 16,
-                                              head_dim);
+                                              head_dim, int64_t(num_seqs) * num_q_heads);
   return fixed > bal ? fixed : bal;
 }
 
@@ -1166,7 +1255,7 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
   const int waves = balanced ? balanced_waves() : 0;
   if (balanced && waves <= 0) return PKV_ERR_HIP;
   const size_t need =
-      balanced ? balanced_workspace_bytes(waves, group, head_dim)
+      balanced ? balanced_workspace_bytes(waves, group, head_dim, int64_t(num_seqs) * num_kv_heads)
                : paged_attention_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
                                                 partition_size == 0 ? kDefaultPartition
                                                                     : partition_size);
@@ -1198,6 +1287,11 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
   a.bw_o = balanced ? ws : nullptr;
   a.bw_m = balanced ? ws + size_t(waves) * 2 * group * head_dim : nullptr;
   a.bw_l = balanced ? a.bw_m + size_t(waves) * 2 * group : nullptr;
+  a.bw_count = balanced ? reinterpret_cast<unsigned long long*>(
+                              static_cast<char*>(workspace) +
+                              balanced_states_bytes(waves, group, head_dim))
+                        : nullptr;
+  a.epoch = balanced ? next_epoch() : 0;
 
   const bool prof = g_prof.on && g_prof.used + 2 <= g_prof.pool.size();
   if (prof) (void)hipEventRecord(g_prof.pool[g_prof.used], stream);
@@ -1207,13 +1301,6 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
       (void)hipEventRecord(g_prof.pool[g_prof.used + 1], stream);
       g_prof.used += 2;
     }
-    pkv_status st = launch_status();
-    if (st != PKV_OK) return st;
-    const unsigned mgrid = static_cast<unsigned>(int64_t(num_seqs) * num_kv_heads);
-    if (head_dim == 128)
-      hipLaunchKernelGGL(balanced_merge_kernel<128>, dim3(mgrid), dim3(64), 0, stream, a);
-    else
-      hipLaunchKernelGGL(balanced_merge_kernel<64>, dim3(mgrid), dim3(64), 0, stream, a);
     return launch_status();
   }
   if (kv_dtype == PKV_BF16) {
