@@ -214,7 +214,8 @@ def main():
         "config": {"workload": WORKLOAD, "num_seqs": s.num_seqs, "num_q_heads": s.num_q_heads,
                    "num_kv_heads": s.num_kv_heads, "head_dim": s.head_dim, "block_size": 16,
                    "mean_context": round(float(kv.lens.mean()), 1),
-                   "partition_tokens": args.partition or 512, "parallelism": "single-gpu"},
+                   "split": "balanced" if args.partition == 0 else f"{args.partition}-token partitions",
+                   "parallelism": "single-gpu"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(s.num_seqs * steps / dt, 1),
         "decode_only": dec,
@@ -223,7 +224,9 @@ def main():
         "pool_usage_percent": round(stats["usage_percent"], 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_bf16_kernel<128>",
+                     "traffic": traffic,
+                     "kernel": ("decode_bf16_balanced_kernel<128,2,2> (split merge inside)"
+                                if args.partition == 0 else "decode_bf16_kernel<128,3,2>"),
                      "avg_launch_ms": round(avg_kernel_ms, 5), "launches": nlaunch,
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
         "hbm_read_ceiling_gbs": round(ceiling, 1) if ceiling else None,

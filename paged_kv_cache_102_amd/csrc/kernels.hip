@@ -465,25 +465,31 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
   const int Hkv = a.num_kv_heads;
   const int64_t wid = blockIdx.x;
 
-  // sequences with no work: zeros for an empty context, NaN for a bad length
-  for (int b = static_cast<int>(wid); b < B; b += gridDim.x) {
-    const int L = a.lens[b];
-    if (!len_ok(L, a) || L == 0) {
-      const float fill = (L == 0) ? 0.f : __builtin_nanf("");
-      for (int e = lane; e < a.num_q_heads * D; e += 64)
-        a.out[int64_t(b) * a.num_q_heads * D + e] = fill;
-    }
-  }
   // Block counts per sequence, 4 sequences per lane and 256 per pass: the
   // total over all sequences, then the tile where this wave's slice starts
   // (kv head, then sequence by a prefix scan).  For up to 256 sequences the
-  // counts stay in registers, so this costs one round of length loads.
-  int cnt[4];
+  // lengths stay in registers, so the start costs one round of length loads.
+  int lenv[4], cnt[4];
   auto load_counts = [&](int c) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int b = c + lane * 4 + k;
-      cnt[k] = b < B ? nblocks_of(a, a.lens[b]) : 0;
+      lenv[k] = b < B ? a.lens[b] : 0;
+      cnt[k] = b < B ? nblocks_of(a, lenv[k]) : 0;
+    }
+  };
+  // wave w writes the rows of the sequences b = w (mod grid) that have no
+  // work: zeros for an empty context, NaN for a bad length
+  auto fill_empty = [&](int c) {
+    for (int b = static_cast<int>(wid); b < B; b += gridDim.x) {
+      if (b < c || b >= c + 256) continue;
+      const int pos = (b - c) >> 2, k = (b - c) & 3;
+      const int L = __builtin_amdgcn_readlane(k == 0 ? lenv[0] : k == 1 ? lenv[1] : k == 2 ? lenv[2] : lenv[3], pos);
+      if (!len_ok(L, a) || L == 0) {
+        const float fill = (L == 0) ? 0.f : __builtin_nanf("");
+        for (int e = lane; e < a.num_q_heads * D; e += 64)
+          a.out[int64_t(b) * a.num_q_heads * D + e] = fill;
+      }
     }
   };
   auto lane_scan = [&](int x) {  // inclusive prefix over lanes
@@ -497,6 +503,7 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
   int total = 0;
   for (int c = 0; c < B; c += 256) {
     load_counts(c);
+    fill_empty(c);
     total += wave_sum_int(cnt[0] + cnt[1] + cnt[2] + cnt[3]);
   }
   const int64_t G = int64_t(total) * Hkv;
@@ -507,7 +514,7 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
 
   int c_kvh = static_cast<int>(g0 / total);
   int rem = static_cast<int>(g0 - int64_t(c_kvh) * total);
-  int c_b = 0, c_blk = 0;
+  int c_b = 0, c_blk = 0, c_L = 0;
   for (int c = 0, base = 0; c < B; c += 256) {
     if (B > 256) load_counts(c);  // else still in registers from the total
     const int mine = cnt[0] + cnt[1] + cnt[2] + cnt[3];
@@ -528,13 +535,15 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
       }
       c_b = c + pos * 4 + k;
       c_blk = r;
+      c_L = __builtin_amdgcn_readlane(
+          k == 0 ? lenv[0] : k == 1 ? lenv[1] : k == 2 ? lenv[2] : lenv[3], pos);
       break;
     }
     base += chunk_total;
   }
   c_b = __builtin_amdgcn_readfirstlane(c_b);
   c_blk = __builtin_amdgcn_readfirstlane(c_blk);
-  int c_L = a.lens[c_b];
+  c_L = __builtin_amdgcn_readfirstlane(c_L);
   int c_nb = nblocks_of(a, c_L);
 
   // the load cursor starts where the compute cursor starts
@@ -602,11 +611,13 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
   int seg_first_blk = 0;
   int64_t seg_start_idx = g0;
   bool seg_is_first = true;  // the segment that starts the slice
-  // partial segments left for the merge: item (b * Hkv + kvh) and its start
-  // in the tile list, per slot (-1: none)
-  int part_item[2] = {-1, -1};
-  int64_t part_start[2] = {0, 0};
-  int part_nb[2] = {0, 0};
+  // partial segments left for the merge: item (b * Hkv + kvh), its start in
+  // the tile list and its block count, per slot (-1: none).  Plain scalars,
+  // not arrays: a runtime-indexed private array would be placed in LDS, whose
+  // per-lane addressing reads the dispatch packet from host memory at start.
+  int part_item0 = -1, part_item1 = -1;
+  int64_t part_start0 = 0, part_start1 = 0;
+  int part_nb0 = 0, part_nb1 = 0;
 
   auto end_segment = [&](bool complete) {
     const float lt = group_sum(lsum);
@@ -645,9 +656,15 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
         __hip_atomic_store(a.bw_l + slot * g + lane, lt, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
-      part_item[sl] = c_b * Hkv + c_kvh;
-      part_start[sl] = seg_start_idx - seg_first_blk;
-      part_nb[sl] = c_nb;
+      if (sl == 0) {
+        part_item0 = c_b * Hkv + c_kvh;
+        part_start0 = seg_start_idx - seg_first_blk;
+        part_nb0 = c_nb;
+      } else {
+        part_item1 = c_b * Hkv + c_kvh;
+        part_start1 = seg_start_idx - seg_first_blk;
+        part_nb1 = c_nb;
+      }
     }
     seg_is_first = false;
   };
@@ -742,13 +759,14 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
   // sequence's counter; the wave that brings the count to the number of
   // waves sharing the sequence merges, reading the states with device-scope
   // loads (no L2 invalidate needed for them).
-  if (part_item[0] < 0 && part_item[1] < 0) return;
+  if (part_item0 < 0 && part_item1 < 0) return;
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   for (int sl = 0; sl < 2; ++sl) {
-    const int item = part_item[sl];
+    const int item = sl == 0 ? part_item0 : part_item1;
     if (item < 0) continue;
-    const int64_t s0 = part_start[sl];
-    const int64_t w0 = s0 / per, w1 = (s0 + part_nb[sl] - 1) / per;
+    const int64_t s0 = sl == 0 ? part_start0 : part_start1;
+    const int nbs = sl == 0 ? part_nb0 : part_nb1;
+    const int64_t w0 = s0 / per, w1 = (s0 + nbs - 1) / per;
     const unsigned need = static_cast<unsigned>(w1 - w0 + 1);
     unsigned arrived = 0;
     if (lane == 0) {
@@ -1026,6 +1044,14 @@ int decode_cache_policy() {
   return aux;
 }
 
+// The balanced kernel also keeps the next segment's query fragments per
+// stage, so it defaults to 2 stages (measured as fast as 3 on MI355X, with
+// fewer registers); PKV_DECODE_STAGES=3 selects 3.
+int pipeline_stages_balanced() {
+  const char* v = std::getenv("PKV_DECODE_STAGES");
+  return (v && std::atoi(v) == 3) ? 3 : 2;
+}
+
 int elem_size(pkv_dtype dt) { return dt == PKV_F32 ? 4 : (dt == PKV_BF16 ? 2 : 0); }
 
 int resolve_partition(int32_t partition_size) {
@@ -1105,10 +1131,10 @@ void launch_decode_bf16_balanced(unsigned grid, hipStream_t stream, const Decode
     hipLaunchKernelGGL((decode_bf16_balanced_kernel<64, 3, 2>), grid, dim3(64), 0, stream, a);
   } else if (aux == 0) {
     hipLaunchKernelGGL((decode_bf16_balanced_kernel<128, 3, 0>), grid, dim3(64), 0, stream, a);
-  } else if (pipeline_stages() == 2) {
-    hipLaunchKernelGGL((decode_bf16_balanced_kernel<128, 2, 2>), grid, dim3(64), 0, stream, a);
-  } else {
+  } else if (pipeline_stages_balanced() == 3) {
     hipLaunchKernelGGL((decode_bf16_balanced_kernel<128, 3, 2>), grid, dim3(64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_bf16_balanced_kernel<128, 2, 2>), grid, dim3(64), 0, stream, a);
   }
 }
 

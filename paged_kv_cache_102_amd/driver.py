@@ -25,16 +25,23 @@ BLOCK = capi.BLOCK_SIZE
 
 
 class _Staging:
-    """A ring of pinned host buffers so that uploads stay asynchronous."""
+    """A ring of pinned host buffers so that uploads stay asynchronous.
 
-    def __init__(self, nbytes: int, depth: int = 4):
+    The copy runs on its own stream (default priority): a step's slots,
+    table deltas and lengths depend only on the host plan, not on the
+    previous step's attention, so their upload overlaps the previous decode
+    and the compute stream only waits on the copy's event."""
+
+    def __init__(self, nbytes: int, device, depth: int = 4):
         self.bufs = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(depth)]
         self.events = [None] * depth
         self.i = 0
+        self.copy_stream = torch.cuda.Stream(device)
 
     def put(self, arrays, device, stream):
         """Packs numpy arrays (8-byte aligned pieces) into the next pinned
-        buffer and copies them to ``device``; returns device views."""
+        buffer and copies them to ``device``; returns device views that
+        ``stream`` may use (it waits for the copy)."""
         k = self.i
         self.i = (self.i + 1) % len(self.bufs)
         if self.events[k] is not None:
@@ -47,10 +54,12 @@ class _Staging:
             n = a.nbytes
             host[off:off + n] = np.ascontiguousarray(a).view(np.uint8).ravel()
             off += (n + 7) & ~7
-        with torch.cuda.stream(stream):
+        with torch.cuda.stream(self.copy_stream):
             dev = buf[:max(off, 8)].to(device, non_blocking=True)
             ev = torch.cuda.Event()
-            ev.record(stream)
+            ev.record(self.copy_stream)
+        dev.record_stream(stream)
+        stream.wait_event(ev)
         self.events[k] = ev
         views = []
         for a, o in zip(arrays, offs):
@@ -93,7 +102,7 @@ class PagedKV:
     def _upload(self, arrays, stream):
         need = sum((a.nbytes + 7) & ~7 for a in arrays) + 8
         if self._staging is None or self._staging.bufs[0].numel() < need:
-            self._staging = _Staging(max(need, 1 << 16))
+            self._staging = _Staging(max(need, 1 << 16), self.device)
         return self._staging.put(arrays, self.device, stream)
 
     def share_prefix(self, src: int, dsts, num_blocks: int):
