@@ -248,10 +248,12 @@ pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pai
  * partition_size > 0 it is 0 when every context fits one partition; for
  * partition_size 0 it covers both the balanced bf16 split (two partial
  * states per wavefront of the current device's grid, plus one 8-byte arrival
- * counter per sequence and kv head) and 512-token fp32 partitions.  Queries
- * the current device (returns 0 if that fails).  The counters carry a tag
- * of the launch that wrote them, so the workspace never needs clearing. */
-size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+ * counter per sequence and kv head) and 512-token fp32 partitions.  Queries the current
+ * device (returns 0 if that fails, or for invalid sizes).  The counters
+ * carry a tag of the launch that wrote them, so the workspace never needs
+ * clearing. */
+size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
                                       int32_t max_context_len, int32_t partition_size);
 
 /* Decode attention: one query token per sequence attends over its whole

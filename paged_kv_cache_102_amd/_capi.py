@@ -56,7 +56,7 @@ _SIGS = {
     "paged_kv_copy_blocks": (C.c_int, [_vp, _vp, _vp, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                        C.c_int, _vp]),
     "paged_attention_workspace_size": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32, C.c_int32,
-                                                    C.c_int32]),
+                                                    C.c_int32, C.c_int32]),
     "paged_attention_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32, C.c_int32,
                                          C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_float,
                                          C.c_int32, _vp, C.c_size_t, C.c_int, _vp, _vp]),
@@ -255,9 +255,9 @@ def paged_kv_copy_blocks(k_cache, v_cache, pairs, num_kv_heads: int, head_dim: i
            "paged_kv_copy_blocks")
 
 
-def paged_attention_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
-                                   partition_size=0) -> int:
-    return int(_lib.paged_attention_workspace_size(num_seqs, num_q_heads, head_dim,
+def paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   max_context_len, partition_size=0) -> int:
+    return int(_lib.paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                    max_context_len, partition_size))
 
 

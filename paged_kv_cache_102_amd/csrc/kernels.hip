@@ -431,6 +431,14 @@ void decode_bf16_kernel(DecodeArgs a) {
 // (output written directly); at most the first and the last segment of a
 // wave are partial, and their (o, m, l) states go to slots 0 and 1 of that
 // wave for the merge kernel.
+// Load of a wave-uniform element through the scalar data cache (read-only
+// constant address space): it waits on the scalar counter, so it does not
+// drain the vector loads in flight, as a vector load with a full wait would.
+__device__ inline int load_uniform(const int* p, int64_t i) {
+  using const_int_ptr = const __attribute__((address_space(4))) int*;
+  return *((const_int_ptr)p + i);
+}
+
 __device__ inline int nblocks_of(const DecodeArgs& a, int L) {
   return len_ok(L, a) ? (L + kBlock - 1) / kBlock : 0;
 }
@@ -560,7 +568,7 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
           break;
         }
       }
-      L = a.lens[b];
+      L = load_uniform(a.lens, b);
       nb = nblocks_of(a, L);
     }
   };
@@ -576,8 +584,7 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
   int64_t l_idx = g0;
   auto issue = [&](int st) {
     const bool live = l_idx < g1;
-    int phys = __builtin_amdgcn_readfirstlane(
-        a.tables[int64_t(l_b) * a.max_blocks + (live ? l_blk : 0)]);
+    int phys = load_uniform(a.tables, int64_t(l_b) * a.max_blocks + (live ? l_blk : 0));
     bool bad = false;
     int bytes = live ? TILE_BYTES : 0;
     if (live && (phys < 0 || phys >= a.num_blocks)) {
@@ -1239,17 +1246,21 @@ pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pai
   return launch_status();
 }
 
-size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
                                       int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || partition_size < 0) return 0;
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      partition_size < 0 || num_q_heads % num_kv_heads != 0)
+    return 0;
   const int part = resolve_partition(partition_size);
   const int64_t mp = max_parts_for(max_context_len, part);
   size_t fixed = mp <= 1 ? 0 : size_t(num_seqs) * num_q_heads * mp * (head_dim + 2) * sizeof(float);
   if (partition_size != 0) return fixed;
   // partition_size 0: the balanced bf16 form (group of at most 16 heads)
   // or 512-token partitions for fp32 -- room for either
-  const size_t bal = balanced_workspace_bytes(balanced_waves(), num_q_heads < 16 ? num_q_heads : 16,
-                                              head_dim, int64_t(num_seqs) * num_q_heads);
+  const int group = num_q_heads / num_kv_heads;
+  const size_t bal = balanced_workspace_bytes(balanced_waves(), group < 16 ? group : 16, head_dim,
+                                              int64_t(num_seqs) * num_kv_heads);
   return fixed > bal ? fixed : bal;
 }
 
@@ -1282,7 +1293,8 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
   if (balanced && waves <= 0) return PKV_ERR_HIP;
   const size_t need =
       balanced ? balanced_workspace_bytes(waves, group, head_dim, int64_t(num_seqs) * num_kv_heads)
-               : paged_attention_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+               : paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                max_context_len,
                                                 partition_size == 0 ? kDefaultPartition
                                                                     : partition_size);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_INVALID;

@@ -93,7 +93,7 @@ class PagedKV:
         self.lens = np.zeros(num_seqs, dtype=np.int32)
         self.tables_d = torch.from_numpy(self.tables).to(self.device)
         self.lens_d = torch.from_numpy(self.lens).to(self.device)
-        ws = capi.paged_attention_workspace_size(num_seqs, num_q_heads, head_dim,
+        ws = capi.paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                  max_blocks_per_seq * BLOCK, partition_size)
         self.workspace = torch.empty(max(ws // 4, 1), dtype=torch.float32, device=self.device)
         self._staging = None
@@ -139,7 +139,8 @@ class PagedKV:
         ps = self.partition_size if partition_size is None else partition_size
         max_ctx = int(self.lens.max()) if self.lens.size else 0
         ws = self.workspace
-        need = capi.paged_attention_workspace_size(self.num_seqs, self.num_q_heads, self.head_dim,
+        need = capi.paged_attention_workspace_size(self.num_seqs, self.num_q_heads,
+                                                   self.num_kv_heads, self.head_dim,
                                                    max_ctx, ps)
         if need > ws.numel() * 4:
             ws = self.workspace = torch.empty(need // 4, dtype=torch.float32, device=self.device)
