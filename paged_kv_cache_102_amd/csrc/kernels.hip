@@ -207,6 +207,10 @@ struct DecodeArgs {
   unsigned long long* bw_count;  // [num_seqs * num_kv_heads]: epoch << 32 | arrivals
   unsigned epoch;                // distinct for every balanced launch
   int grid_waves;
+  // per-CU form: overflow partial-state slots, fixed share of each
+  // wavefront (per mille of the CU's range), minimum chunk size in tiles
+  float* cu_over;
+  int static_permille, chunk_min;
 };
 
 // Length check shared by the kernels: a bad length poisons the sequence.
@@ -857,6 +861,526 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ A5: decode, bf16, per-CU balanced
+// The same tile list, split first into one contiguous range per compute
+// unit (one workgroup of 8 wavefronts per CU, holding all of its LDS).
+// Inside a CU the work adapts to how fast each wavefront is served: each
+// wavefront starts with a fixed share of the CU's range, then the rest is
+// handed out in chunks of C tiles claimed from a counter in LDS.  Partial
+// segments (at unit boundaries) go to slots, in LDS while it lasts, then in
+// a per-CU overflow area of the workspace; after a workgroup barrier the
+// wavefronts fold the slots of each sequence: a sequence wholly inside the
+// CU's range is finished there, one that crosses the range boundary leaves
+// one partial state per CU in global memory, merged (as in the per-wave
+// form) by the last CU to arrive.  Claims and slot grants are LDS atomics,
+// so nothing in the walk waits on vector memory beyond its own loads.
+constexpr int kCuWaves = 8;
+constexpr int kCuLdsBytes = 160 * 1024;
+constexpr int kCuChunksMax = 64;                           // chunks per CU
+constexpr int kCuSlots = 2 * (kCuWaves + kCuChunksMax);    // partial segments per CU
+constexpr int kCuHeaderBytes = 64 + kCuSlots * 3 * 4;      // counters + slot metadata
+
+// Partial-state slots: m and l [slot][group], then o [slot][group][D].
+__host__ __device__ inline int cu_state_floats(int group, int head_dim) {
+  return group * (head_dim + 2);
+}
+// Slots that fit in LDS next to the header (the rest overflow).
+__host__ __device__ inline int cu_lds_slots(int group, int head_dim) {
+  const int n = (kCuLdsBytes - kCuHeaderBytes) / (cu_state_floats(group, head_dim) * 4);
+  return n > kCuSlots ? kCuSlots : n;
+}
+
+template <int D, int ST, int AUX>
+__global__ __launch_bounds__(64 * kCuWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_bf16_cu_kernel(DecodeArgs a) {
+  constexpr int NJ = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int64_t TILE = int64_t(kBlock) * D;
+  constexpr int TILE_BYTES = static_cast<int>(TILE * 2);
+  constexpr int NW = kCuWaves;
+  constexpr int NKMAX = 8;  // folded elements per lane: group * D / 64 <= 8
+
+  __shared__ __align__(16) unsigned char smem[kCuLdsBytes];
+  const int g = a.group;
+  const int cap = cu_lds_slots(g, D);  // slots held in LDS
+  int* hdr = reinterpret_cast<int*>(smem);
+  int* s_item = hdr + 16;
+  int* s_s0 = s_item + kCuSlots;
+  int* s_nb = s_s0 + kCuSlots;
+  float* s_m = reinterpret_cast<float*>(smem + kCuHeaderBytes);
+  float* s_l = s_m + cap * g;
+  float* s_o = s_l + cap * g;
+  // overflow slots of this CU in the workspace, [m g][l g][o g*D] per slot.
+  // LDS and global slots are accessed on separate branches, so each access
+  // compiles to an LDS or a global instruction (a pointer that could be
+  // either would become a flat access, which the compiler waits on with the
+  // vector-memory counter).
+  float* const o_base = a.cu_over + int64_t(blockIdx.x) * (kCuSlots - cap) * cu_state_floats(g, D);
+
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (scalar register): everything derived from it stays uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hcol = lane & 15;
+  const int grp = lane >> 4;
+  const int B = a.num_seqs;
+  const int Hkv = a.num_kv_heads;
+  const int wg = blockIdx.x;
+  const int NWG = gridDim.x;
+
+  // lengths and block counts of up to 256 sequences, 4 per lane; the loads
+  // go through a buffer resource sized to the B lengths (reads past them
+  // return 0), so all four are issued together
+  int lenv[4], cnt[4];
+  {
+    const __amdgpu_buffer_rsrc_t rl = tile_rsrc(a.lens, B * 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      lenv[k] = __builtin_amdgcn_raw_buffer_load_b32(rl, (lane * 4 + k) * 4, 0, 0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cnt[k] = nblocks_of(a, lenv[k]);
+  }
+  auto pick = [](const int (&v)[4], int k) {
+    return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
+  };
+  // rows of sequences with no work: zeros for an empty context, NaN for a
+  // bad length, spread over all wavefronts of the grid
+  for (int b = wg * NW + wave; b < B; b += NWG * NW) {
+    const int L = __builtin_amdgcn_readlane(pick(lenv, b & 3), b >> 2);
+    if (!len_ok(L, a) || L == 0) {
+      const float fill = (L == 0) ? 0.f : __builtin_nanf("");
+      for (int e = lane; e < a.num_q_heads * D; e += 64)
+        a.out[int64_t(b) * a.num_q_heads * D + e] = fill;
+    }
+  }
+  const int mine = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+  int incl = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int up = __shfl_up(incl, d);
+    if (lane >= d) incl += up;
+  }
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  const int G = total * Hkv;  // < 2^31 (checked on the host)
+
+  // this CU's range, the fixed share of each wavefront and the chunk size
+  const int pc = G > 0 ? (G + NWG - 1) / NWG : 1;
+  const int R0 = min(wg * pc, G);
+  const int R1 = min(R0 + pc, G);
+  const int S = static_cast<int>((int64_t(R1 - R0) * a.static_permille / 1000) / NW);
+  const int Rs = R0 + NW * S;
+  int C = (R1 - Rs + kCuChunksMax - 1) / kCuChunksMax;
+  if (C < a.chunk_min) C = a.chunk_min;
+  if (threadIdx.x == 0) {
+    hdr[0] = Rs;  // next unclaimed tile
+    hdr[1] = 0;   // slots used
+  }
+  __syncthreads();
+
+  // tile index -> (kv head, sequence, block, length, block count), from registers
+  auto locate = [&](int t, int& kvh, int& b, int& blk, int& L, int& nb) {
+    kvh = t / total;
+    const int rem = t - kvh * total;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > rem);
+    const int pos = static_cast<int>(__builtin_ctzll(hit));
+    int r = rem - (__builtin_amdgcn_readlane(incl, pos) - __builtin_amdgcn_readlane(mine, pos));
+    int k = 0;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int nq = __builtin_amdgcn_readlane(cnt[q], pos);
+      if (k == q && r >= nq) {
+        r -= nq;
+        k = q + 1;
+      }
+    }
+    b = __builtin_amdgcn_readfirstlane(pos * 4 + k);
+    blk = __builtin_amdgcn_readfirstlane(r);
+    L = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(pick(lenv, k), pos));
+    nb = nblocks_of(a, L);
+  };
+  auto advance = [&](int& kvh, int& b, int& blk, int& L, int& nb) {
+    ++blk;
+    while (blk >= nb) {  // skips empty sequences
+      blk = 0;
+      if (++b == B) {
+        b = 0;
+        if (++kvh == Hkv) {  // past the list: park (never used for a live load)
+          kvh = 0;
+          nb = 1 << 30;
+          break;
+        }
+      }
+      L = load_uniform(a.lens, b);
+      nb = nblocks_of(a, L);
+    }
+  };
+  // claims the next chunk of the CU's range: [s, e), empty when none is left
+  auto claim = [&](int& s, int& e) {
+    int cs = 0;
+    if (lane == 0) cs = atomicAdd(&hdr[0], C);
+    cs = __builtin_amdgcn_readfirstlane(cs);
+    s = min(cs, R1);
+    e = min(cs + C, R1);
+  };
+
+  // load cursor: the fixed share first (or a first claim when there is none)
+  int l_us = R0 + wave * S, l_ue = R0 + (wave + 1) * S;
+  if (S == 0) claim(l_us, l_ue);
+  bool l_live = l_us < l_ue;
+  int l_idx = l_us;
+  int l_kvh = 0, l_b = 0, l_blk = 0, l_L = 0, l_nb = 1;
+  if (l_live) locate(l_us, l_kvh, l_b, l_blk, l_L, l_nb);
+
+  const int64_t block_bytes = int64_t(Hkv) * TILE_BYTES;
+  const int loff = lane * 16;
+  const int qoff = (hcol * D + grp * 8) * 2;  // >= g*D*2 for padded heads: reads as 0
+  const int qbytes = g * D * 2;
+
+  uint4 kr[ST][NJ], vr[ST][NJ], qr[ST][NJ];
+  bool st_bad[ST], rec_live[ST], rec_first[ST], rec_last[ST];
+  int rec_kvh[ST], rec_b[ST], rec_blk[ST], rec_L[ST], rec_nb[ST], rec_idx[ST];
+
+  auto issue = [&](int st) {
+    const bool live = l_live;
+    rec_live[st] = live;
+    rec_kvh[st] = l_kvh;
+    rec_b[st] = l_b;
+    rec_blk[st] = l_blk;
+    rec_L[st] = l_L;
+    rec_nb[st] = l_nb;
+    rec_idx[st] = l_idx;
+    rec_first[st] = l_idx == l_us;
+    rec_last[st] = l_idx == l_ue - 1;
+    int phys = live ? load_uniform(a.tables, int64_t(l_b) * a.max_blocks + l_blk) : 0;
+    bool bad = false;
+    int bytes = live ? TILE_BYTES : 0;
+    if (live && (phys < 0 || phys >= a.num_blocks)) {
+      bad = true;
+      bytes = 0;
+    }
+    const int64_t off = (bytes ? int64_t(phys) * block_bytes : 0) + int64_t(l_kvh) * TILE_BYTES;
+    const char* kc = static_cast<const char*>(a.kc) + off;
+    const char* vc = static_cast<const char*>(a.vc) + off;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc, bytes);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc, bytes);
+    const bool needq = live && (l_blk == 0 || l_idx == l_us);
+    const char* qb = static_cast<const char*>(a.q) +
+                     (int64_t(l_b) * a.num_q_heads + int64_t(l_kvh) * g) * D * 2;
+    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(qb, needq ? qbytes : 0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      kr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + 1024 * j, 0, AUX));
+      vr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + 1024 * j, 0, AUX));
+      qr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 64 * j, 0, 0));
+    }
+    st_bad[st] = bad;
+    if (live) {
+      if (l_idx == l_ue - 1) {
+        claim(l_us, l_ue);
+        l_live = l_us < l_ue;
+        l_idx = l_us;
+        if (l_live) locate(l_us, l_kvh, l_b, l_blk, l_L, l_nb);
+      } else {
+        advance(l_kvh, l_b, l_blk, l_L, l_nb);
+        ++l_idx;
+      }
+    }
+  };
+
+  bf16x8 qf[NJ];
+  f32x4 o[NT];
+  float m = -INFINITY, lsum = 0.f;
+  bool seg_bad = false;
+  int seg_first_blk = 0;
+  int seg_start_idx = 0;
+
+  auto end_segment = [&](bool complete, int c_b, int c_kvh, int c_nb) {
+    const float lt = group_sum(lsum);
+    if (complete) {
+      const int64_t head0 = int64_t(c_b) * a.num_q_heads + int64_t(c_kvh) * g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = grp * 4 + r;
+        const float lr = __shfl(lt, h);
+        const float inv = seg_bad ? __builtin_nanf("") : 1.0f / lr;
+        if (h < g) {
+          float* dst = a.out + (head0 + h) * D + hcol;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) dst[16 * n] = o[n][r] * inv;
+        }
+      }
+    } else {
+      // (at most 2 per unit and 8 + kCuChunksMax units per CU: the slot
+      // index stays below kCuSlots)
+      int slot = 0;
+      if (lane == 0) slot = atomicAdd(&hdr[1], 1);
+      slot = __builtin_amdgcn_readfirstlane(slot);
+      const float mv = seg_bad ? __builtin_nanf("") : m;
+      if (slot < cap) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = grp * 4 + r;
+          if (h < g) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) s_o[(slot * g + h) * D + hcol + 16 * n] = o[n][r];
+          }
+        }
+        if (lane < g) {
+          s_m[slot * g + lane] = mv;
+          s_l[slot * g + lane] = lt;
+        }
+      } else {
+        float* const base = o_base + (slot - cap) * cu_state_floats(g, D);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = grp * 4 + r;
+          if (h < g) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) base[2 * g + h * D + hcol + 16 * n] = o[n][r];
+          }
+        }
+        if (lane < g) {
+          base[lane] = mv;
+          base[g + lane] = lt;
+        }
+      }
+      if (lane == 0) {
+        s_item[slot] = c_b * Hkv + c_kvh;
+        s_s0[slot] = seg_start_idx - seg_first_blk;
+        s_nb[slot] = c_nb;
+      }
+    }
+  };
+
+  auto compute = [&](int st) {
+    const int c_blk = rec_blk[st], c_L = rec_L[st], c_nb = rec_nb[st];
+    if (c_blk == 0 || rec_first[st]) {  // a segment starts: its Q came with this block
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) qf[j] = __builtin_bit_cast(bf16x8, qr[st][j]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m = -INFINITY;
+      lsum = 0.f;
+      seg_bad = false;
+      seg_first_blk = c_blk;
+      seg_start_idx = rec_idx[st];
+    }
+    seg_bad |= st_bad[st];
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[st][j]), qf[j], s,
+                                                   0, 0, 0);
+    const int tb = c_blk * kBlock + grp * 4;
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = (tb + r < c_L) ? s[r] * a.scale_log2e : -INFINITY;
+    float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mloc = group_max(mloc);
+    const float mnew = fmaxf(m, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sv[r] - mnew);
+    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    m = mnew;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, grp * 4 + r);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) o[n][r] *= ar;
+      }
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hi[r] = bf16_bits_rne(p[r]);
+      lo[r] = bf16_bits_rne(p[r] - __uint_as_float(hi[r] << 16));
+    }
+    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
+    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
+    if (c_blk * kBlock + kBlock > c_L) {
+      const uint32_t m01 = (tb + 0 < c_L ? 0x0000FFFFu : 0u) | (tb + 1 < c_L ? 0xFFFF0000u : 0u);
+      const uint32_t m23 = (tb + 2 < c_L ? 0x0000FFFFu : 0u) | (tb + 3 < c_L ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        vr[st][j].x &= m01;
+        vr[st][j].y &= m23;
+        vr[st][j].z &= m01;
+        vr[st][j].w &= m23;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const s16x4 v0 = __builtin_bit_cast(s16x4, make_uint2(vr[st][j].x, vr[st][j].y));
+      const s16x4 v1 = __builtin_bit_cast(s16x4, make_uint2(vr[st][j].z, vr[st][j].w));
+      o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, v0, o[2 * j], 0, 0, 0);
+      o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, v0, o[2 * j], 0, 0, 0);
+      o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, v1, o[2 * j + 1], 0, 0, 0);
+      o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, v1, o[2 * j + 1], 0, 0, 0);
+    }
+    const bool last_of_seq = (c_blk == c_nb - 1);
+    if (last_of_seq || rec_last[st])
+      end_segment(last_of_seq && seg_first_blk == 0, rec_b[st], rec_kvh[st], c_nb);
+  };
+
+  // Every trip issues every stage (a stage past the end issues zero-size
+  // loads), so the number of loads in flight at each wait is the same on all
+  // paths and the compiler's waits stay partial.  Stages are filled in tile
+  // order, so a dead stage 0 means all stages are dead.
+#pragma unroll
+  for (int st = 0; st < ST; ++st) issue(st);
+  while (rec_live[0]) {
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      if (rec_live[st]) compute(st);
+      issue(st);
+    }
+  }
+  // overflow slots were written with plain stores by other wavefronts of
+  // this workgroup: complete them before the barrier
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // Fold the slots of each sequence.  Wavefront w leads the slots s = w
+  // (mod 8) that are the first slot of their sequence; lane element k is
+  // channel (64 k + lane) of the group's heads, head (64 k + lane) / D.
+  const int nsl = hdr[1];
+  const int nk = g * D / 64;
+  for (int s = wave; s < nsl; s += NW) {
+    const int item = s_item[s];
+    bool dup = false;
+    for (int j0 = 0; j0 < s && !dup; j0 += 64) {
+      const int j = j0 + lane;
+      dup = __builtin_amdgcn_ballot_w64(j < s && s_item[j] == item) != 0;
+    }
+    if (dup) continue;
+    float acc[NKMAX], M[NKMAX], den[NKMAX];
+#pragma unroll
+    for (int k = 0; k < NKMAX; ++k) {
+      acc[k] = 0.f;
+      M[k] = -INFINITY;
+      den[k] = 0.f;
+    }
+    bool bad = false;
+    for (int j = s; j < nsl; ++j) {
+      if (s_item[j] != item) continue;
+#pragma unroll
+      for (int k = 0; k < NKMAX; ++k) {
+        if (k < nk) {
+          const int e = 64 * k + lane;
+          const int h = (64 * k) / D;
+          float mj, lj, oj;
+          if (j < cap) {
+            mj = s_m[j * g + h];
+            lj = s_l[j * g + h];
+            oj = s_o[j * g * D + e];
+          } else {
+            const float* base = o_base + (j - cap) * cu_state_floats(g, D);
+            mj = base[h];
+            lj = base[g + h];
+            oj = base[2 * g + e];
+          }
+          bad |= (mj != mj);
+          const float mn = fmaxf(M[k], mj);
+          const float fo = __builtin_amdgcn_exp2f(M[k] - mn);
+          const float fn = __builtin_amdgcn_exp2f(mj - mn);
+          acc[k] = acc[k] * fo + oj * fn;
+          den[k] = den[k] * fo + lj * fn;
+          M[k] = mn;
+        }
+      }
+    }
+    const int s0 = s_s0[s], nbs = s_nb[s];
+    const int b = item / Hkv, kvh = item % Hkv;
+    const int64_t head0 = int64_t(b) * a.num_q_heads + int64_t(kvh) * g;
+    const bool cross_start = s0 < R0, cross_end = s0 + nbs > R1;
+    if (!cross_start && !cross_end) {
+#pragma unroll
+      for (int k = 0; k < NKMAX; ++k)
+        if (k < nk) a.out[head0 * D + 64 * k + lane] = bad ? __builtin_nanf("") : acc[k] / den[k];
+    } else {
+      // this CU's share of a sequence that crosses its range: slot 0 when
+      // the sequence begins at or before the range start, else slot 1
+      const int64_t slot = int64_t(wg) * 2 + (s0 <= R0 ? 0 : 1);
+#pragma unroll
+      for (int k = 0; k < NKMAX; ++k) {
+        if (k < nk) {
+          const int e = 64 * k + lane;
+          const int h = (64 * k) / D;
+          __hip_atomic_store(a.bw_o + slot * g * D + e, acc[k], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+          if ((e % D) == 0) {
+            __hip_atomic_store(a.bw_m + slot * g + h, bad ? __builtin_nanf("") : M[k],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.bw_l + slot * g + h, den[k], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+      // once the stores have completed, count this CU's arrival
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // arrival: the CU that brings the count to the number of CU ranges
+      // covering the sequence merges their partial states
+      const int w0 = s0 / pc, w1 = (s0 + nbs - 1) / pc;
+      const unsigned need = static_cast<unsigned>(w1 - w0 + 1);
+      unsigned arrived = 0;
+      if (lane == 0) {
+        unsigned long long* cp = a.bw_count + item;
+        unsigned long long old = __hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned long long nv = 0;
+        for (int tries = 0; tries < (1 << 20); ++tries) {
+          nv = (unsigned(old >> 32) == a.epoch)
+                   ? old + 1
+                   : ((static_cast<unsigned long long>(a.epoch) << 32) | 1ull);
+          if (__hip_atomic_compare_exchange_weak(cp, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            break;
+        }
+        arrived = static_cast<unsigned>(nv);
+      }
+      arrived = __builtin_amdgcn_readlane(arrived, 0);
+      if (arrived != need) continue;
+      __asm__ volatile("" ::: "memory");
+      float gacc[NKMAX], gM[NKMAX], gden[NKMAX];
+#pragma unroll
+      for (int k = 0; k < NKMAX; ++k) {
+        gacc[k] = 0.f;
+        gM[k] = -INFINITY;
+        gden[k] = 0.f;
+      }
+      bool gbad = false;
+      for (int w = w0; w <= w1; ++w) {
+        const int64_t gs = int64_t(w) * 2 + ((w == w0 && int64_t(w0) * pc < s0) ? 1 : 0);
+#pragma unroll
+        for (int k = 0; k < NKMAX; ++k) {
+          if (k < nk) {
+            const int e = 64 * k + lane;
+            const int h = (64 * k) / D;
+            const float mj = __hip_atomic_load(a.bw_m + gs * g + h, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+            const float lj = __hip_atomic_load(a.bw_l + gs * g + h, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+            const float oj = __hip_atomic_load(a.bw_o + gs * g * D + e, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+            gbad |= (mj != mj);
+            const float mn = fmaxf(gM[k], mj);
+            const float fo = __builtin_amdgcn_exp2f(gM[k] - mn);
+            const float fn = __builtin_amdgcn_exp2f(mj - mn);
+            gacc[k] = gacc[k] * fo + oj * fn;
+            gden[k] = gden[k] * fo + lj * fn;
+            gM[k] = mn;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NKMAX; ++k)
+        if (k < nk)
+          a.out[head0 * D + 64 * k + lane] = gbad ? __builtin_nanf("") : gacc[k] / gden[k];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ A5: decode, fp32
 // One wave per (sequence, query head, partition); lane holds channels lane
 // and lane + 64.  Plain vector-ALU form for the fp32 cache.
@@ -1078,13 +1602,48 @@ int balanced_waves() {
   return cus * 8;
 }
 
+// Compute units of the current device (0 if the query fails).
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
 // Balanced-mode scratch: per wave two partial states (D + 2 floats per head
-// of the group), then one 8-byte arrival counter per (sequence, kv head).
+// of the group), then the per-CU overflow slots of the per-CU form, then one
+// 8-byte arrival counter per (sequence, kv head).
 size_t balanced_states_bytes(int waves, int group, int head_dim) {
   return (size_t(waves) * 2 * group * (head_dim + 2) * sizeof(float) + 255) & ~size_t(255);
 }
+size_t cu_overflow_bytes(int cus, int group, int head_dim) {
+  const int over = kCuSlots - cu_lds_slots(group, head_dim);
+  return (size_t(cus) * over * cu_state_floats(group, head_dim) * sizeof(float) + 255) &
+         ~size_t(255);
+}
 size_t balanced_workspace_bytes(int waves, int group, int head_dim, int64_t seq_heads) {
-  return balanced_states_bytes(waves, group, head_dim) + size_t(seq_heads) * 8;
+  return balanced_states_bytes(waves, group, head_dim) +
+         cu_overflow_bytes(device_cus(), group, head_dim) + size_t(seq_heads) * 8;
+}
+
+// Per-CU form parameters: each wavefront's fixed share of its CU's range
+// (per mille) and the smallest chunk.  The default gives the whole range to
+// fixed shares: on MI355X a CU finishes its range at the same time whether
+// its wavefronts share it out dynamically or not (the CU's aggregate read
+// rate is the limit, and wavefronts that finish early leave it to the
+// others), and chunks only add partial states.  PKV_CU_STATIC_PERMILLE and
+// PKV_CU_CHUNK_MIN override them for tuning and tests, PKV_DECODE_SPLIT=wave
+// selects the per-wave form.
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* v = std::getenv(name);
+  if (!v) return dflt;
+  const int x = std::atoi(v);
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+bool cu_split_enabled() {
+  const char* v = std::getenv("PKV_DECODE_SPLIT");
+  return !(v && std::strcmp(v, "wave") == 0);
 }
 
 // Launch tag for the arrival counters: a counter left by an earlier launch
@@ -1142,6 +1701,15 @@ void launch_decode_bf16_balanced(unsigned grid, hipStream_t stream, const Decode
     hipLaunchKernelGGL((decode_bf16_balanced_kernel<128, 3, 2>), grid, dim3(64), 0, stream, a);
   } else {
     hipLaunchKernelGGL((decode_bf16_balanced_kernel<128, 2, 2>), grid, dim3(64), 0, stream, a);
+  }
+}
+
+void launch_decode_bf16_cu(unsigned grid, hipStream_t stream, const DecodeArgs& a, int head_dim) {
+  const dim3 block(64 * kCuWaves);
+  if (head_dim == 64) {
+    hipLaunchKernelGGL((decode_bf16_cu_kernel<64, 3, 2>), grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_bf16_cu_kernel<128, 2, 2>), grid, block, 0, stream, a);
   }
 }
 
@@ -1325,16 +1893,32 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
   a.bw_o = balanced ? ws : nullptr;
   a.bw_m = balanced ? ws + size_t(waves) * 2 * group * head_dim : nullptr;
   a.bw_l = balanced ? a.bw_m + size_t(waves) * 2 * group : nullptr;
+  const int cus = balanced ? device_cus() : 0;
+  a.cu_over = balanced ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                  balanced_states_bytes(waves, group, head_dim))
+                       : nullptr;
   a.bw_count = balanced ? reinterpret_cast<unsigned long long*>(
                               static_cast<char*>(workspace) +
-                              balanced_states_bytes(waves, group, head_dim))
+                              balanced_states_bytes(waves, group, head_dim) +
+                              cu_overflow_bytes(cus, group, head_dim))
                         : nullptr;
   a.epoch = balanced ? next_epoch() : 0;
+  a.static_permille = env_int("PKV_CU_STATIC_PERMILLE", 1000, 0, 1000);
+  a.chunk_min = env_int("PKV_CU_CHUNK_MIN", 4, 1, 1 << 20);
+  // per-CU form: up to 256 sequences (lengths held in registers), a tile
+  // list indexed in 32 bits, at most 8 folded elements per lane, and
+  // partial-state slots for 2 CUs per wave of the per-wave grid
+  const bool cu_form = balanced && cu_split_enabled() && num_seqs <= 256 &&
+                       int64_t(num_seqs) * max_blocks_per_seq * num_kv_heads < (int64_t(1) << 31) &&
+                       group * head_dim / 64 <= 8 && cus > 0 && cus * 2 <= waves * 2;
 
   const bool prof = g_prof.on && g_prof.used + 2 <= g_prof.pool.size();
   if (prof) (void)hipEventRecord(g_prof.pool[g_prof.used], stream);
   if (balanced) {
-    launch_decode_bf16_balanced(static_cast<unsigned>(waves), stream, a, head_dim);
+    if (cu_form)
+      launch_decode_bf16_cu(static_cast<unsigned>(cus), stream, a, head_dim);
+    else
+      launch_decode_bf16_balanced(static_cast<unsigned>(waves), stream, a, head_dim);
     if (prof) {
       (void)hipEventRecord(g_prof.pool[g_prof.used + 1], stream);
       g_prof.used += 2;

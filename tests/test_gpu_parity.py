@@ -190,6 +190,39 @@ def test_table_update_and_fused_append():
     assert torch.equal(t2.cpu(), exp)
 
 
+# (fixed share per mille, smallest chunk): fixed shares only, the default,
+# chunks only, 1-tile chunks
+_CU_SPLITS = [("1000", "4"), ("600", "4"), ("0", "4"), ("300", "1")]
+
+
+@pytest.mark.parametrize("key", ["gqa-8b-bf16", "long-70b-bf16", "mha-7b-bf16"])
+def test_cu_split_any_mix(key, monkeypatch):
+    """The per-CU balanced form folds partial states in LDS (spilling to
+    the workspace when LDS is full) and merges sequences that cross CU
+    ranges in global memory: every mix of fixed shares and chunks gives the
+    oracle's answer, repeatedly, and agrees with fixed 512-token partitions
+    and with the per-wave form."""
+    w = synth.generate(key)
+    p = _pair(w)
+    B = w.spec.num_seqs
+    sample = list(range(0, B, max(1, B // 16))) + [B - 1]
+    ref = p.kv.decode(p.q, w.spec.scale, partition_size=512).cpu()
+    monkeypatch.setenv("PKV_DECODE_SPLIT", "wave")
+    per_wave = p.kv.decode(p.q, w.spec.scale, partition_size=0).cpu()
+    assert (per_wave - ref).abs().max().item() < 5e-5
+    monkeypatch.delenv("PKV_DECODE_SPLIT")
+    for permille, cmin in _CU_SPLITS:
+        monkeypatch.setenv("PKV_CU_STATIC_PERMILLE", permille)
+        monkeypatch.setenv("PKV_CU_CHUNK_MIN", cmin)
+        print(f"[cu split] {key} permille={permille} chunk_min={cmin}", flush=True)
+        for _ in range(3):
+            p.kv.workspace.fill_(float("nan"))   # a stale partial state would show up
+            out = p.kv.decode(p.q, w.spec.scale, partition_size=0).cpu()
+            assert torch.isfinite(out).all()
+            assert (out - ref).abs().max().item() < 5e-5
+        p.check_decode(seqs=sample, partition_size=0)
+
+
 @pytest.mark.parametrize("key", ["gqa-8b-bf16", "long-70b-bf16"])
 def test_balanced_split_any_grid(key, monkeypatch):
     """The balanced split merges partial states across wavefronts (a
@@ -200,6 +233,7 @@ def test_balanced_split_any_grid(key, monkeypatch):
     B = w.spec.num_seqs
     sample = list(range(0, B, max(1, B // 16))) + [B - 1]
     ref = p.kv.decode(p.q, w.spec.scale, partition_size=512).cpu()
+    monkeypatch.setenv("PKV_DECODE_SPLIT", "wave")
     for waves in ("37", "256", "1000", "2048", "4099", "16384"):
         monkeypatch.setenv("PKV_BALANCED_WAVES", waves)
         print(f"[balanced] {key} waves={waves}", flush=True)
