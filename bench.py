@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "gqa-8b-bf16"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_gqa-8b_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_cu_gqa-8b_traffic.txt")
 
 
 def log(*a):
@@ -55,6 +55,64 @@ def committed_traffic():
     if not m or not t or m.group(1) != kernel_source_hash():
         return None
     return float(t.group(1))
+
+
+def kernel_name(partition: int) -> str:
+    """The decode main kernel the library launches for the headline workload."""
+    if partition != 0:
+        return "decode_bf16_kernel<128,3,2> + lse_reduce_kernel"
+    if os.environ.get("PKV_DECODE_SPLIT") == "wave":
+        return "decode_bf16_balanced_kernel<128,2,2> (per-wave split, merge inside)"
+    return "decode_bf16_cu_kernel<128,2,2> (per-CU split, LDS fold, merge inside)"
+
+
+def all_configs(path: str, dev):
+    """Decode alone (back to back, after warm-up) on every bf16 workload at
+    its full size; written to ``path`` as JSON."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_102_amd.driver import PagedKV, replay_prefill
+    from workloads import synth
+    res = {}
+    for key in ("mha-7b-bf16", "gqa-8b-bf16", "long-70b-bf16", "shared-prefix-bf16"):
+        w = synth.generate(key)
+        s = w.spec
+
+        def to_dev(rows):
+            return torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).to(dev).view(
+                torch.bfloat16)
+        kv = PagedKV(num_blocks=w.num_blocks, num_seqs=s.num_seqs,
+                     max_blocks_per_seq=w.max_blocks_per_seq, num_q_heads=s.num_q_heads,
+                     num_kv_heads=s.num_kv_heads, head_dim=s.head_dim, dtype=s.dtype, device=dev,
+                     init_order=w.pool_order)
+        replay_prefill(kv, w, to_dev)
+        q = to_dev(w.q)
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        for _ in range(20):
+            kv.decode(q, s.scale, out=out)
+        torch.cuda.synchronize()
+        n = 100
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            kv.decode(q, s.scale, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        logical = kv_bytes(kv.lens, s.num_kv_heads, s.head_dim)
+        blocks = -(-kv.lens.astype(np.int64) // 16)
+        unique = (int(blocks.sum()) if s.prefix_len == 0 else
+                  int(blocks.sum()) - (s.num_seqs - 1) * (s.prefix_len // 16)) * 16 \
+            * 2 * s.num_kv_heads * s.head_dim * 2
+        res[key] = {"ms": round(ms, 4), "seqs_per_s": round(s.num_seqs / ms * 1e3, 1),
+                    "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+                    "effective_kv_gb_per_s": round(logical / ms / 1e6, 1),
+                    "frac_of_hbm_peak_unique": round(unique / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] {key}: {res[key]}")
+        del kv, q, out
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
 
 
 def kv_bytes(lens, num_kv_heads, head_dim, elem=2) -> int:
@@ -97,6 +155,10 @@ def main():
                     help="skip the streaming-read ceiling measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--no-contiguous", dest="contiguous", action="store_false",
+                    help="skip the paged-vs-contiguous comparison")
+    ap.add_argument("--all-configs", metavar="PATH", default=None,
+                    help="also time decode alone on every workload and write them to PATH (JSON)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path "
@@ -137,6 +199,38 @@ def main():
     k_new, v_new = to_dev(w.k_app), to_dev(w.v_app)
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+
+    # paged vs contiguous: the same lengths and values with the blocks of
+    # each sequence consecutive in the pool (identity free-list order), decode
+    # alone, back to back
+    paged_vs_contig = None
+    if args.contiguous and args.decode_only_steps > 0:
+        kc = PagedKV(num_blocks=w.num_blocks, num_seqs=s.num_seqs,
+                     max_blocks_per_seq=w.max_blocks_per_seq, num_q_heads=s.num_q_heads,
+                     num_kv_heads=s.num_kv_heads, head_dim=s.head_dim, dtype=s.dtype, device=dev,
+                     init_order=None, partition_size=args.partition)
+        replay_prefill(kc, w, to_dev)
+        kv.decode(q, s.scale, out=out)
+        kc.decode(q, s.scale, out=out)
+        times = {}
+        for name, obj in (("paged", kv), ("contiguous", kc)):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.decode_only_steps):
+                obj.decode(q, s.scale, out=out)
+            e1.record()
+            torch.cuda.synchronize()
+            times[name] = e0.elapsed_time(e1) / args.decode_only_steps
+        paged_vs_contig = {"paged_ms": round(times["paged"], 4),
+                           "contiguous_ms": round(times["contiguous"], 4),
+                           "paged_overhead_pct": round(100 * (times["paged"] / times["contiguous"] - 1),
+                                                       2),
+                           "note": "after prefill, same lengths and values; contiguous = each "
+                                   "sequence's blocks consecutive in the pool"}
+        del kc
+        torch.cuda.empty_cache()
+
 
     def step():
         kv.append(k_new, v_new)
@@ -225,13 +319,17 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": ("decode_bf16_balanced_kernel<128,2,2> (split merge inside)"
-                                if args.partition == 0 else "decode_bf16_kernel<128,3,2>"),
+                     "kernel": kernel_name(args.partition),
                      "avg_launch_ms": round(avg_kernel_ms, 5), "launches": nlaunch,
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
+        "paged_vs_contiguous": paged_vs_contig,
         "hbm_read_ceiling_gbs": round(ceiling, 1) if ceiling else None,
         "decode_frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None,
     }
+    if args.all_configs:
+        del kv
+        torch.cuda.empty_cache()
+        all_configs(args.all_configs, dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(w)
