@@ -898,7 +898,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   constexpr int64_t TILE = int64_t(kBlock) * D;
   constexpr int TILE_BYTES = static_cast<int>(TILE * 2);
   constexpr int NW = kCuWaves;
-  constexpr int NKMAX = 8;  // folded elements per lane: group * D / 64 <= 8
+  constexpr int NKMAX = 16 * D / 64;  // folded elements per lane: group * D / 64
 
   __shared__ __align__(16) unsigned char smem[kCuLdsBytes];
   const int g = a.group;
@@ -1906,11 +1906,11 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
   a.static_permille = env_int("PKV_CU_STATIC_PERMILLE", 1000, 0, 1000);
   a.chunk_min = env_int("PKV_CU_CHUNK_MIN", 4, 1, 1 << 20);
   // per-CU form: up to 256 sequences (lengths held in registers), a tile
-  // list indexed in 32 bits, at most 8 folded elements per lane, and
-  // partial-state slots for 2 CUs per wave of the per-wave grid
+  // list indexed in 32 bits, and global partial-state slots (2 per CU) within
+  // those of the per-wave grid
   const bool cu_form = balanced && cu_split_enabled() && num_seqs <= 256 &&
                        int64_t(num_seqs) * max_blocks_per_seq * num_kv_heads < (int64_t(1) << 31) &&
-                       group * head_dim / 64 <= 8 && cus > 0 && cus * 2 <= waves * 2;
+                       cus > 0 && cus <= waves;
 
   const bool prof = g_prof.on && g_prof.used + 2 <= g_prof.pool.size();
   if (prof) (void)hipEventRecord(g_prof.pool[g_prof.used], stream);
