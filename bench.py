@@ -115,6 +115,58 @@ def all_configs(path: str, dev):
         json.dump(res, f, indent=1)
 
 
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def prefill_measure(dev, reps: int = 20):
+    """Multi-query (chunked prefill) attention: 8 sequences of the gqa-8b
+    shape with 1024..2048 cached tokens each take a 512-token chunk, causal
+    inside the chunk.  Returns the kernel time and its rate against the bf16
+    matrix-core peak (4 * D flops per (query row, attended token))."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_102_amd.driver import PagedKV, replay_prefill
+    from workloads import synth
+    n = 512
+    w = synth.small_random(4242, num_seqs=8, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           dtype="bf16", max_len=2048, min_len=1024, append=n)
+    s = w.spec
+
+    def to_dev(rows):
+        return torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).to(dev).view(torch.bfloat16)
+    kv = PagedKV(num_blocks=w.num_blocks, num_seqs=s.num_seqs,
+                 max_blocks_per_seq=w.max_blocks_per_seq, num_q_heads=s.num_q_heads,
+                 num_kv_heads=s.num_kv_heads, head_dim=s.head_dim, dtype=s.dtype, device=dev,
+                 init_order=w.pool_order)
+    replay_prefill(kv, w, to_dev)
+    kv.append(to_dev(w.k_app), to_dev(w.v_app), w.append_counts)
+    T = n * s.num_seqs
+    q = torch.randn((T, s.num_q_heads, s.head_dim), device=dev).to(torch.bfloat16)
+    qstart = np.arange(0, T + 1, n, dtype=np.int32)
+    out = torch.empty((T, s.num_q_heads, s.head_dim), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        kv.prefill_attention(q, qstart, s.scale, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        kv.prefill_attention(q, qstart, s.scale, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    lens = kv.lens.astype(np.int64)
+    attended = int(sum(int(L) * n - n * (n - 1) // 2 for L in lens))   # sum over rows of (p + 1)
+    flops = 4.0 * s.head_dim * s.num_q_heads * attended
+    kv_unique = int(lens.sum()) * 2 * s.num_kv_heads * s.head_dim * 2
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": "8 sequences x 512-token chunks on 1024..2048 cached tokens, 32 q / 8 kv heads, "
+                        "head_dim 128, bf16",
+            "kernel": "prefill_bf16_kernel<128,2,2>", "ms": round(ms, 4),
+            "tflops": round(tflops, 2), "bound": "mfma", "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+            "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "unique_kv_gb_per_s": round(kv_unique / ms / 1e6, 1)}
+
+
 def kv_bytes(lens, num_kv_heads, head_dim, elem=2) -> int:
     return int(lens.astype("int64").sum()) * 2 * num_kv_heads * head_dim * elem
 
@@ -157,6 +209,8 @@ def main():
                     help="run one plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--no-contiguous", dest="contiguous", action="store_false",
                     help="skip the paged-vs-contiguous comparison")
+    ap.add_argument("--no-prefill", dest="prefill", action="store_false",
+                    help="skip the multi-query (chunked prefill) measurement")
     ap.add_argument("--all-configs", metavar="PATH", default=None,
                     help="also time decode alone on every workload and write them to PATH (JSON)")
     args = ap.parse_args()
@@ -289,6 +343,11 @@ def main():
         ceiling = buf.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         del buf, sink
 
+    prefill = None
+    if args.prefill:
+        torch.cuda.synchronize()
+        prefill = prefill_measure(dev)
+
     traffic = committed_traffic()
     stats = capi.kv_pool_stats(kv.pool)
     waste = float(np.sum(-(-kv.lens // 16) * 16 - kv.lens) / np.sum(-(-kv.lens // 16) * 16))
@@ -323,6 +382,7 @@ def main():
                      "avg_launch_ms": round(avg_kernel_ms, 5), "launches": nlaunch,
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
         "paged_vs_contiguous": paged_vs_contig,
+        "prefill_chunked": prefill,
         "hbm_read_ceiling_gbs": round(ceiling, 1) if ceiling else None,
         "decode_frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None,
     }

@@ -302,6 +302,35 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
                                   size_t workspace_bytes, pkv_dtype kv_dtype, float* out,
                                   hipStream_t stream);
 
+/* Multi-query attention over the paged cache (chunked prefill): several new
+ * query tokens per sequence, mixed with one-token decode rows in the same
+ * call, over the same block tables ["PagedAttention por dentro", «Chunked
+ * prefill integrado con paged KV»: prefill chunks and decode share one step
+ * and one paged cache].  Sequence s's chunk is rows query_start[s] ..
+ * query_start[s+1]-1 of q; they are the LAST n_s = query_start[s+1] -
+ * query_start[s] of its L = context_lens[s] cached tokens (write their K/V
+ * with paged_kv_write / paged_kv_append first).  Chunk row i is position
+ * p = L - n_s + i and attends causally to positions 0..p:
+ *   out[r][h][:] = sum_{t<=p} softmax_t(scale * q[r][h] . K_t) V_t,
+ * kv head h / (num_q_heads / num_kv_heads).  n_s = 1 is a decode step; n_s = 0
+ * leaves the sequence out.
+ *
+ *   q: device [T][num_q_heads][head_dim] in the cache dtype, T = query_start[num_seqs]
+ *   query_start: device int32 [num_seqs + 1], non-decreasing, query_start[0] = 0
+ *   out: device fp32 [T][num_q_heads][head_dim], written for every chunk row
+ *   max_query_len: host-side upper bound of n_s (sizes the grid)
+ * bf16 caches only; head_dim 64 or 128; at most 16 query heads per kv head.
+ * Errors: as paged_attention_decode (PKV_ERR_INVALID / PKV_ERR_UNSUPPORTED);
+ * on the device a sequence with a bad length, n_s > L, or a table entry
+ * outside [0, num_blocks) gets NaN rows instead of out-of-range reads. */
+pkv_status paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   const int32_t* query_start, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_blocks, int32_t max_blocks_per_seq,
+                                   int32_t max_context_len, int32_t max_query_len, float scale,
+                                   pkv_dtype kv_dtype, float* out, hipStream_t stream);
+
 /* ===== Measurement ==========================================================
  * While profiling is on, every paged_attention_decode call records a pair of
  * HIP events around its main (block-walking) kernel on the caller's stream.

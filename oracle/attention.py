@@ -80,3 +80,33 @@ def attend_partitioned(q, k, v, scale, partition_tokens: int) -> np.ndarray:
     states = [partial_state(q, k[a:a + partition_tokens], v[a:a + partition_tokens], scale)
               for a in range(0, L, partition_tokens)]
     return merge_states(states)
+
+
+def prefill(q_stored: np.ndarray, cache: CacheModel, tables: np.ndarray, lens: np.ndarray,
+            query_start: np.ndarray, num_q_heads: int, num_kv_heads: int,
+            scale: float) -> np.ndarray:
+    """Multi-query attention over the paged cache (chunked prefill).
+
+    "PagedAttention por dentro" (blog.lo0.es), "Chunked prefill integrado con
+    paged KV": prefill split into chunks runs in the same step as decode, on
+    the same paged cache.  Reading (the page gives no formula): sequence b's
+    chunk holds rows query_start[b] .. query_start[b+1]-1 of ``q_stored``
+    [T][Hq][D]; they are the last n_b of its L_b cached tokens, so chunk row
+    i is the token at position p = L_b - n_b + i and attends to positions
+    0..p only (the causal rule of a language model, applied inside the
+    chunk).  With n_b = 1 this is ``decode``.  Returns out [T][Hq][D]
+    float64."""
+    T, _, D = q_stored.shape
+    group = num_q_heads // num_kv_heads
+    q = widen(q_stored, cache.dtype)
+    out = np.zeros((T, num_q_heads, D), dtype=np.float64)
+    for b in range(len(lens)):
+        r0, r1 = int(query_start[b]), int(query_start[b + 1])
+        n, L = r1 - r0, int(lens[b])
+        for kvh in range(num_kv_heads):
+            k, v = cache.gather(tables[b], L, kvh)
+            for i in range(n):
+                p = L - n + i
+                for h in range(kvh * group, (kvh + 1) * group):
+                    out[r0 + i, h] = attend(q[r0 + i, h], k[:p + 1], v[:p + 1], scale)
+    return out

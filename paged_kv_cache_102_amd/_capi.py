@@ -60,6 +60,9 @@ _SIGS = {
     "paged_attention_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32, C.c_int32,
                                          C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_float,
                                          C.c_int32, _vp, C.c_size_t, C.c_int, _vp, _vp]),
+    "paged_attention_prefill": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
+                                          C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                          C.c_int32, C.c_float, C.c_int, _vp, _vp]),
     "pkv_profile_begin": (C.c_int, []),
     "pkv_profile_end": (C.c_int, [_i32p, C.POINTER(C.c_double)]),
     "pkv_stream_read": (C.c_int, [_vp, C.c_size_t, _vp, _vp]),
@@ -275,6 +278,23 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, out,
                                        num_blocks, mb, max_context_len, scale, partition_size,
                                        ws_ptr, ws_bytes, _dtype_code(k_cache), _dev(out, "out"),
                                        _stream(stream)), "paged_attention_decode")
+
+
+def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, out, *,
+                            num_kv_heads: int, num_blocks: int, max_context_len: int,
+                            max_query_len: int, scale: float, stream=None) -> None:
+    """q [T][Hq][D] (chunk rows of all sequences, in order), query_start
+    int32 [B + 1]; out [T][Hq][D] fp32."""
+    T, Hq, D = q.shape
+    B = context_lens.shape[0]
+    mb = block_tables.shape[1]
+    _check(_lib.paged_attention_prefill(_dev(q, "q"), _dev(k_cache, "k_cache"),
+                                        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+                                        _dev(context_lens, "context_lens"),
+                                        _dev(query_start, "query_start"), B, Hq, num_kv_heads, D,
+                                        num_blocks, mb, max_context_len, max_query_len, scale,
+                                        _dtype_code(k_cache), _dev(out, "out"), _stream(stream)),
+           "paged_attention_prefill")
 
 
 def pkv_profile_begin() -> None:

@@ -1381,6 +1381,203 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ next: multi-query (chunked prefill), bf16
+// Several new query tokens per sequence over the same paged cache: sequence
+// b's chunk of n_b tokens holds the last n_b of its L_b cached positions
+// (their K/V written before the call); chunk token i sits at position
+// p = L_b - n_b + i and attends to positions 0..p (causal inside the chunk).
+// A decode step is the case n_b = 1.  One wavefront per (kv head, sequence,
+// tile of query positions): the 16 columns of the score tile are
+// (position, head-in-group) pairs, QB = 16 / g positions per tile, so one
+// load of a K/V tile serves 16 query rows (g for decode).
+struct PrefillArgs {
+  const void* q;          // [T][Hq][D] bf16, T = qstart[B]
+  const void* kc;
+  const void* vc;
+  const int32_t* tables;
+  const int32_t* lens;
+  const int32_t* qstart;  // [B + 1] first chunk row of each sequence
+  float* out;             // [T][Hq][D] fp32
+  int num_seqs, num_q_heads, num_kv_heads, group, qb;
+  int num_blocks, max_blocks, max_ctx;
+  float scale_log2e;
+};
+
+template <int D, int ST, int AUX>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_bf16_kernel(PrefillArgs a) {
+  constexpr int NJ = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int64_t TILE = int64_t(kBlock) * D;
+  constexpr int TILE_BYTES = static_cast<int>(TILE * 2);
+
+  const int lane = threadIdx.x;
+  const int64_t wid = blockIdx.x;  // kv head fastest, then sequence, then query tile
+  const int kvh = static_cast<int>(wid % a.num_kv_heads);
+  const int b = static_cast<int>((wid / a.num_kv_heads) % a.num_seqs);
+  const int qt = static_cast<int>(wid / (int64_t(a.num_kv_heads) * a.num_seqs));
+  const int hcol = lane & 15;
+  const int grp = lane >> 4;
+  const int g = a.group;
+  const int QB = a.qb;
+  const int qs = load_uniform(a.qstart, b);
+  const int n = load_uniform(a.qstart, b + 1) - qs;
+  const int q0 = qt * QB;
+  if (q0 >= n || n <= 0) return;
+  const int L = load_uniform(a.lens, b);
+  const int nq = min(QB, n - q0);  // positions in this tile
+  // column c = (position qi, head hh); columns past the tile are padding
+  const int qi = hcol / g, hh = hcol % g;
+  const bool col_ok = hcol < nq * g;
+
+  auto out_row = [&](int c) -> float* {  // output row of column c
+    return a.out + ((int64_t(qs) + q0 + c / g) * a.num_q_heads + int64_t(kvh) * g + c % g) * D;
+  };
+  const bool len_bad = L < 0 || L > a.max_ctx || int64_t(L) > int64_t(a.max_blocks) * kBlock ||
+                       n > L;
+  if (len_bad) {
+    for (int c = 0; c < nq * g; ++c)
+      for (int e = lane; e < D; e += 64) out_row(c)[e] = __builtin_nanf("");
+    return;
+  }
+  const int p_last = L - n + q0 + nq - 1;          // last position of the tile
+  const int p_col = col_ok ? L - n + q0 + qi : p_last;
+  const int nblk = p_last / kBlock + 1;
+  const int32_t* row = a.tables + int64_t(b) * a.max_blocks;
+
+  // Q^T as B operand: lane holds q[row of column hcol][32j + 8 grp .. +8]
+  bf16x8 qf[NJ];
+  {
+    // one resource over the tile's query rows; padding columns read past it (zeros)
+    const int row_bytes = a.num_q_heads * D * 2;
+    const char* qb = static_cast<const char*>(a.q) + (int64_t(qs) + q0) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(qb, nq * row_bytes);
+    const int qoff = col_ok ? qi * row_bytes + (kvh * g + hh) * D * 2 : nq * row_bytes;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      qf[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + (32 * j + grp * 8) * 2, 0, 0));
+  }
+
+  const char* kc = static_cast<const char*>(a.kc) + int64_t(kvh) * TILE_BYTES;
+  const char* vc = static_cast<const char*>(a.vc) + int64_t(kvh) * TILE_BYTES;
+  const int64_t block_bytes = int64_t(a.num_kv_heads) * TILE_BYTES;
+  const int loff = lane * 16;
+
+  f32x4 o[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+  bool bad = false;
+
+  uint4 kr[ST][NJ], vr[ST][NJ];
+  auto issue = [&](int i, int st) {
+    int bytes = TILE_BYTES;
+    int phys = 0;
+    if (i >= nblk) {
+      bytes = 0;
+    } else {
+      phys = load_uniform(row, i);
+      if (phys < 0 || phys >= a.num_blocks) {
+        bad = true;
+        bytes = 0;
+      }
+    }
+    const int64_t off = int64_t(bytes ? phys : 0) * block_bytes;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + off, bytes);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + off, bytes);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      kr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + 1024 * j, 0, AUX));
+      vr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + 1024 * j, 0, AUX));
+    }
+  };
+
+  auto compute_block = [&](int i, int st) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[st][j]), qf[j], s,
+                                                   0, 0, 0);
+    const int tb = i * kBlock + grp * 4;
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = (tb + r <= p_col) ? s[r] * a.scale_log2e : -INFINITY;
+    float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mloc = group_max(mloc);
+    const float mnew = fmaxf(m, mloc);
+    // a column whose positions all lie past this block keeps m = -inf
+    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      p[r] = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r] - mnew);
+    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    m = mnew;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, grp * 4 + r);
+#pragma unroll
+        for (int k = 0; k < NT; ++k) o[k][r] *= ar;
+      }
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hi[r] = bf16_bits_rne(p[r]);
+      lo[r] = bf16_bits_rne(p[r] - __uint_as_float(hi[r] << 16));
+    }
+    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
+    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
+    if (i * kBlock + kBlock > L) {
+      // slots past the context may hold anything: zero their V
+      const uint32_t m01 = (tb + 0 < L ? 0x0000FFFFu : 0u) | (tb + 1 < L ? 0xFFFF0000u : 0u);
+      const uint32_t m23 = (tb + 2 < L ? 0x0000FFFFu : 0u) | (tb + 3 < L ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        vr[st][j].x &= m01;
+        vr[st][j].y &= m23;
+        vr[st][j].z &= m01;
+        vr[st][j].w &= m23;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const s16x4 v0 = __builtin_bit_cast(s16x4, make_uint2(vr[st][j].x, vr[st][j].y));
+      const s16x4 v1 = __builtin_bit_cast(s16x4, make_uint2(vr[st][j].z, vr[st][j].w));
+      o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, v0, o[2 * j], 0, 0, 0);
+      o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, v0, o[2 * j], 0, 0, 0);
+      o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, v1, o[2 * j + 1], 0, 0, 0);
+      o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, v1, o[2 * j + 1], 0, 0, 0);
+    }
+  };
+
+  // ST-stage pipeline; every trip issues the same loads (empty past the end)
+#pragma unroll
+  for (int st = 0; st < ST; ++st) issue(st, st);
+  for (int i0 = 0; i0 < nblk; i0 += ST) {
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      const int i = i0 + st;
+      if (i < nblk) compute_block(i, st);
+      issue(i + ST, st);
+    }
+  }
+
+  lsum = group_sum(lsum);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int c = grp * 4 + r;  // output row = score column
+    const float lr = __shfl(lsum, c);
+    const float inv = bad ? __builtin_nanf("") : 1.0f / lr;
+    if (c < nq * g) {
+      float* dst = out_row(c) + hcol;
+#pragma unroll
+      for (int k = 0; k < NT; ++k) dst[16 * k] = o[k][r] * inv;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ A5: decode, fp32
 // One wave per (sequence, query head, partition); lane holds channels lane
 // and lane + 64.  Plain vector-ALU form for the fp32 cache.
@@ -1713,6 +1910,13 @@ void launch_decode_bf16_cu(unsigned grid, hipStream_t stream, const DecodeArgs& 
   }
 }
 
+void launch_prefill_bf16(unsigned grid, hipStream_t stream, const PrefillArgs& a, int head_dim) {
+  if (head_dim == 64)
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, 3, 2>), grid, dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, 2, 2>), grid, dim3(64), 0, stream, a);
+}
+
 // ============================================================================ C ABI
 extern "C" {
 
@@ -1830,6 +2034,48 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
   const size_t bal = balanced_workspace_bytes(balanced_waves(), group < 16 ? group : 16, head_dim,
                                               int64_t(num_seqs) * num_kv_heads);
   return fixed > bal ? fixed : bal;
+}
+
+pkv_status paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   const int32_t* query_start, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_blocks, int32_t max_blocks_per_seq,
+                                   int32_t max_context_len, int32_t max_query_len, float scale,
+                                   pkv_dtype kv_dtype, float* out, hipStream_t stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0 || max_query_len < 0)
+    return PKV_ERR_INVALID;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (kv_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  const int group = num_q_heads / num_kv_heads;
+  if (group > 16) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+    return PKV_ERR_INVALID;
+  PrefillArgs a;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.qstart = query_start;
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.qb = 16 / group;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  const int64_t tiles = (int64_t(max_query_len) + a.qb - 1) / a.qb;
+  const int64_t grid = tiles * num_seqs * num_kv_heads;
+  if (grid > 0x7FFFFFFF) return PKV_ERR_UNSUPPORTED;
+  launch_prefill_bf16(static_cast<unsigned>(grid), stream, a, head_dim);
+  return launch_status();
 }
 
 pkv_status paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,

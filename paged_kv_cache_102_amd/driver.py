@@ -150,6 +150,22 @@ class PagedKV:
                                     workspace=ws, stream=stream.cuda_stream)
         return out
 
+    def prefill_attention(self, q, query_start, scale: float, out=None, stream=None):
+        """Multi-query attention for chunk rows q [T][Hq][D] (their K/V already
+        appended); query_start int32 [B + 1] (numpy, uploaded here)."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        qs = np.ascontiguousarray(query_start, dtype=np.int32)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        qs_d = torch.from_numpy(qs).to(self.device)
+        max_q = int(np.max(np.diff(qs))) if qs.size > 1 else 0
+        max_ctx = int(self.lens.max()) if self.lens.size else 0
+        capi.paged_attention_prefill(q, self.k_cache, self.v_cache, self.tables_d, self.lens_d, qs_d,
+                                     out, num_kv_heads=self.num_kv_heads, num_blocks=self.num_blocks,
+                                     max_context_len=max_ctx, max_query_len=max_q, scale=scale,
+                                     stream=stream.cuda_stream)
+        return out
+
     def free_sequence(self, s: int):
         """Returns sequence s's blocks to the pool (one reference each)."""
         n = -(-int(self.lens[s]) // BLOCK)

@@ -243,3 +243,67 @@ def test_balanced_split_any_grid(key, monkeypatch):
             assert torch.isfinite(out).all()
             assert (out - ref).abs().max().item() < 5e-5
         p.check_decode(seqs=sample, partition_size=0)
+
+
+# ---------------------------------------------------------------- multi-query (chunked prefill)
+@pytest.mark.parametrize("Hq,Hkv,D,seed", [(8, 2, 128, 1), (4, 4, 64, 2), (32, 8, 128, 3),
+                                             (16, 1, 128, 4), (6, 3, 64, 5), (16, 2, 128, 6)])
+def test_prefill_chunks_vs_oracle(Hq, Hkv, D, seed):
+    """Chunks of 0..max tokens per sequence (decode rows, whole prompts,
+    chunks continuing a context) appended through the planner, then
+    multi-query attention: every chunk row against the oracle's causal
+    attention, within the bf16 tolerance."""
+    from oracle import attention as oatt
+    from oracle.slots import plan_append
+    from tests.gpu_parity import to_device
+    B, maxc = 9, 70
+    w = synth.small_random(100 + seed, num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           dtype="bf16", max_len=300, append=maxc, fixed=[0, 0, 1, 16, 17])
+    p = _pair(w)
+    rng = np.random.default_rng(seed)
+    counts = rng.integers(0, maxc + 1, size=B)
+    counts[:5] = [maxc, 33, 1, 0, 16]
+    counts[5] = 1
+    T = int(counts.sum())
+    k_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    v_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    q = synth.round_bf16_bits(rng.standard_normal((T, Hq, D)).astype(np.float32))
+    # both sides append the chunks through their own planner and write
+    slots, _, cows = plan_append(p.ora.pool, p.ora.tables, p.ora.lens, counts)
+    p.ora.cache.copy_blocks(cows)
+    p.ora.cache.write(k_new, v_new, slots)
+    p.kv.append(to_device(k_new), to_device(v_new), counts.astype(np.int32))
+    p.check_state()
+    qstart = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    print(f"[prefill] Hq={Hq} Hkv={Hkv} D={D} T={T} counts={counts.tolist()}", flush=True)
+    out = p.kv.prefill_attention(to_device(q), qstart, w.spec.scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    exp = oatt.prefill(q, p.ora.cache, p.ora.tables, p.ora.lens, qstart, Hq, Hkv, w.spec.scale)
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - exp)))
+    assert err <= 2e-3, f"max abs error {err:.3e}"
+    # a one-row chunk is a decode step: same rows as the decode kernel
+    dec_rows = [b for b in range(B) if counts[b] == 1]
+    qd = np.zeros((B, Hq, D), np.uint16)
+    for b in dec_rows:
+        qd[b] = q[qstart[b]]
+    dout = p.kv.decode(to_device(qd), w.spec.scale).cpu().numpy()
+    for b in dec_rows:
+        assert np.max(np.abs(dout[b] - got[qstart[b]])) <= 2e-3
+
+
+def test_prefill_bad_rows_are_nan():
+    """A chunk longer than its context, or a table entry outside the pool,
+    gives NaN rows for that sequence only."""
+    w = synth.small_random(77, num_seqs=3, num_q_heads=4, num_kv_heads=1, head_dim=128,
+                           dtype="bf16", max_len=40, min_len=20)
+    p = _pair(w)
+    qstart = np.array([0, 5, 5 + int(p.kv.lens[1]) + 1, 5 + int(p.kv.lens[1]) + 4], np.int32)
+    T = int(qstart[-1])
+    q = torch.zeros((T, 4, 128), dtype=torch.bfloat16, device="cuda")
+    p.kv.tables_d[2, 0] = w.num_blocks + 5
+    out = p.kv.prefill_attention(q, qstart, w.spec.scale).cpu()
+    assert torch.isfinite(out[:5]).all()
+    assert torch.isnan(out[5:qstart[2]]).all()
+    assert torch.isnan(out[qstart[2]:]).all()

@@ -118,3 +118,37 @@ def test_mutation_cow_copies_always(monkeypatch):
         return new, True
     monkeypatch.setattr(pool.PoolModel, "cow", bad_cow)
     assert _fails(pins.test_cow_beam_fork)
+
+
+@pytest.mark.parametrize("shift", [-1, 1])
+def test_mutation_prefill_causal_off_by_one(monkeypatch, shift):
+    """A causal limit one position early or late is caught."""
+    def bad_prefill(q_stored, cache, tables, lens, query_start, num_q_heads, num_kv_heads, scale):
+        T, _, D = q_stored.shape
+        g = num_q_heads // num_kv_heads
+        q = attention.widen(q_stored, cache.dtype)
+        out = np.zeros((T, num_q_heads, D))
+        for b in range(len(lens)):
+            r0, r1 = int(query_start[b]), int(query_start[b + 1])
+            n, L = r1 - r0, int(lens[b])
+            for kvh in range(num_kv_heads):
+                k, v = cache.gather(tables[b], L, kvh)
+                for i in range(n):
+                    p = max(0, min(L - 1, L - n + i + shift))
+                    for h in range(kvh * g, (kvh + 1) * g):
+                        out[r0 + i, h] = attention.attend(q[r0 + i, h], k[:p + 1], v[:p + 1], scale)
+        return out
+    monkeypatch.setattr(attention, "prefill", bad_prefill)
+    assert _fails(pins.test_prefill_equals_causal_sdpa, 8, 2, "f32")
+
+
+def test_mutation_prefill_query_rows(monkeypatch):
+    """Chunk rows read as the first n positions (not the last n) is caught."""
+    orig = attention.prefill
+
+    def bad_prefill(q_stored, cache, tables, lens, query_start, num_q_heads, num_kv_heads, scale):
+        n = np.diff(np.asarray(query_start))
+        return orig(q_stored, cache, tables, np.minimum(np.asarray(lens), n + 0) * 0 + n,
+                    query_start, num_q_heads, num_kv_heads, scale)
+    monkeypatch.setattr(attention, "prefill", bad_prefill)
+    assert _fails(pins.test_prefill_equals_causal_sdpa, 4, 4, "bf16")

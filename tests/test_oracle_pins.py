@@ -476,3 +476,75 @@ def test_replay_shared_prefix_cow():
     assert p.refcount[last] == 1
     assert list(lens) == list(w.spec.prefix_len + w.suffix_lens + 1)
     p.check_invariants([list(tables[b, :slots.blocks_for(int(lens[b]))]) for b in range(B)])
+
+
+# ---------------------------------------------------------------- multi-query (chunked prefill)
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (6, 3)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_equals_causal_sdpa(Hq, Hkv, dtype):
+    """oracle.attention.prefill against torch SDPA (fp64, CPU) with an
+    explicit causal mask on contiguous K/V: chunk row i of sequence b is
+    position L_b - n_b + i and sees positions 0..that."""
+    rng = np.random.default_rng(Hq * 10 + Hkv + (dtype == "bf16"))
+    B, D, NB = 5, 32, 40
+    lens = np.array([1, 17, 40, 64, 70])
+    chunks = np.array([1, 0, 40, 5, 33])           # a decode row, an idle sequence, a full prefill
+    p = PoolModel(NB, init_order=rng.permutation(NB))
+    mb = max(-(-int(n) // 16) for n in lens)
+    tables = np.full((B, mb), -1, np.int32)
+    cur = np.zeros(B, np.int32)
+    sl, _, _ = slots.plan_append(p, tables, cur, lens)
+    T = int(lens.sum())
+    kf = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    vf = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    Q = int(chunks.sum())
+    qf = rng.standard_normal((Q, Hq, D)).astype(np.float32)
+    if dtype == "bf16":
+        kf, vf, qf = (synth.bf16_bits_to_f32(synth.round_bf16_bits(x)) for x in (kf, vf, qf))
+        ks, vs, qs = (synth.round_bf16_bits(x) for x in (kf, vf, qf))
+    else:
+        ks, vs, qs = kf, vf, qf
+    c = cache.CacheModel(NB, Hkv, D, dtype, fill=np.uint16(0x7FC0) if dtype == "bf16" else np.nan)
+    c.write(ks, vs, sl)
+    qstart = np.concatenate([[0], np.cumsum(chunks)])
+    scale = 1 / math.sqrt(D)
+    out = attention.prefill(qs, c, tables, cur, qstart, Hq, Hkv, scale)
+    start = np.concatenate([[0], np.cumsum(lens)])
+    for b in range(B):
+        n, L = int(chunks[b]), int(lens[b])
+        if n == 0:
+            continue
+        k = torch.from_numpy(kf[start[b]:start[b + 1]].astype(np.float64)).permute(1, 0, 2)
+        v = torch.from_numpy(vf[start[b]:start[b + 1]].astype(np.float64)).permute(1, 0, 2)
+        k = k.repeat_interleave(Hq // Hkv, dim=0).contiguous()
+        v = v.repeat_interleave(Hq // Hkv, dim=0).contiguous()
+        q = torch.from_numpy(qf[qstart[b]:qstart[b + 1]].astype(np.float64)).permute(1, 0, 2)
+        pos = torch.arange(L - n, L)[:, None]
+        mask = torch.arange(L)[None, :] <= pos             # [n][L], True = attend
+        ref = torch.nn.functional.scaled_dot_product_attention(q.contiguous(), k, v,
+                                                               attn_mask=mask, scale=scale)
+        np.testing.assert_allclose(out[qstart[b]:qstart[b + 1]], ref.permute(1, 0, 2).numpy(),
+                                   rtol=0, atol=1e-12)
+
+
+def test_prefill_closed_forms():
+    """Chunk row at position 0 sees only token 0: its output is v_0; a
+    one-row chunk at the end of the context is a decode step."""
+    rng = np.random.default_rng(3)
+    D, L = 32, 20
+    p = PoolModel(4, init_order=np.arange(4))
+    tables = np.full((1, 2), -1, np.int32)
+    cur = np.zeros(1, np.int32)
+    sl, _, _ = slots.plan_append(p, tables, cur, [L])
+    kv = rng.standard_normal((L, 1, D)).astype(np.float32)
+    vv = rng.standard_normal((L, 1, D)).astype(np.float32)
+    c = cache.CacheModel(4, 1, D, "f32", fill=np.nan)
+    c.write(kv, vv, sl)
+    q = rng.standard_normal((L, 2, D)).astype(np.float32)
+    out = attention.prefill(q, c, tables, cur, np.array([0, L]), 2, 1, 0.25)
+    np.testing.assert_array_equal(out[0, 0], vv[0, 0].astype(np.float64))
+    np.testing.assert_array_equal(out[0, 1], vv[0, 0].astype(np.float64))
+    # the last chunk row equals plain attention over the whole context
+    ref = attention.attend(q[L - 1, 1].astype(np.float64), kv[:, 0].astype(np.float64),
+                           vv[:, 0].astype(np.float64), 0.25)
+    np.testing.assert_allclose(out[L - 1, 1], ref, atol=1e-15)
