@@ -15,7 +15,9 @@ Readings where the pages are silent: the softmax is scaled by ``scale``
 (1/sqrt(head_dim) in every workload) and stabilised by subtracting the
 maximum (equal in exact arithmetic); query head h uses kv head
 h // (num_q_heads // num_kv_heads); there is no mask beyond the context
-length and no positional term; an empty context gives a zero row.
+length and no positional term; an empty context gives a zero row.  With an
+FP8 cache the queries are bf16 and K, V are the codes' values times their
+tensor scales (see ``fp8``).
 """
 from __future__ import annotations
 
@@ -42,7 +44,7 @@ def decode(q_stored: np.ndarray, cache: CacheModel, tables: np.ndarray, lens: np
     B = q_stored.shape[0]
     D = q_stored.shape[2]
     group = num_q_heads // num_kv_heads
-    q = widen(q_stored, cache.dtype)
+    q = widen(q_stored, "bf16" if cache.dtype == "fp8" else cache.dtype)
     out = np.zeros((B, num_q_heads, D), dtype=np.float64)
     for b in (range(B) if seqs is None else seqs):
         L = int(lens[b])
@@ -98,7 +100,7 @@ def prefill(q_stored: np.ndarray, cache: CacheModel, tables: np.ndarray, lens: n
     float64."""
     T, _, D = q_stored.shape
     group = num_q_heads // num_kv_heads
-    q = widen(q_stored, cache.dtype)
+    q = widen(q_stored, "bf16" if cache.dtype == "fp8" else cache.dtype)
     out = np.zeros((T, num_q_heads, D), dtype=np.float64)
     for b in range(len(lens)):
         r0, r1 = int(query_start[b]), int(query_start[b + 1])

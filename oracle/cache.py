@@ -10,18 +10,23 @@ scattered blocks through the table without copying them into a contiguous
 buffer -- the gather below exists only to state the result, it is not a
 step of the GPU path.
 
-Values are kept exactly as stored (float32, or bf16 as raw uint16 bits);
-gathers widen them exactly to float64.
+Values are kept exactly as stored (float32, bf16 as raw uint16 bits, or
+FP8 E4M3 codes as uint8 with one scale per tensor); gathers widen them
+exactly to float64 (FP8: the code's value times the tensor's scale).
 """
 from __future__ import annotations
 
 import numpy as np
 
+from . import fp8 as fp8codec
 from .layout import BLOCK_SIZE, offset_tables
 
 
-def widen(stored: np.ndarray, dtype: str) -> np.ndarray:
-    """Stored values -> float64, exactly (bf16 bits shift into float32)."""
+def widen(stored: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Stored values -> float64, exactly (bf16 bits shift into float32; FP8
+    codes decode to their value times ``scale``)."""
+    if dtype == "fp8":
+        return fp8codec.decode(stored) * float(np.float32(scale))
     if dtype == "f32":
         return np.asarray(stored, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
@@ -34,14 +39,15 @@ class CacheModel:
     """k, v: arrays [num_blocks][num_kv_heads][16 * D] of stored elements."""
 
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
-                 fill=None):
+                 fill=None, k_scale: float = 1.0, v_scale: float = 1.0):
         self.num_blocks, self.num_kv_heads, self.head_dim, self.dtype = (
             num_blocks, num_kv_heads, head_dim, dtype)
-        store = np.float32 if dtype == "f32" else np.uint16
+        self.k_scale, self.v_scale = k_scale, v_scale
+        store = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
         shape = (num_blocks, num_kv_heads, BLOCK_SIZE * head_dim)
         self.k = np.full(shape, 0 if fill is None else fill, dtype=store)
         self.v = np.full(shape, 0 if fill is None else fill, dtype=store)
-        self.koff, self.voff = offset_tables(head_dim)
+        self.koff, self.voff = offset_tables(head_dim, fp8=(dtype == "fp8"))
 
     def write(self, k_new: np.ndarray, v_new: np.ndarray, slots: np.ndarray):
         """k_new, v_new [T][Hkv][D] stored values; slots int64 [T].  A slot
@@ -75,7 +81,7 @@ class CacheModel:
         slot = t % BLOCK_SIZE
         k = self.k[blk[:, None], kv_head, self.koff[slot]]
         v = self.v[blk[:, None], kv_head, self.voff[slot]]
-        return widen(k, self.dtype), widen(v, self.dtype)
+        return widen(k, self.dtype, self.k_scale), widen(v, self.dtype, self.v_scale)
 
     def stored_bytes(self):
         return self.k.tobytes(), self.v.tobytes()

@@ -152,3 +152,34 @@ def test_mutation_prefill_query_rows(monkeypatch):
                     query_start, num_q_heads, num_kv_heads, scale)
     monkeypatch.setattr(attention, "prefill", bad_prefill)
     assert _fails(pins.test_prefill_equals_causal_sdpa, 4, 4, "bf16")
+
+
+def test_mutation_fp8_bias_8(monkeypatch):
+    """An E4M3 decode with exponent bias 8 (another FP8 variant) is caught."""
+    from oracle import fp8
+    orig = fp8.decode
+    monkeypatch.setattr(fp8, "decode", lambda c: orig(c) / 2)
+    assert _fails(pins.test_fp8_decode_matches_torch_all_codes)
+
+
+def test_mutation_fp8_ties_away(monkeypatch):
+    """Rounding ties away from zero instead of to even is caught."""
+    from oracle import fp8
+    vals = fp8.decode(np.arange(0x7F, dtype=np.uint8))
+
+    def bad_encode(y):
+        y = np.asarray(y, dtype=np.float32)
+        a = np.minimum(np.abs(y.astype(np.float64)).ravel(), 448.0)
+        codes = np.array([int(np.argmin(np.abs(vals - v) - 1e-30 * np.arange(len(vals))))
+                          for v in a], dtype=np.uint8)
+        return (codes | (np.signbit(y.ravel()).astype(np.uint8) << 7)).reshape(y.shape)
+    monkeypatch.setattr(fp8, "encode_f32", bad_encode)
+    assert _fails(pins.test_fp8_worked_values)
+
+
+def test_mutation_fp8_scale_inverted(monkeypatch):
+    """Quantising with x * scale instead of x / scale is caught."""
+    from oracle import fp8
+    monkeypatch.setattr(fp8, "quantize",
+                        lambda x, scale: fp8.encode_f32(np.asarray(x, np.float32) * np.float32(scale)))
+    assert _fails(pins.test_fp8_worked_values)

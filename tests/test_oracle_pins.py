@@ -548,3 +548,90 @@ def test_prefill_closed_forms():
     ref = attention.attend(q[L - 1, 1].astype(np.float64), kv[:, 0].astype(np.float64),
                            vv[:, 0].astype(np.float64), 0.25)
     np.testing.assert_allclose(out[L - 1, 1], ref, atol=1e-15)
+
+
+# ---------------------------------------------------------------- FP8 E4M3 cache
+from oracle import fp8 as ofp8  # noqa: E402
+
+
+def test_fp8_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = ofp8.decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
+def test_fp8_encode_matches_torch_in_range():
+    rng = np.random.default_rng(8)
+    x = np.concatenate([rng.standard_normal(20000) * 40, rng.standard_normal(5000) * 1e-3,
+                        ofp8.decode(np.arange(0x7F, dtype=np.uint8)),           # exact values
+                        (ofp8.decode(np.arange(0x7E, dtype=np.uint8)) +          # midpoints: ties
+                         ofp8.decode(np.arange(1, 0x7F, dtype=np.uint8))) / 2]).astype(np.float32)
+    x = np.concatenate([x, -x])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ofp8.encode_f32(x), ref)
+
+
+def test_fp8_worked_values():
+    """Values fixed by the OCP E4M3 definition, and this build's clamp."""
+    cases = [(448.0, 0x7E), (2.0 ** -6, 0x08), (2.0 ** -9, 0x01), (1.0, 0x38), (-2.0, 0xC0),
+             (0.0, 0x00), (-0.0, 0x80), (1 + 1 / 16, 0x38), (1 + 3 / 16, 0x3A), (1e6, 0x7E),
+             (-1e6, 0xFE), (464.0, 0x7E), (3 * 2.0 ** -10, 0x02), (2.0 ** -10, 0x00)]
+    for v, c in cases:
+        assert int(ofp8.encode_f32(np.float32(v))) == c, (v, c)
+    assert int(ofp8.encode_f32(np.float32(np.nan))) == 0x7F
+    assert ofp8.decode(np.uint8(0x7E)) == 448.0 and np.isnan(ofp8.decode(np.uint8(0xFF)))
+    # quantize: one float32 multiply by float32(1/scale), then the code
+    assert int(ofp8.quantize(np.float32(3.0), 0.5)) == int(ofp8.encode_f32(np.float32(6.0)))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_layout_is_the_bf16_operand_order(D):
+    """Every byte of an FP8 tile is used once, and (t, d) sits at the same
+    (lane, piece, position) as in the bf16 tile: bf16 16-byte piece j of lane
+    l starts at element 512 j + 8 l, the FP8 8-byte piece at byte D/4 l + 8 j."""
+    for k8, k16 in ((layout.k8_offset, layout.k_offset), (layout.v8_offset, layout.v_offset)):
+        seen = set()
+        for t in range(16):
+            for d in range(D):
+                o8, o16 = k8(t, d, D), k16(t, d)
+                seen.add(o8)
+                j, l, w = o16 // 512, (o16 % 512) // 8, o16 % 8
+                assert o8 == (D // 4) * l + 8 * j + w
+        assert seen == set(range(16 * D))
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
+def test_fp8_paged_equals_contiguous_sdpa(Hq, Hkv):
+    """Decode over an FP8 cache equals torch SDPA (fp64) on the dequantised
+    values, gathered contiguously."""
+    rng = np.random.default_rng(80 + Hq)
+    B, D, NB = 4, 64, 24
+    lens = rng.integers(1, 80, size=B)
+    p = PoolModel(NB, init_order=rng.permutation(NB))
+    mb = max(-(-int(n) // 16) for n in lens)
+    tables = np.full((B, mb), -1, np.int32)
+    cur = np.zeros(B, np.int32)
+    sl, _, _ = slots.plan_append(p, tables, cur, lens)
+    T = int(lens.sum())
+    ks_, vs_ = 0.05, 0.02
+    kx = rng.standard_normal((T, Hkv, D)).astype(np.float32) * 3
+    vx = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    kc, vc = ofp8.quantize(kx, ks_), ofp8.quantize(vx, vs_)
+    qf = synth.bf16_bits_to_f32(synth.round_bf16_bits(rng.standard_normal((B, Hq, D)).astype(np.float32)))
+    qs = synth.round_bf16_bits(qf)
+    c = cache.CacheModel(NB, Hkv, D, "fp8", fill=np.uint8(0x7F), k_scale=ks_, v_scale=vs_)
+    c.write(kc, vc, sl)
+    out = attention.decode(qs, c, tables, cur, Hq, Hkv, 1 / math.sqrt(D))
+    kd = ofp8.decode(kc) * float(np.float32(ks_))
+    vd = ofp8.decode(vc) * float(np.float32(vs_))
+    start = np.concatenate([[0], np.cumsum(lens)])
+    for b in range(B):
+        k = torch.from_numpy(kd[start[b]:start[b + 1]]).permute(1, 0, 2)
+        v = torch.from_numpy(vd[start[b]:start[b + 1]]).permute(1, 0, 2)
+        k = k.repeat_interleave(Hq // Hkv, dim=0).contiguous()
+        v = v.repeat_interleave(Hq // Hkv, dim=0).contiguous()
+        q = torch.from_numpy(qf[b].astype(np.float64))[:, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=1 / math.sqrt(D))
+        np.testing.assert_allclose(out[b], ref[:, 0, :].numpy(), rtol=0, atol=1e-12)
