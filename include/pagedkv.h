@@ -51,6 +51,21 @@
  * fragment the gfx950 matrix instructions consume; the element type (fp32 or
  * bf16) does not change the order.
  *
+ * FP8 cache (PKV_FP8_E4M3, one byte per element, tile of 16 * D bytes).  The
+ * bytes are in the same lane/piece order as the bf16 tile, so a lane's two
+ * 16-byte loads expand to the bf16 operand pieces; with W = D / 4:
+ *
+ *   K:  W * (16 * ((d / 8) % 4) + t) + 8 * (d / 32) + (d % 8)
+ *   V:  W * (16 * (t / 4) + d % 16) + 8 * (d / 32) + ((d / 16) % 2) * 4 + (t % 4)
+ *
+ * A byte is an OCP FP8 E4M3 code (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, subnormals m * 2^-9, no infinity, 0x7F/0xFF = NaN, largest
+ * finite 448) standing for its value times the tensor's scale (one scale
+ * for K, one for V).  ["KV cache: la memoria de trabajo...", «Cuantización
+ * del KV cache»: an 8-bit cache halves its size and the bytes read per
+ * step, and FP8 is described as safe almost always; the format and the
+ * scaling are this library's reading.]
+ *
  * Token position p of sequence s (0-based) lives in physical block
  * block_tables[s * max_blocks_per_seq + p / 16] at slot p % 16
  * [P5 "La tabla de paginas": token 200 is found at table position 200/16 = 12].
@@ -90,7 +105,8 @@ typedef enum pkv_status {
 
 typedef enum pkv_dtype {
   PKV_F32 = 0,
-  PKV_BF16 = 1
+  PKV_BF16 = 1,
+  PKV_FP8_E4M3 = 2 /* OCP FP8 E4M3 codes with one scale per tensor (see "FP8 cache") */
 } pkv_dtype;
 
 typedef struct pkv_pool pkv_pool;
@@ -239,7 +255,7 @@ pkv_status paged_kv_append(const void* k_new, const void* v_new, const int64_t* 
  * Pairs with an id outside [0, num_blocks) are skipped.  Destinations must
  * be distinct and must not be sources of other pairs in the same call.
  * Enqueue before paged_kv_write on the same stream so the copy sees the
- * block as it was before the new tokens arrive. */
+ * block as it was before the new tokens arrive.  dtype may be PKV_FP8_E4M3 (byte copy). */
 pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
                                 int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t num_blocks, pkv_dtype dtype, hipStream_t stream);
@@ -301,6 +317,34 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
                                   float scale, int32_t partition_size, void* workspace,
                                   size_t workspace_bytes, pkv_dtype kv_dtype, float* out,
                                   hipStream_t stream);
+
+/* FP8 cache write: like paged_kv_write, but k_new / v_new (bf16 or fp32,
+ * src_dtype) are quantised into an FP8 E4M3 cache: y = x * (1 / scale) in
+ * float32 (1 / scale rounded to float32 on the host), then the nearest E4M3
+ * code, ties to the even mantissa; magnitudes from 448 up clamp to 448, NaN
+ * gives 0x7F with the input's sign.  k_cache / v_cache hold uint8 codes in
+ * the FP8 tile order above.  Scales must be positive and finite, else
+ * PKV_ERR_INVALID; other errors as paged_kv_write. */
+pkv_status paged_kv_write_fp8(const void* k_new, const void* v_new, pkv_dtype src_dtype,
+                              const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                              int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t num_blocks, float k_scale, float v_scale,
+                              hipStream_t stream);
+
+/* Decode over an FP8 E4M3 cache: paged_attention_decode's result for K, V =
+ * code value x k_scale, v_scale (q is bf16 [B][Hq][D], out fp32).  The codes
+ * are expanded to bf16 exactly in registers; k_scale folds into the score
+ * scale and v_scale into the output.  Balanced split only (partition_size
+ * 0 implied): up to 256 sequences and a tile list below 2^31, else
+ * PKV_ERR_UNSUPPORTED.  Workspace as paged_attention_workspace_size(...,
+ * partition_size 0).  Errors otherwise as paged_attention_decode. */
+pkv_status paged_attention_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, float k_scale, float v_scale, void* workspace,
+                                      size_t workspace_bytes, float* out, hipStream_t stream);
 
 /* Multi-query attention over the paged cache (chunked prefill): several new
  * query tokens per sequence, mixed with one-token decode rows in the same

@@ -18,7 +18,7 @@ neither the 8-bit format nor how values are scaled.  Readings:
 
 Written from that definition: every code is decoded by its fields, and
 encoding is a nearest search over the 127 non-negative finite values (in
-float64, where y is exact).
+float64, where y is exact; the two neighbours of y are compared).
 """
 from __future__ import annotations
 
@@ -48,27 +48,16 @@ def encode_f32(y) -> np.ndarray:
     """float32 values -> uint8 codes: nearest E4M3 value, ties to the even
     mantissa (the even code), clamped to +-448, NaN -> NaN code."""
     y = np.asarray(y, dtype=np.float32)
-    a = np.abs(y.astype(np.float64)).ravel()
-    codes = np.empty(a.shape, dtype=np.uint8)
-    for i, v in enumerate(a):
-        if np.isnan(v):
-            codes[i] = NAN_CODE
-            continue
-        v = min(v, MAX_FINITE)
-        k = int(np.searchsorted(_POS_VALUES, v))      # first value >= v
-        if k < len(_POS_VALUES) and _POS_VALUES[k] == v:
-            codes[i] = k
-            continue
-        lo, hi = k - 1, k
-        dlo, dhi = v - _POS_VALUES[lo], _POS_VALUES[hi] - v
-        if dlo < dhi:
-            codes[i] = lo
-        elif dhi < dlo:
-            codes[i] = hi
-        else:
-            codes[i] = lo if lo % 2 == 0 else hi
-    sign = np.signbit(y.ravel()).astype(np.uint8) << 7
-    return (codes | sign).reshape(y.shape)
+    nan = np.isnan(y)
+    a = np.minimum(np.abs(np.where(nan, 0, y).astype(np.float64)), MAX_FINITE)
+    hi = np.minimum(np.searchsorted(_POS_VALUES, a), len(_POS_VALUES) - 1)   # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _POS_VALUES[lo]
+    dhi = _POS_VALUES[hi] - a
+    code = np.where(dhi == 0, hi,
+                    np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi))))
+    code = np.where(nan, NAN_CODE, code).astype(np.uint8)
+    return code | (np.signbit(y).astype(np.uint8) << 7)
 
 
 def quantize(x, scale: float) -> np.ndarray:

@@ -21,7 +21,7 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP = range(5)
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 BLOCK_SIZE = 16
 
 _i32p = C.POINTER(C.c_int32)
@@ -63,6 +63,12 @@ _SIGS = {
     "paged_attention_prefill": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
                                           C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                           C.c_int32, C.c_float, C.c_int, _vp, _vp]),
+    "paged_attention_decode_fp8": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
+                                             C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                             C.c_float, C.c_float, C.c_float, _vp, C.c_size_t, _vp,
+                                             _vp]),
+    "paged_kv_write_fp8": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, _vp, C.c_int32, C.c_int32,
+                                     C.c_int32, C.c_int32, C.c_float, C.c_float, _vp]),
     "pkv_profile_begin": (C.c_int, []),
     "pkv_profile_end": (C.c_int, [_i32p, C.POINTER(C.c_double)]),
     "pkv_stream_read": (C.c_int, [_vp, C.c_size_t, _vp, _vp]),
@@ -210,6 +216,8 @@ def _dtype_code(t) -> int:
         return PKV_F32
     if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
         return PKV_BF16
+    if t.dtype == torch.uint8:
+        return PKV_FP8_E4M3
     raise ValueError(f"unsupported cache dtype {t.dtype}")
 
 
@@ -295,6 +303,36 @@ def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, que
                                         num_blocks, mb, max_context_len, max_query_len, scale,
                                         _dtype_code(k_cache), _dev(out, "out"), _stream(stream)),
            "paged_attention_prefill")
+
+
+def paged_kv_write_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, num_kv_heads: int,
+                       head_dim: int, num_blocks: int, k_scale: float, v_scale: float,
+                       stream=None) -> None:
+    """k_new, v_new: bf16 or fp32 [T][Hkv][D]; caches: uint8 FP8 E4M3 codes."""
+    n = slot_mapping.shape[0]
+    if n == 0:
+        return
+    _check(_lib.paged_kv_write_fp8(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new),
+                                   _dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"),
+                                   _dev(v_cache, "v_cache"), n, num_kv_heads, head_dim, num_blocks,
+                                   k_scale, v_scale, _stream(stream)), "paged_kv_write_fp8")
+
+
+def paged_attention_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, out, *,
+                               num_kv_heads: int, num_blocks: int, max_context_len: int,
+                               scale: float, k_scale: float, v_scale: float, workspace=None,
+                               stream=None) -> None:
+    B, Hq, D = q.shape
+    mb = block_tables.shape[1]
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.paged_attention_decode_fp8(_dev(q, "q"), _dev(k_cache, "k_cache"),
+                                           _dev(v_cache, "v_cache"),
+                                           _dev(block_tables, "block_tables"),
+                                           _dev(context_lens, "context_lens"), B, Hq, num_kv_heads,
+                                           D, num_blocks, mb, max_context_len, scale, k_scale,
+                                           v_scale, ws_ptr, ws_bytes, _dev(out, "out"),
+                                           _stream(stream)), "paged_attention_decode_fp8")
 
 
 def pkv_profile_begin() -> None:

@@ -211,6 +211,7 @@ struct DecodeArgs {
   // wavefront (per mille of the CU's range), minimum chunk size in tiles
   float* cu_over;
   int static_permille, chunk_min;
+  float out_scale;  // FP8 cache: the V tensor scale (1 otherwise)
 };
 
 // Length check shared by the kernels: a bad length poisons the sequence.
@@ -861,6 +862,95 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ FP8 E4M3 (OCP) codes
+// Decode: the code's exponent and mantissa bits placed at the bottom of a
+// float32 exponent field, times 2^120 (the bias difference 127 - 7), give
+// the exact value for normal codes, and for exponent field 0 the float32
+// subnormal times 2^120 gives m * 2^-9; both have at most 4 significant
+// bits, so the upper 16 bits of the float32 are the exact bf16.  (The NaN
+// codes are not special-cased: the write below never stores them for
+// finite inputs.)
+__device__ inline float e4m3_to_f32(uint32_t b) {
+  return __uint_as_float(((b & 0x7Fu) << 20) | ((b & 0x80u) << 24)) * 0x1p120f;
+}
+__device__ inline uint32_t bf16x2_of(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+// 8 codes (bytes of lo then hi) -> 8 bf16 in the same order
+__device__ inline uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  uint4 r;
+  r.x = bf16x2_of(e4m3_to_f32(lo & 0xFF), e4m3_to_f32((lo >> 8) & 0xFF));
+  r.y = bf16x2_of(e4m3_to_f32((lo >> 16) & 0xFF), e4m3_to_f32(lo >> 24));
+  r.z = bf16x2_of(e4m3_to_f32(hi & 0xFF), e4m3_to_f32((hi >> 8) & 0xFF));
+  r.w = bf16x2_of(e4m3_to_f32((hi >> 16) & 0xFF), e4m3_to_f32(hi >> 24));
+  return r;
+}
+// Encode y (already divided by the tensor scale) as the nearest E4M3 code,
+// ties to the even mantissa; magnitudes from 448 up clamp to 448 (0x7E);
+// NaN gives the NaN code 0x7F; the sign bit is kept (also for zero).
+__device__ inline uint32_t f32_to_e4m3(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (a != a) return sign | 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0x1p-6f) return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));  // m * 2^-9
+  uint32_t u = __float_as_uint(a);
+  u += 0x7FFFFu + ((u >> 20) & 1u);  // round the mantissa to 3 bits, ties to even
+  const uint32_t code = ((((u >> 23) & 0xFFu) - 120u) << 3) | ((u >> 20) & 7u);
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// FP8 cache write: one thread per (token, kv head, group of 8 channels);
+// the inputs (bf16 or fp32) are multiplied by the inverse tensor scales in
+// float32 and encoded.  FP8 tile order (one byte per element, W = D / 4
+// bytes per lane): K byte (t, d) at W (16 ((d / 8) % 4) + t) + 8 (d / 32) +
+// d % 8; V byte (t, d) at W (16 (t / 4) + d % 16) + 8 (d / 32) +
+// ((d / 16) % 2) 4 + t % 4 -- the bf16 tile's lane and piece order.
+template <typename T>
+__device__ inline float widen_in(T x);
+template <>
+__device__ inline float widen_in<uint16_t>(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+template <>
+__device__ inline float widen_in<float>(float x) { return x; }
+
+template <typename T>
+__global__ void kv_write_fp8_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
+                                    const int64_t* __restrict__ slots, uint8_t* __restrict__ kc,
+                                    uint8_t* __restrict__ vc, int64_t total, int num_kv_heads,
+                                    int head_dim, int64_t num_slots, float k_inv, float v_inv) {
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int chunks = head_dim >> 3;
+  const int c = static_cast<int>(idx % chunks);
+  const int64_t ih = idx / chunks;
+  const int h = static_cast<int>(ih % num_kv_heads);
+  const int64_t i = ih / num_kv_heads;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot >> 4;
+  const int t = static_cast<int>(slot & 15);
+  const int64_t src = (i * num_kv_heads + h) * head_dim + c * 8;
+  const int64_t tile = (blk * num_kv_heads + h) * int64_t(kBlock) * head_dim;
+  const int W = head_dim / 4;
+  uint32_t kq[8], vq[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    kq[e] = f32_to_e4m3(widen_in<T>(k_new[src + e]) * k_inv);
+    vq[e] = f32_to_e4m3(widen_in<T>(v_new[src + e]) * v_inv);
+  }
+  // K: the 8 channels of the group are 8 consecutive bytes of one lane piece
+  const int d0 = c * 8;
+  uint8_t* kd = kc + tile + W * (16 * ((d0 / 8) % 4) + t) + 8 * (d0 / 32);
+  *reinterpret_cast<uint2*>(kd) = make_uint2(kq[0] | (kq[1] << 8) | (kq[2] << 16) | (kq[3] << 24),
+                                             kq[4] | (kq[5] << 8) | (kq[6] << 16) | (kq[7] << 24));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = d0 + e;
+    vc[tile + W * (16 * (t / 4) + d % 16) + 8 * (d / 32) + ((d / 16) % 2) * 4 + t % 4] =
+        static_cast<uint8_t>(vq[e]);
+  }
+}
+
 // ------------------------------------------------------------------ A5: decode, bf16, per-CU balanced
 // The same tile list, split first into one contiguous range per compute
 // unit (one workgroup of 8 wavefronts per CU, holding all of its LDS).
@@ -890,13 +980,16 @@ __host__ __device__ inline int cu_lds_slots(int group, int head_dim) {
   return n > kCuSlots ? kCuSlots : n;
 }
 
-template <int D, int ST, int AUX>
+// F8: the cache holds FP8 E4M3 codes (tiles of 16 D bytes, converted to
+// bf16 in registers; scales folded into the score scale and out_scale).
+template <int D, int ST, int AUX, bool F8 = false>
 __global__ __launch_bounds__(64 * kCuWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_bf16_cu_kernel(DecodeArgs a) {
   constexpr int NJ = D / 32;
   constexpr int NT = D / 16;
+  constexpr int NJ8 = NJ / 2;  // 16-byte loads per lane per FP8 tile (K and V each)
   constexpr int64_t TILE = int64_t(kBlock) * D;
-  constexpr int TILE_BYTES = static_cast<int>(TILE * 2);
+  constexpr int TILE_BYTES = static_cast<int>(TILE * (F8 ? 1 : 2));
   constexpr int NW = kCuWaves;
   constexpr int NKMAX = 16 * D / 64;  // folded elements per lane: group * D / 64
 
@@ -1035,7 +1128,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   const int qoff = (hcol * D + grp * 8) * 2;  // >= g*D*2 for padded heads: reads as 0
   const int qbytes = g * D * 2;
 
-  uint4 kr[ST][NJ], vr[ST][NJ], qr[ST][NJ];
+  uint4 kr[ST][F8 ? NJ8 : NJ], vr[ST][F8 ? NJ8 : NJ], qr[ST][NJ];
   bool st_bad[ST], rec_live[ST], rec_first[ST], rec_last[ST];
   int rec_kvh[ST], rec_b[ST], rec_blk[ST], rec_L[ST], rec_nb[ST], rec_idx[ST];
 
@@ -1066,11 +1159,22 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     const char* qb = static_cast<const char*>(a.q) +
                      (int64_t(l_b) * a.num_q_heads + int64_t(l_kvh) * g) * D * 2;
     const __amdgpu_buffer_rsrc_t rq = tile_rsrc(qb, needq ? qbytes : 0);
+    if constexpr (F8) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      kr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + 1024 * j, 0, AUX));
-      vr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + 1024 * j, 0, AUX));
-      qr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 64 * j, 0, 0));
+      for (int j = 0; j < NJ8; ++j) {
+        kr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane * (D / 4) + 16 * j, 0, AUX));
+        vr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane * (D / 4) + 16 * j, 0, AUX));
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        qr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 64 * j, 0, 0));
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        kr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + 1024 * j, 0, AUX));
+        vr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + 1024 * j, 0, AUX));
+        qr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 64 * j, 0, 0));
+      }
     }
     st_bad[st] = bad;
     if (live) {
@@ -1101,7 +1205,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int h = grp * 4 + r;
         const float lr = __shfl(lt, h);
-        const float inv = seg_bad ? __builtin_nanf("") : 1.0f / lr;
+        const float inv = seg_bad ? __builtin_nanf("") : a.out_scale / lr;
         if (h < g) {
           float* dst = a.out + (head0 + h) * D + hcol;
 #pragma unroll
@@ -1165,10 +1269,23 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
       seg_start_idx = rec_idx[st];
     }
     seg_bad |= st_bad[st];
+    // the stage's K and V as bf16 operand pieces
+    uint4 kx[NJ], vx[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if constexpr (F8) {
+        const uint4 kw = kr[st][j / 2], vw = vr[st][j / 2];
+        kx[j] = (j & 1) ? e4m3x8_to_bf16x8(kw.z, kw.w) : e4m3x8_to_bf16x8(kw.x, kw.y);
+        vx[j] = (j & 1) ? e4m3x8_to_bf16x8(vw.z, vw.w) : e4m3x8_to_bf16x8(vw.x, vw.y);
+      } else {
+        kx[j] = kr[st][j];
+        vx[j] = vr[st][j];
+      }
+    }
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[st][j]), qf[j], s,
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kx[j]), qf[j], s,
                                                    0, 0, 0);
     const int tb = c_blk * kBlock + grp * 4;
     float sv[4];
@@ -1204,16 +1321,16 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
       const uint32_t m23 = (tb + 2 < c_L ? 0x0000FFFFu : 0u) | (tb + 3 < c_L ? 0xFFFF0000u : 0u);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        vr[st][j].x &= m01;
-        vr[st][j].y &= m23;
-        vr[st][j].z &= m01;
-        vr[st][j].w &= m23;
+        vx[j].x &= m01;
+        vx[j].y &= m23;
+        vx[j].z &= m01;
+        vx[j].w &= m23;
       }
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const s16x4 v0 = __builtin_bit_cast(s16x4, make_uint2(vr[st][j].x, vr[st][j].y));
-      const s16x4 v1 = __builtin_bit_cast(s16x4, make_uint2(vr[st][j].z, vr[st][j].w));
+      const s16x4 v0 = __builtin_bit_cast(s16x4, make_uint2(vx[j].x, vx[j].y));
+      const s16x4 v1 = __builtin_bit_cast(s16x4, make_uint2(vx[j].z, vx[j].w));
       o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, v0, o[2 * j], 0, 0, 0);
       o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, v0, o[2 * j], 0, 0, 0);
       o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, v1, o[2 * j + 1], 0, 0, 0);
@@ -1298,7 +1415,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     if (!cross_start && !cross_end) {
 #pragma unroll
       for (int k = 0; k < NKMAX; ++k)
-        if (k < nk) a.out[head0 * D + 64 * k + lane] = bad ? __builtin_nanf("") : acc[k] / den[k];
+        if (k < nk) a.out[head0 * D + 64 * k + lane] = bad ? __builtin_nanf("") : acc[k] / den[k] * a.out_scale;
     } else {
       // this CU's share of a sequence that crosses its range: slot 0 when
       // the sequence begins at or before the range start, else slot 1
@@ -1376,7 +1493,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < NKMAX; ++k)
         if (k < nk)
-          a.out[head0 * D + 64 * k + lane] = gbad ? __builtin_nanf("") : gacc[k] / gden[k];
+          a.out[head0 * D + 64 * k + lane] = gbad ? __builtin_nanf("") : gacc[k] / gden[k] * a.out_scale;
     }
   }
 }
@@ -1901,9 +2018,15 @@ void launch_decode_bf16_balanced(unsigned grid, hipStream_t stream, const Decode
   }
 }
 
-void launch_decode_bf16_cu(unsigned grid, hipStream_t stream, const DecodeArgs& a, int head_dim) {
+void launch_decode_bf16_cu(unsigned grid, hipStream_t stream, const DecodeArgs& a, int head_dim,
+                           bool fp8) {
   const dim3 block(64 * kCuWaves);
-  if (head_dim == 64) {
+  if (fp8) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL((decode_bf16_cu_kernel<64, 3, 2, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_bf16_cu_kernel<128, 2, 2, true>), grid, block, 0, stream, a);
+  } else if (head_dim == 64) {
     hipLaunchKernelGGL((decode_bf16_cu_kernel<64, 3, 2>), grid, block, 0, stream, a);
   } else {
     hipLaunchKernelGGL((decode_bf16_cu_kernel<128, 2, 2>), grid, block, 0, stream, a);
@@ -2008,10 +2131,11 @@ pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pai
                                 int32_t num_blocks, pkv_dtype dtype, hipStream_t stream) {
   if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0)
     return PKV_ERR_INVALID;
-  if (head_dim % 32 != 0 || elem_size(dtype) == 0) return PKV_ERR_UNSUPPORTED;
+  const int esize = dtype == PKV_FP8_E4M3 ? 1 : elem_size(dtype);
+  if (head_dim % 32 != 0 || esize == 0) return PKV_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !pairs) return PKV_ERR_INVALID;
-  const int64_t run_bytes = int64_t(num_kv_heads) * kBlock * head_dim * elem_size(dtype);
+  const int64_t run_bytes = int64_t(num_kv_heads) * kBlock * head_dim * esize;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, stream,
                      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), pairs,
                      run_bytes / 16, num_blocks);
@@ -2078,23 +2202,32 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
   return launch_status();
 }
 
-pkv_status paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
-                                  const int32_t* block_tables, const int32_t* context_lens,
-                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                  int32_t head_dim, int32_t num_blocks,
-                                  int32_t max_blocks_per_seq, int32_t max_context_len,
-                                  float scale, int32_t partition_size, void* workspace,
-                                  size_t workspace_bytes, pkv_dtype kv_dtype, float* out,
-                                  hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Decode for every cache dtype; fp8 (E4M3 codes with tensor scales) runs
+// only in the per-CU balanced form.
+pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                       float scale, int32_t partition_size, void* workspace,
+                       size_t workspace_bytes, pkv_dtype kv_dtype, float k_scale, float v_scale,
+                       float* out, hipStream_t stream) {
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || partition_size < 0)
     return PKV_ERR_INVALID;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
   if (partition_size % 32 != 0) return PKV_ERR_INVALID;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
-  if (elem_size(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
+  if (elem_size(kv_dtype) == 0 && !fp8) return PKV_ERR_UNSUPPORTED;
+  if (fp8 && (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) ||
+              !std::isfinite(v_scale)))
+    return PKV_ERR_INVALID;
+  if (fp8 && partition_size != 0) return PKV_ERR_UNSUPPORTED;
   const int group = num_q_heads / num_kv_heads;
-  if (kv_dtype == PKV_BF16 && group > 16) return PKV_ERR_UNSUPPORTED;
+  if ((kv_dtype == PKV_BF16 || fp8) && group > 16) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return PKV_ERR_INVALID;
@@ -2102,7 +2235,7 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
   const int64_t max_parts = max_parts_for(max_context_len, part);
   // one workgroup per (partition, sequence, head) must fit a 1D grid
   if (max_parts * num_seqs * num_q_heads > 0x7FFFFFFF) return PKV_ERR_UNSUPPORTED;
-  const bool balanced = kv_dtype == PKV_BF16 && partition_size == 0;
+  const bool balanced = (kv_dtype == PKV_BF16 || fp8) && partition_size == 0;
   const int waves = balanced ? balanced_waves() : 0;
   if (balanced && waves <= 0) return PKV_ERR_HIP;
   const size_t need =
@@ -2134,7 +2267,8 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
   a.max_ctx = max_context_len;
   a.part_tokens = part;
   a.max_parts = static_cast<int>(max_parts);
-  a.scale_log2e = scale * 1.4426950408889634f;
+  a.scale_log2e = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
+  a.out_scale = fp8 ? v_scale : 1.0f;
   a.grid_waves = waves;
   a.bw_o = balanced ? ws : nullptr;
   a.bw_m = balanced ? ws + size_t(waves) * 2 * group * head_dim : nullptr;
@@ -2157,12 +2291,13 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
   const bool cu_form = balanced && cu_split_enabled() && num_seqs <= 256 &&
                        int64_t(num_seqs) * max_blocks_per_seq * num_kv_heads < (int64_t(1) << 31) &&
                        cus > 0 && cus <= waves;
+  if (fp8 && !cu_form) return PKV_ERR_UNSUPPORTED;
 
   const bool prof = g_prof.on && g_prof.used + 2 <= g_prof.pool.size();
   if (prof) (void)hipEventRecord(g_prof.pool[g_prof.used], stream);
   if (balanced) {
     if (cu_form)
-      launch_decode_bf16_cu(static_cast<unsigned>(cus), stream, a, head_dim);
+      launch_decode_bf16_cu(static_cast<unsigned>(cus), stream, a, head_dim, fp8);
     else
       launch_decode_bf16_balanced(static_cast<unsigned>(waves), stream, a, head_dim);
     if (prof) {
@@ -2192,6 +2327,72 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
     hipLaunchKernelGGL(lse_reduce_kernel<128>, dim3(rgrid), dim3(64), 0, stream, a);
   else
     hipLaunchKernelGGL(lse_reduce_kernel<64>, dim3(rgrid), dim3(64), 0, stream, a);
+  return launch_status();
+}
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  float scale, int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, pkv_dtype kv_dtype, float* out,
+                                  hipStream_t stream) {
+  if (kv_dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;  // needs the scales
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len,
+                     scale, partition_size, workspace, workspace_bytes, kv_dtype, 1.0f, 1.0f, out,
+                     stream);
+}
+
+pkv_status paged_attention_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, float k_scale, float v_scale, void* workspace,
+                                      size_t workspace_bytes, float* out, hipStream_t stream) {
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len,
+                     scale, 0, workspace, workspace_bytes, PKV_FP8_E4M3, k_scale, v_scale, out,
+                     stream);
+}
+
+pkv_status paged_kv_write_fp8(const void* k_new, const void* v_new, pkv_dtype src_dtype,
+                              const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                              int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t num_blocks, float k_scale, float v_scale,
+                              hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0)
+    return PKV_ERR_INVALID;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return PKV_ERR_INVALID;
+  if (head_dim % 32 != 0) return PKV_ERR_UNSUPPORTED;
+  if (src_dtype != PKV_BF16 && src_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_INVALID;
+  const int64_t num_slots = int64_t(num_blocks) * kBlock;
+  if (debug_checks()) {
+    pkv_status st = check_slots(slot_mapping, num_tokens, num_slots, stream);
+    if (st != PKV_OK) return st;
+  }
+  const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;
+  const int64_t total = int64_t(num_tokens) * num_kv_heads * (head_dim / 8);
+  const int threads = 256;
+  const int64_t grid = (total + threads - 1) / threads;
+  if (src_dtype == PKV_BF16)
+    hipLaunchKernelGGL(kv_write_fp8_kernel<uint16_t>, dim3(grid), dim3(threads), 0, stream,
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                       slot_mapping, static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                       total, num_kv_heads, head_dim, num_slots, k_inv, v_inv);
+  else
+    hipLaunchKernelGGL(kv_write_fp8_kernel<float>, dim3(grid), dim3(threads), 0, stream,
+                       static_cast<const float*>(k_new), static_cast<const float*>(v_new),
+                       slot_mapping, static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                       total, num_kv_heads, head_dim, num_slots, k_inv, v_inv);
   return launch_status();
 }
 

@@ -72,20 +72,27 @@ class _Staging:
 class PagedKV:
     def __init__(self, *, num_blocks: int, num_seqs: int, max_blocks_per_seq: int,
                  num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
-                 device="cuda", init_order=None, fill=None, partition_size: int = 0):
+                 device="cuda", init_order=None, fill=None, partition_size: int = 0,
+                 k_scale: float = 1.0, v_scale: float = 1.0):
+        """dtype "f32", "bf16" or "fp8" (E4M3 codes with tensor scales k_scale,
+        v_scale; appended rows are bf16 or fp32 and quantised on write)."""
         self.num_blocks, self.num_seqs, self.max_blocks = num_blocks, num_seqs, max_blocks_per_seq
         self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
         self.dtype = dtype
+        self.k_scale, self.v_scale = k_scale, v_scale
         self.device = torch.device(device)
         self.partition_size = partition_size
         self.pool = capi.pkv_pool_create(num_blocks, BLOCK, init_order)
-        tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dtype]
         n = num_blocks * num_kv_heads * BLOCK * head_dim
         self.k_cache = torch.empty(n, dtype=tdt, device=self.device)
         self.v_cache = torch.empty(n, dtype=tdt, device=self.device)
         if fill is None:
             self.k_cache.zero_()
             self.v_cache.zero_()
+        elif dtype == "fp8":
+            self.k_cache.fill_(0x7F)   # the NaN code
+            self.v_cache.fill_(0x7F)
         else:
             self.k_cache.fill_(fill)
             self.v_cache.fill_(fill)
@@ -128,8 +135,15 @@ class PagedKV:
         self.lens_d = d_lens
         capi.paged_kv_copy_blocks(self.k_cache, self.v_cache, d_cows, self.num_kv_heads,
                                   self.head_dim, self.num_blocks, s)
-        capi.paged_kv_append(k_new, v_new, d_slots, self.k_cache, self.v_cache, self.num_kv_heads,
-                             self.head_dim, self.num_blocks, self.tables_d, d_upd, s)
+        if self.dtype == "fp8":
+            capi.paged_block_table_update(self.tables_d, d_upd, s)
+            capi.paged_kv_write_fp8(k_new, v_new, d_slots, self.k_cache, self.v_cache,
+                                    self.num_kv_heads, self.head_dim, self.num_blocks,
+                                    self.k_scale, self.v_scale, s)
+        else:
+            capi.paged_kv_append(k_new, v_new, d_slots, self.k_cache, self.v_cache,
+                                 self.num_kv_heads, self.head_dim, self.num_blocks, self.tables_d,
+                                 d_upd, s)
         return slots, upd, cows
 
     def decode(self, q, scale: float, out=None, stream=None, partition_size=None):
@@ -144,6 +158,14 @@ class PagedKV:
                                                    max_ctx, ps)
         if need > ws.numel() * 4:
             ws = self.workspace = torch.empty(need // 4, dtype=torch.float32, device=self.device)
+        if self.dtype == "fp8":
+            capi.paged_attention_decode_fp8(q, self.k_cache, self.v_cache, self.tables_d,
+                                            self.lens_d, out, num_kv_heads=self.num_kv_heads,
+                                            num_blocks=self.num_blocks, max_context_len=max_ctx,
+                                            scale=scale, k_scale=self.k_scale,
+                                            v_scale=self.v_scale, workspace=ws,
+                                            stream=stream.cuda_stream)
+            return out
         capi.paged_attention_decode(q, self.k_cache, self.v_cache, self.tables_d, self.lens_d, out,
                                     num_kv_heads=self.num_kv_heads, num_blocks=self.num_blocks,
                                     max_context_len=max_ctx, scale=scale, partition_size=ps,
