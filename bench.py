@@ -167,6 +167,44 @@ def prefill_measure(dev, reps: int = 20):
             "unique_kv_gb_per_s": round(kv_unique / ms / 1e6, 1)}
 
 
+def fp8_measure(dev, w, reps: int = 50):
+    """Decode alone over an FP8 E4M3 copy of the headline workload's cache
+    (same lengths, same block placement, rows quantised with per-tensor
+    scales on the GPU): time per call and rate of its FP8 bytes."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_102_amd.driver import PagedKV, replay_prefill
+    s = w.spec
+
+    def to_dev(rows):
+        return torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).to(dev).view(torch.bfloat16)
+    kv = PagedKV(num_blocks=w.num_blocks, num_seqs=s.num_seqs,
+                 max_blocks_per_seq=w.max_blocks_per_seq, num_q_heads=s.num_q_heads,
+                 num_kv_heads=s.num_kv_heads, head_dim=s.head_dim, dtype="fp8", device=dev,
+                 init_order=w.pool_order, k_scale=6.0 / 448, v_scale=6.0 / 448)
+    replay_prefill(kv, w, to_dev)
+    q = to_dev(w.q)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    for _ in range(10):
+        kv.decode(q, s.scale, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        kv.decode(q, s.scale, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    b = kv_bytes(kv.lens, s.num_kv_heads, s.head_dim, elem=1)
+    res = {"workload": f"{WORKLOAD} at its prefill lengths, FP8 E4M3 cache", "ms": round(ms, 4),
+           "kv_bytes": b, "kv_gb_per_s": round(b / ms / 1e6, 1),
+           "frac_of_hbm_peak": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
+           "seqs_per_s": round(s.num_seqs / ms * 1e3, 1)}
+    del kv
+    torch.cuda.empty_cache()
+    return res
+
+
 def kv_bytes(lens, num_kv_heads, head_dim, elem=2) -> int:
     return int(lens.astype("int64").sum()) * 2 * num_kv_heads * head_dim * elem
 
@@ -209,6 +247,8 @@ def main():
                     help="run one plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--no-contiguous", dest="contiguous", action="store_false",
                     help="skip the paged-vs-contiguous comparison")
+    ap.add_argument("--no-fp8", dest="fp8", action="store_false",
+                    help="skip the FP8 cache decode measurement")
     ap.add_argument("--no-prefill", dest="prefill", action="store_false",
                     help="skip the multi-query (chunked prefill) measurement")
     ap.add_argument("--all-configs", metavar="PATH", default=None,
@@ -343,6 +383,7 @@ def main():
         ceiling = buf.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         del buf, sink
 
+    fp8 = fp8_measure(dev, w) if args.fp8 else None
     prefill = None
     if args.prefill:
         torch.cuda.synchronize()
@@ -383,6 +424,7 @@ def main():
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
         "paged_vs_contiguous": paged_vs_contig,
         "prefill_chunked": prefill,
+        "fp8_decode": fp8,
         "hbm_read_ceiling_gbs": round(ceiling, 1) if ceiling else None,
         "decode_frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None,
     }

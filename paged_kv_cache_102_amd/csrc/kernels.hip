@@ -863,26 +863,25 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ FP8 E4M3 (OCP) codes
-// Decode: the code's exponent and mantissa bits placed at the bottom of a
-// float32 exponent field, times 2^120 (the bias difference 127 - 7), give
-// the exact value for normal codes, and for exponent field 0 the float32
-// subnormal times 2^120 gives m * 2^-9; both have at most 4 significant
-// bits, so the upper 16 bits of the float32 are the exact bf16.  (The NaN
-// codes are not special-cased: the write below never stores them for
-// finite inputs.)
-__device__ inline float e4m3_to_f32(uint32_t b) {
-  return __uint_as_float(((b & 0x7Fu) << 20) | ((b & 0x80u) << 24)) * 0x1p120f;
-}
+// Decode: gfx950's v_cvt_pk_f32_fp8 expands two E4M3 codes to float32 (it
+// reads the OCP E4M3 encoding; its output matches the format's definition
+// for all 256 codes, NaN included, on MI355X).  Every E4M3 value has at most
+// 4 significant bits, so the upper 16 bits of the float32 are the exact
+// bf16.
 __device__ inline uint32_t bf16x2_of(float lo, float hi) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
 }
 // 8 codes (bytes of lo then hi) -> 8 bf16 in the same order
 __device__ inline uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), false);  // bytes 0, 1
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), true);   // bytes 2, 3
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), true);
   uint4 r;
-  r.x = bf16x2_of(e4m3_to_f32(lo & 0xFF), e4m3_to_f32((lo >> 8) & 0xFF));
-  r.y = bf16x2_of(e4m3_to_f32((lo >> 16) & 0xFF), e4m3_to_f32(lo >> 24));
-  r.z = bf16x2_of(e4m3_to_f32(hi & 0xFF), e4m3_to_f32((hi >> 8) & 0xFF));
-  r.w = bf16x2_of(e4m3_to_f32((hi >> 16) & 0xFF), e4m3_to_f32(hi >> 24));
+  r.x = bf16x2_of(a[0], a[1]);
+  r.y = bf16x2_of(b[0], b[1]);
+  r.z = bf16x2_of(c[0], c[1]);
+  r.w = bf16x2_of(d[0], d[1]);
   return r;
 }
 // Encode y (already divided by the tensor scale) as the nearest E4M3 code,
