@@ -176,6 +176,52 @@ pkv_status kv_pool_stats(const pkv_pool* pool, pkv_stats* out_stats);
 pkv_status kv_pool_free_list(const pkv_pool* pool, int32_t capacity, int32_t* out_ids,
                              int32_t* out_n);
 
+/* ===== Prefix caching by block hash ==========================================
+ * ["Como funciona realmente vLLM", «Automatic Prefix Caching»: instead of
+ * dropping a finished request's blocks, the engine indexes them by a hash of
+ * their content, and a new request that starts with the same tokens (a
+ * shared system prompt or conversation history) reuses those blocks in
+ * VRAM without recomputing them; "PagedAttention por dentro", «Prefix
+ * caching cross-session»: blocks are hashed, no radix tree.]  Readings:
+ *   - only full blocks are indexed; a block's content is its 16 token ids
+ *     together with the chain of indexed blocks holding every earlier token
+ *     (a block matches only as part of a matching prefix);
+ *   - an indexed block whose last reference is dropped stays indexed on a
+ *     second free list, least recently freed first; allocations take blocks
+ *     holding nothing first (the LIFO stack), then evict the least recently
+ *     freed indexed block, which leaves the index together with every block
+ *     indexed below it;
+ *   - the hash (FNV-1a over the parent id and tokens) only locates
+ *     candidates; a hit is confirmed by comparing parent and tokens, so a
+ *     match is exact.
+ * The free list seen by kv_pool_free_list / kv_pool_stats is the stack
+ * (top first) followed by the indexed free blocks (least recent first). */
+
+/* Turns prefix caching on for this pool (idempotent). */
+pkv_status pkv_prefix_cache_enable(pkv_pool* pool);
+
+/* The longest run of indexed blocks holding tokens[0 .. 16 k) (k <= number
+ * of full blocks of tokens, k <= max_blocks): their ids go to out_ids[0..k)
+ * in order and each gains one reference (an indexed free block leaves the
+ * free list).  The caller puts them at the head of the new sequence's
+ * table with length 16 k and appends the remaining tokens as usual.
+ * tokens: host int32 [num_tokens].  Prefix caching off -> PKV_ERR_INVALID. */
+pkv_status pkv_prefix_match(pkv_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                            int32_t max_blocks, int32_t* out_ids, int32_t* out_num_blocks);
+
+/* Indexes the full blocks of a sequence whose K/V are written: block i
+ * (i < num_tokens / 16) is block_ids[i] and holds tokens[16 i .. 16 i + 16).
+ * A block already indexed is left as it is (it must hold exactly that
+ * content); a block whose content is already indexed under another id is
+ * not indexed again (the chain continues through the indexed one).  The
+ * blocks must be live and distinct, else PKV_ERR_INVALID with nothing
+ * changed. */
+pkv_status pkv_prefix_register(pkv_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                               const int32_t* block_ids);
+
+/* Number of indexed blocks, and how many of them are free. */
+pkv_status pkv_prefix_stats(const pkv_pool* pool, int32_t* num_cached, int32_t* num_cached_free);
+
 /* ===== Slot planning for appended tokens (host) =============================
  * [P5 "La tabla de paginas"]: when a sequence produces a token at position
  * p (p = tokens already cached), it is written into the last block if that

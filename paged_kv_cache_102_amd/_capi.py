@@ -45,6 +45,10 @@ _SIGS = {
     "kv_block_refcount": (C.c_int, [_vp, C.c_int32, _i32p]),
     "kv_pool_stats": (C.c_int, [_vp, C.POINTER(pkv_stats)]),
     "kv_pool_free_list": (C.c_int, [_vp, C.c_int32, _i32p, _i32p]),
+    "pkv_prefix_cache_enable": (C.c_int, [_vp]),
+    "pkv_prefix_match": (C.c_int, [_vp, _i32p, C.c_int32, C.c_int32, _i32p, _i32p]),
+    "pkv_prefix_register": (C.c_int, [_vp, _i32p, C.c_int32, _i32p]),
+    "pkv_prefix_stats": (C.c_int, [_vp, _i32p, _i32p]),
     "paged_kv_append_slots": (C.c_int, [_vp, C.c_int32, C.c_int32, _i32p, _i32p, _i32p, _i64p,
                                         C.c_int64, _i32p, C.c_int32, _i32p, _i32p, C.c_int32,
                                         _i32p]),
@@ -167,6 +171,36 @@ def kv_pool_free_list(pool: Pool) -> np.ndarray:
     _check(_lib.kv_pool_free_list(pool.handle, n.value, out.ctypes.data_as(_i32p), C.byref(n)),
            "kv_pool_free_list")
     return out
+
+
+def pkv_prefix_cache_enable(pool: Pool) -> None:
+    _check(_lib.pkv_prefix_cache_enable(pool.handle), "pkv_prefix_cache_enable")
+
+
+def pkv_prefix_match(pool: Pool, tokens, max_blocks: int | None = None) -> np.ndarray:
+    """Ids of the cached blocks holding the longest indexed prefix of tokens
+    (one reference taken on each)."""
+    arr, ptr = _i32(tokens)
+    cap = arr.size // BLOCK_SIZE if max_blocks is None else max_blocks
+    out = np.empty(max(cap, 1), dtype=np.int32)
+    n = C.c_int32()
+    _check(_lib.pkv_prefix_match(pool.handle, ptr, arr.size, cap, out.ctypes.data_as(_i32p),
+                                 C.byref(n)), "pkv_prefix_match")
+    return out[:n.value].copy()
+
+
+def pkv_prefix_register(pool: Pool, tokens, block_ids) -> None:
+    arr, ptr = _i32(tokens)
+    ids, iptr = _i32(block_ids)
+    if ids.size < arr.size // BLOCK_SIZE:
+        raise ValueError("fewer block ids than full blocks")
+    _check(_lib.pkv_prefix_register(pool.handle, ptr, arr.size, iptr), "pkv_prefix_register")
+
+
+def pkv_prefix_stats(pool: Pool):
+    a, b = C.c_int32(), C.c_int32()
+    _check(_lib.pkv_prefix_stats(pool.handle, C.byref(a), C.byref(b)), "pkv_prefix_stats")
+    return a.value, b.value
 
 
 def paged_kv_append_slots(pool: Pool, block_tables: np.ndarray, context_lens: np.ndarray,

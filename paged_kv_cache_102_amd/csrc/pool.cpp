@@ -11,18 +11,64 @@
 //
 // The free list is a LIFO stack (std::vector, top at the back).  Every call
 // validates before it mutates, so a failing call leaves the pool unchanged.
+//
+// Prefix caching ("Como funciona realmente vLLM", "Automatic Prefix
+// Caching": instead of dropping a finished request's blocks, the engine
+// indexes them by a hash of their content and a new request that starts
+// with the same tokens reuses them directly): once enabled, full blocks are
+// registered under (the registered block holding the previous 16 tokens,
+// their 16 token ids), so a block is found only through the chain of
+// blocks holding everything before it.  A registered block whose last
+// reference is dropped stays indexed on a second free list, least recently
+// freed first; allocation takes blocks holding nothing first (the LIFO
+// stack) and only then evicts the least recently freed cached block.  An
+// evicted block leaves the index with every block registered below it (they
+// stay where they are on the free lists).  The hash only locates
+// candidates; a hit is confirmed by comparing the parent and the tokens.
 #include <algorithm>
+#include <array>
 #include <cstdint>
+#include <list>
 #include <new>
 #include <unordered_map>
 #include <vector>
 
 #include "pagedkv.h"
 
+namespace {
+struct CachedBlock {
+  int32_t parent = -1;                        // registered block of the previous 16 tokens, -1 for the first
+  std::vector<int32_t> children;              // blocks registered with this one as parent
+  std::array<int32_t, PKV_BLOCK_SIZE> tokens{};
+  uint64_t hash = 0;
+  bool on = false;                            // registered
+  std::list<int32_t>::iterator lru_it;        // valid while refcount 0 and registered
+};
+
+// FNV-1a (64-bit) over the parent id and the token ids, 4 bytes each, little end first.
+uint64_t block_hash(int32_t parent, const int32_t* tokens) {
+  uint64_t h = 0xcbf29ce484222325ull;
+  auto mix = [&](uint32_t v) {
+    for (int i = 0; i < 4; ++i) {
+      h ^= (v >> (8 * i)) & 0xFFu;
+      h *= 0x100000001b3ull;
+    }
+  };
+  mix(static_cast<uint32_t>(parent));
+  for (int i = 0; i < PKV_BLOCK_SIZE; ++i) mix(static_cast<uint32_t>(tokens[i]));
+  return h;
+}
+}  // namespace
+
 struct pkv_pool {
   int32_t num_blocks = 0;
   std::vector<int32_t> free_stack;  // back() is handed out next
   std::vector<int32_t> ref;         // 0 = free
+  // prefix caching (off until pkv_prefix_cache_enable)
+  bool prefix_on = false;
+  std::vector<CachedBlock> cached;
+  std::unordered_multimap<uint64_t, int32_t> index;
+  std::list<int32_t> lru;           // cached blocks with refcount 0, least recently freed first
 };
 
 namespace {
@@ -31,11 +77,65 @@ bool live(const pkv_pool* p, int32_t id) {
   return id >= 0 && id < p->num_blocks && p->ref[id] > 0;
 }
 
+size_t num_free(const pkv_pool* p) { return p->free_stack.size() + p->lru.size(); }
+
+// Removes `id` and everything registered below it from the index.
+void unregister(pkv_pool* p, int32_t id) {
+  std::vector<int32_t> todo{id};
+  while (!todo.empty()) {
+    const int32_t x = todo.back();
+    todo.pop_back();
+    CachedBlock& c = p->cached[x];
+    if (!c.on) continue;
+    auto range = p->index.equal_range(c.hash);
+    for (auto it = range.first; it != range.second; ++it)
+      if (it->second == x) {
+        p->index.erase(it);
+        break;
+      }
+    c.on = false;
+    for (int32_t ch : c.children)
+      if (p->cached[ch].on && p->cached[ch].parent == x) todo.push_back(ch);
+    c.children.clear();
+  }
+}
+
+// Hands out a free block (refcount 1): one holding nothing first, else the
+// least recently freed cached block, which leaves the index.
 int32_t pop_block(pkv_pool* p) {
-  int32_t id = p->free_stack.back();
-  p->free_stack.pop_back();
+  int32_t id;
+  if (!p->free_stack.empty()) {
+    id = p->free_stack.back();
+    p->free_stack.pop_back();
+  } else {
+    id = p->lru.front();
+    p->lru.pop_front();
+    unregister(p, id);
+  }
   p->ref[id] = 1;
   return id;
+}
+
+// The last reference of `id` is gone.
+void release(pkv_pool* p, int32_t id) {
+  if (p->prefix_on && p->cached[id].on) {
+    p->lru.push_back(id);
+    p->cached[id].lru_it = std::prev(p->lru.end());
+  } else {
+    p->free_stack.push_back(id);
+  }
+}
+
+// The registered block matching (parent, tokens), or -1.
+int32_t find_cached(const pkv_pool* p, int32_t parent, const int32_t* tokens) {
+  const uint64_t h = block_hash(parent, tokens);
+  auto range = p->index.equal_range(h);
+  for (auto it = range.first; it != range.second; ++it) {
+    const CachedBlock& c = p->cached[it->second];
+    if (c.parent == parent && std::equal(c.tokens.begin(), c.tokens.end(), tokens))
+      return it->second;
+  }
+  return -1;
 }
 
 }  // namespace
@@ -83,7 +183,7 @@ void pkv_pool_destroy(pkv_pool* pool) { delete pool; }
 
 pkv_status kv_block_alloc(pkv_pool* p, int32_t n, int32_t* out_ids) {
   if (!p || n < 0 || (n > 0 && !out_ids)) return PKV_ERR_INVALID;
-  if (static_cast<size_t>(n) > p->free_stack.size()) return PKV_ERR_OOM;
+  if (static_cast<size_t>(n) > num_free(p)) return PKV_ERR_OOM;
   for (int32_t i = 0; i < n; ++i) out_ids[i] = pop_block(p);
   return PKV_OK;
 }
@@ -106,7 +206,7 @@ pkv_status kv_block_free(pkv_pool* p, int32_t n, const int32_t* ids) {
   }
   for (int32_t i = 0; i < n; ++i) {
     int32_t id = ids[i];
-    if (--p->ref[id] == 0) p->free_stack.push_back(id);
+    if (--p->ref[id] == 0) release(p, id);
   }
   return PKV_OK;
 }
@@ -118,7 +218,7 @@ pkv_status kv_block_cow(pkv_pool* p, int32_t id, int32_t* out_id, int32_t* needs
     *needs_copy = 0;
     return PKV_OK;
   }
-  if (p->free_stack.empty()) return PKV_ERR_OOM;
+  if (num_free(p) == 0) return PKV_ERR_OOM;
   int32_t fresh = pop_block(p);
   --p->ref[id];
   *out_id = fresh;
@@ -142,7 +242,7 @@ pkv_status kv_pool_stats(const pkv_pool* p, pkv_stats* s) {
     refs += r;
   }
   s->num_blocks = p->num_blocks;
-  s->num_free = static_cast<int32_t>(p->free_stack.size());
+  s->num_free = static_cast<int32_t>(num_free(p));
   s->num_used = used;
   s->num_shared = shared;
   s->num_refs = refs;
@@ -153,9 +253,11 @@ pkv_status kv_pool_stats(const pkv_pool* p, pkv_stats* s) {
 pkv_status kv_pool_free_list(const pkv_pool* p, int32_t capacity, int32_t* out_ids,
                              int32_t* out_n) {
   if (!p || !out_n || capacity < 0 || (capacity > 0 && !out_ids)) return PKV_ERR_INVALID;
-  const int32_t n = static_cast<int32_t>(p->free_stack.size());
-  const int32_t k = std::min(n, capacity);
-  for (int32_t i = 0; i < k; ++i) out_ids[i] = p->free_stack[n - 1 - i];
+  const int32_t ns = static_cast<int32_t>(p->free_stack.size());
+  const int32_t n = static_cast<int32_t>(num_free(p));
+  int32_t k = 0;
+  for (int32_t i = 0; i < ns && k < capacity; ++i) out_ids[k++] = p->free_stack[ns - 1 - i];
+  for (auto it = p->lru.begin(); it != p->lru.end() && k < capacity; ++it) out_ids[k++] = *it;
   *out_n = n;
   return PKV_OK;
 }
@@ -202,7 +304,7 @@ pkv_status paged_kv_append_slots(pkv_pool* p, int32_t num_seqs, int32_t max_bloc
       }
     }
   }
-  if (allocs > static_cast<int64_t>(p->free_stack.size())) return PKV_ERR_OOM;
+  if (allocs > static_cast<int64_t>(num_free(p))) return PKV_ERR_OOM;
   if (slots > slot_capacity || allocs > update_capacity || cows > cow_capacity)
     return PKV_ERR_INVALID;
   if ((slots > 0 && !slot_mapping) || (allocs > 0 && !table_updates) || (cows > 0 && !cow_pairs))
@@ -241,6 +343,88 @@ pkv_status paged_kv_append_slots(pkv_pool* p, int32_t num_seqs, int32_t max_bloc
   }
   *num_updates = nu;
   *num_cow = nc;
+  return PKV_OK;
+}
+
+
+pkv_status pkv_prefix_cache_enable(pkv_pool* p) {
+  if (!p) return PKV_ERR_INVALID;
+  if (!p->prefix_on) {
+    p->prefix_on = true;
+    p->cached.assign(p->num_blocks, CachedBlock{});
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_prefix_match(pkv_pool* p, const int32_t* tokens, int32_t num_tokens,
+                            int32_t max_blocks, int32_t* out_ids, int32_t* out_num_blocks) {
+  if (!p || !p->prefix_on || num_tokens < 0 || max_blocks < 0 || !out_num_blocks ||
+      (num_tokens > 0 && !tokens) || (max_blocks > 0 && !out_ids))
+    return PKV_ERR_INVALID;
+  const int32_t full = std::min(num_tokens / PKV_BLOCK_SIZE, max_blocks);
+  int32_t k = 0, parent = -1;
+  for (; k < full; ++k) {
+    const int32_t id = find_cached(p, parent, tokens + int64_t(k) * PKV_BLOCK_SIZE);
+    if (id < 0) break;
+    out_ids[k] = id;
+    parent = id;
+  }
+  for (int32_t i = 0; i < k; ++i) {
+    const int32_t id = out_ids[i];
+    if (p->ref[id] == 0) p->lru.erase(p->cached[id].lru_it);
+    ++p->ref[id];
+  }
+  *out_num_blocks = k;
+  return PKV_OK;
+}
+
+pkv_status pkv_prefix_register(pkv_pool* p, const int32_t* tokens, int32_t num_tokens,
+                               const int32_t* block_ids) {
+  if (!p || !p->prefix_on || num_tokens < 0 || (num_tokens > 0 && (!tokens || !block_ids)))
+    return PKV_ERR_INVALID;
+  const int32_t full = num_tokens / PKV_BLOCK_SIZE;
+  // Walk the chain: the parent of block i is the registered block holding
+  // tokens [16(i-1), 16i) -- the sequence's own block, or an equal one
+  // already indexed.  Validate first (live, distinct, and a registered block
+  // must hold exactly this content), then register.
+  for (int pass = 0; pass < 2; ++pass) {
+    int32_t parent = -1;
+    for (int32_t i = 0; i < full; ++i) {
+      const int32_t id = block_ids[i];
+      const int32_t* t = tokens + int64_t(i) * PKV_BLOCK_SIZE;
+      if (pass == 0) {
+        if (!live(p, id)) return PKV_ERR_INVALID;
+        for (int32_t j = 0; j < i; ++j)
+          if (block_ids[j] == id) return PKV_ERR_INVALID;
+      }
+      const int32_t found = parent < -1 ? -1 : find_cached(p, parent, t);
+      CachedBlock& c = p->cached[id];
+      if (c.on) {
+        if (found != id) return PKV_ERR_INVALID;  // (pass 0 only: pass 1 sees the same state)
+        parent = id;
+      } else if (found >= 0) {
+        parent = found;
+      } else if (pass == 0) {
+        parent = -2;  // registered in pass 1: nothing below it can be indexed yet
+      } else {
+        c.parent = parent;
+        std::copy(t, t + PKV_BLOCK_SIZE, c.tokens.begin());
+        c.hash = block_hash(parent, t);
+        c.on = true;
+        c.children.clear();
+        p->index.emplace(c.hash, id);
+        if (parent >= 0) p->cached[parent].children.push_back(id);
+        parent = id;
+      }
+    }
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_prefix_stats(const pkv_pool* p, int32_t* num_cached, int32_t* num_cached_free) {
+  if (!p || !num_cached || !num_cached_free) return PKV_ERR_INVALID;
+  *num_cached = static_cast<int32_t>(p->index.size());
+  *num_cached_free = static_cast<int32_t>(p->lru.size());
   return PKV_OK;
 }
 

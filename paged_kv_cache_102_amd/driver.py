@@ -188,6 +188,30 @@ class PagedKV:
                                      stream=stream.cuda_stream)
         return out
 
+    # ------------------------------------------------------------------ prefix caching
+    def enable_prefix_cache(self):
+        capi.pkv_prefix_cache_enable(self.pool)
+
+    def match_prefix(self, s: int, tokens) -> int:
+        """Sequence s (empty) takes the cached blocks holding the longest
+        indexed prefix of ``tokens``; returns the number of tokens covered."""
+        assert self.lens[s] == 0
+        ids = capi.pkv_prefix_match(self.pool, tokens, self.max_blocks)
+        k = len(ids)
+        if k:
+            self.tables[s, :k] = ids
+            self.lens[s] = k * BLOCK
+            self.tables_d[s, :k] = torch.from_numpy(ids.astype(np.int32)).to(self.device)
+            self.lens_d[s] = int(self.lens[s])
+        return k * BLOCK
+
+    def register_prefix(self, s: int, tokens):
+        """Indexes the full blocks of sequence s, whose first tokens are ``tokens``."""
+        n = min(len(tokens), int(self.lens[s]))
+        full = n // BLOCK  # only full blocks are indexed
+        capi.pkv_prefix_register(self.pool, np.asarray(tokens[:full * BLOCK], np.int32),
+                                 self.tables[s, :full])
+
     def free_sequence(self, s: int):
         """Returns sequence s's blocks to the pool (one reference each)."""
         n = -(-int(self.lens[s]) // BLOCK)

@@ -407,3 +407,58 @@ def test_fp8_copy_blocks_and_errors():
         capi.paged_attention_decode_fp8(q, kc, vc, tables, lens, out, num_kv_heads=2,
                                         num_blocks=8, max_context_len=1, scale=1.0, k_scale=0.0,
                                         v_scale=1.0)
+
+
+# ---------------------------------------------------------------- prefix caching
+def test_prefix_cache_reuse_end_to_end():
+    """Request A (system prompt + own tokens) is written and indexed, then
+    finishes; request B with the same system prompt reuses A's full blocks
+    (no rewrite), appends only its own tokens, and its decode equals plain
+    attention over the rows it should see (the system rows then its own)."""
+    from oracle import attention as oatt
+    from paged_kv_cache_102_amd.driver import PagedKV
+    from tests.gpu_parity import to_device
+    rng = np.random.default_rng(5)
+    Hq, Hkv, D = 8, 2, 128
+    sys_len, a_own, b_own = 250, 37, 61
+    sys_tok = rng.integers(0, 32000, size=sys_len)
+    a_tok = np.concatenate([sys_tok, rng.integers(0, 32000, size=a_own)]).astype(np.int32)
+    b_tok = np.concatenate([sys_tok, rng.integers(0, 32000, size=b_own)]).astype(np.int32)
+
+    def rows(n):
+        return synth.round_bf16_bits(rng.standard_normal((n, Hkv, D)).astype(np.float32))
+    sys_k, sys_v = rows(sys_len), rows(sys_len)
+    a_k = np.concatenate([sys_k, rows(a_own)])
+    a_v = np.concatenate([sys_v, rows(a_own)])
+    b_own_k, b_own_v = rows(b_own), rows(b_own)
+    kv = PagedKV(num_blocks=64, num_seqs=2, max_blocks_per_seq=24, num_q_heads=Hq,
+                 num_kv_heads=Hkv, head_dim=D, dtype="bf16", fill=float("nan"))
+    kv.enable_prefix_cache()
+    # request A in sequence 0
+    assert kv.match_prefix(0, a_tok) == 0
+    kv.append(to_device(a_k), to_device(a_v), np.array([len(a_tok), 0], np.int32))
+    kv.register_prefix(0, a_tok)
+    a_blocks = kv.tables[0, :len(a_tok) // 16].copy()
+    kv.free_sequence(0)
+    assert capi_stats(kv) == (len(a_tok) // 16, len(a_tok) // 16)
+    # request B in sequence 1 reuses the system prompt's full blocks
+    covered = kv.match_prefix(1, b_tok)
+    assert covered == (sys_len // 16) * 16
+    assert np.array_equal(kv.tables[1, :sys_len // 16], a_blocks[:sys_len // 16])
+    rest = len(b_tok) - covered
+    k_rest = np.concatenate([sys_k[covered:], b_own_k])
+    v_rest = np.concatenate([sys_v[covered:], b_own_v])
+    kv.append(to_device(k_rest), to_device(v_rest), np.array([0, rest], np.int32))
+    q = synth.round_bf16_bits(rng.standard_normal((2, Hq, D)).astype(np.float32))
+    out = kv.decode(to_device(q), 1 / np.sqrt(D)).cpu().numpy().astype(np.float64)
+    kb = synth.bf16_bits_to_f32(np.concatenate([sys_k, b_own_k])).astype(np.float64)
+    vb = synth.bf16_bits_to_f32(np.concatenate([sys_v, b_own_v])).astype(np.float64)
+    qf = synth.bf16_bits_to_f32(q).astype(np.float64)
+    for h in range(Hq):
+        exp = oatt.attend(qf[1, h], kb[:, h // (Hq // Hkv)], vb[:, h // (Hq // Hkv)], 1 / np.sqrt(D))
+        assert np.max(np.abs(out[1, h] - exp)) <= 2e-3
+
+
+def capi_stats(kv):
+    from paged_kv_cache_102_amd import _capi as capi
+    return capi.pkv_prefix_stats(kv.pool)

@@ -183,3 +183,41 @@ def test_mutation_fp8_scale_inverted(monkeypatch):
     monkeypatch.setattr(fp8, "quantize",
                         lambda x, scale: fp8.encode_f32(np.asarray(x, np.float32) * np.float32(scale)))
     assert _fails(pins.test_fp8_worked_values)
+
+
+def test_mutation_prefix_match_without_chain(monkeypatch):
+    """Matching blocks by their own 16 tokens only (not the whole prefix) is caught."""
+    from oracle import prefix
+    from tests import test_prefix_cache as pc
+
+    def bad_match(self, tokens, max_blocks=None):
+        tokens = tuple(int(t) for t in tokens)
+        out = []
+        for i in range(len(tokens) // 16):
+            blk = tokens[16 * i:16 * (i + 1)]
+            hit = next((b for k, b in self._block_of.items() if k[-16:] == blk), None)
+            if hit is None:
+                break
+            out.append(hit)
+        for b in out:
+            if self.refcount[b] == 0:
+                del self._lru[b]
+            self.refcount[b] += 1
+        return out
+    monkeypatch.setattr(prefix.PrefixPoolModel, "match", bad_match)
+    assert _fails(pc.test_block_reused_only_under_its_own_prefix)
+
+
+def test_mutation_prefix_evicts_most_recent(monkeypatch):
+    """Evicting the most recently freed indexed block first is caught."""
+    from oracle import prefix
+    from tests import test_prefix_cache as pc
+
+    def bad_take(self):
+        if self._free:
+            return self._free.pop()
+        b, _ = self._lru.popitem(last=True)
+        self._drop_index(b)
+        return b
+    monkeypatch.setattr(prefix.PrefixPoolModel, "_take", bad_take)
+    assert _fails(pc.test_eviction_order_and_descendants)
