@@ -7,7 +7,10 @@
  *        estado del arte del KV cache en 2026" (blog.lo0.es/posts/
  *        pagedattention-deep-dive): sections "El modelo de bloques",
  *        "La tabla de paginas (block table)" with its figure, "El pool de
- *        bloques", "Copy-on-write para sampling paralelo", "El kernel CUDA".
+ *        bloques", "Copy-on-write para sampling paralelo", "El kernel CUDA",
+ *        "Eviccion y preemption" ("Estrategia 2: swap"), and under "Lo que
+ *        vLLM hace hoy": "Chunked prefill integrado con paged KV", "Prefix
+ *        caching cross-session", "Sliding window attention".
  *   [P3] "Como funciona realmente vLLM (y por que lo necesitas)"
  *        (alexanderzelada.com): "Que es el mecanismo de atencion",
  *        "PagedAttention: la paginacion del sistema operativo aplicada a la
@@ -222,6 +225,56 @@ pkv_status pkv_prefix_register(pkv_pool* pool, const int32_t* tokens, int32_t nu
 /* Number of indexed blocks, and how many of them are free. */
 pkv_status pkv_prefix_stats(const pkv_pool* pool, int32_t* num_cached, int32_t* num_cached_free);
 
+/* ===== Block swap and sliding-window release (host) =========================
+ * [P5 "Eviccion y preemption", "Estrategia 2: swap"]: when the pool runs
+ * dry, a session can be preempted by moving its blocks to CPU memory over
+ * the host link, which frees their device blocks, and brought back when it
+ * is scheduled again.  The swap space is a second pkv_pool (its ids index a
+ * cache of the same block shape in pinned host memory); a swap moves block
+ * references from one pool to the other, and paged_kv_swap_blocks copies the
+ * data. */
+
+/* Moves n block references, ids[0..n) held in `from`, to fresh blocks of
+ * `to`.  Each distinct id gets one new block (first-seen order), whose
+ * refcount in `to` is the number of times the id occurs in ids (so blocks
+ * shared inside a group of sequences stay shared); out_ids[i] is the new
+ * block of ids[i].  Every occurrence then drops one reference in `from`
+ * (a block reaching 0 returns to its free list).  pairs[2k], pairs[2k+1] =
+ * (old id, new id) for each distinct id, *num_pairs of them: the copies to
+ * enqueue with paged_kv_swap_blocks BEFORE any later write can reuse the
+ * freed blocks (same stream).  Swap-out: from = device pool, to = host
+ * pool; swap-in: the reverse.  Host arrays: ids, out_ids [n], pairs [2 n].
+ * All-or-nothing: an id that is not live in `from` or occurs more often
+ * than its refcount, or from == to -> PKV_ERR_INVALID; fewer free blocks in
+ * `to` than distinct ids -> PKV_ERR_OOM; nothing is changed then. */
+pkv_status kv_block_swap(pkv_pool* from, pkv_pool* to, int32_t n, const int32_t* ids,
+                         int32_t* out_ids, int32_t* pairs, int32_t* num_pairs);
+
+/* Sliding-window release [P5 "Sliding window attention": a model that
+ * attends only to the last W tokens needs only the blocks of the active
+ * window; the engine frees the older ones, so the cache stops growing].
+ * For each sequence s, every table entry i < max(0, context_lens[s] -
+ * window) / 16 (blocks whose 16 positions all lie before the window start)
+ * that is >= 0 drops one reference (the block returns to the free list at
+ * 0) and becomes -1; the change goes to table_updates as (s *
+ * max_blocks_per_seq + i, -1), for paged_block_table_update.  Entries
+ * already -1 are skipped, so repeated calls are harmless.  context_lens[s]
+ * is the context length seen by the sequence's earliest query still to
+ * run: its length for a decode step, L - n + 1 before a chunk of n new
+ * tokens (paged_attention_prefill's first row).  The last block is never
+ * released (window >= 1).
+ *   tables: host int32 [num_seqs][max_blocks_per_seq], updated in place
+ *   context_lens: host int32 [num_seqs]
+ *   table_updates: host int32 [update_capacity][2]
+ * All-or-nothing: window < 1, a length outside [0, 16 max_blocks_per_seq],
+ * an entry >= 0 that is not a live block (or more releases of a block than
+ * its references), or too small a capacity -> PKV_ERR_INVALID, nothing
+ * changed. */
+pkv_status pkv_window_release(pkv_pool* pool, int32_t num_seqs, int32_t max_blocks_per_seq,
+                              int32_t* tables, const int32_t* context_lens, int32_t window,
+                              int32_t* table_updates, int32_t update_capacity,
+                              int32_t* num_updates);
+
 /* ===== Slot planning for appended tokens (host) =============================
  * [P5 "La tabla de paginas"]: when a sequence produces a token at position
  * p (p = tokens already cached), it is written into the last block if that
@@ -305,6 +358,27 @@ pkv_status paged_kv_append(const void* k_new, const void* v_new, const int64_t* 
 pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
                                 int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t num_blocks, pkv_dtype dtype, hipStream_t stream);
+
+/* Copies for a block swap [P5 "Estrategia 2: swap": the blocks of a
+ * preempted session go to CPU memory over PCIe and come back when it runs
+ * again].  Block pairs[i][0] of the source cache (src_k, src_v, with
+ * src_num_blocks blocks) is copied to block pairs[i][1] of the destination
+ * cache (dst_k, dst_v, dst_num_blocks blocks): whole blocks, all kv heads
+ * and 16 slots, K and V, bytes unchanged.  Both caches have the layout
+ * above with the same num_kv_heads, head_dim and dtype; either one may be
+ * pinned host memory (hipHostMalloc), which the kernel reads or writes
+ * directly across the host link.  Plan the pairs with kv_block_swap.
+ *   pairs: int32 [num_pairs][2], device or pinned host memory
+ * Pairs with an id out of range are skipped; destination blocks must be
+ * distinct (two pairs with one destination race).  The source and
+ * destination must be different buffers, else PKV_ERR_INVALID (use
+ * paged_kv_copy_blocks inside one cache).  Head_dim not a multiple of 32 ->
+ * PKV_ERR_UNSUPPORTED.  A host destination holds the data once the stream
+ * has passed the call (synchronize or wait on an event first). */
+pkv_status paged_kv_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                                const int32_t* pairs, int32_t num_pairs, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t src_num_blocks, int32_t dst_num_blocks,
+                                pkv_dtype dtype, hipStream_t stream);
 
 /* Bytes of scratch paged_attention_decode needs for these sizes.  For
  * partition_size > 0 it is 0 when every context fits one partition; for
@@ -400,10 +474,13 @@ pkv_status paged_attention_decode_fp8(const void* q, const void* k_cache, const 
  * query_start[s+1]-1 of q; they are the LAST n_s = query_start[s+1] -
  * query_start[s] of its L = context_lens[s] cached tokens (write their K/V
  * with paged_kv_write / paged_kv_append first).  Chunk row i is position
- * p = L - n_s + i and attends causally to positions 0..p:
- *   out[r][h][:] = sum_{t<=p} softmax_t(scale * q[r][h] . K_t) V_t,
- * kv head h / (num_q_heads / num_kv_heads).  n_s = 1 is a decode step; n_s = 0
- * leaves the sequence out.
+ * p = L - n_s + i and attends causally to positions lo..p:
+ *   out[r][h][:] = sum_{lo<=t<=p} softmax_t(scale * q[r][h] . K_t) V_t,
+ * kv head h / (num_q_heads / num_kv_heads), lo = 0, or with a sliding window
+ * of `window` > 0 tokens ["Sliding window attention": only the last W
+ * tokens are attended] lo = max(0, p - window + 1).  Table entries before
+ * the block of the first row's lo are never read.  n_s = 1 is a decode
+ * step; n_s = 0 leaves the sequence out.
  *
  *   q: device [T][num_q_heads][head_dim] in the cache dtype, T = query_start[num_seqs]
  *   query_start: device int32 [num_seqs + 1], non-decreasing, query_start[0] = 0
@@ -419,7 +496,28 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t num_blocks, int32_t max_blocks_per_seq,
                                    int32_t max_context_len, int32_t max_query_len, float scale,
-                                   pkv_dtype kv_dtype, float* out, hipStream_t stream);
+                                   int32_t window, pkv_dtype kv_dtype, float* out,
+                                   hipStream_t stream);
+
+/* Decode with a sliding window, for every cache dtype [P5 "Sliding window
+ * attention": the model attends only to the last W tokens].  The query of
+ * sequence s (position L - 1, L = context_lens[s]) attends to positions
+ * max(0, L - window) .. L - 1 only; window 0 means the whole context, and
+ * the call is then paged_attention_decode (or, for PKV_FP8_E4M3,
+ * paged_attention_decode_fp8 with k_scale, v_scale; the scales are ignored
+ * for other dtypes).  Table entries before the block holding position
+ * L - window are never read (pkv_window_release may have set them to -1).
+ * Arguments, layouts, workspace and errors otherwise as
+ * paged_attention_decode; window < 0 -> PKV_ERR_INVALID. */
+pkv_status paged_attention_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                                         float scale, int32_t window, int32_t partition_size,
+                                         void* workspace, size_t workspace_bytes,
+                                         pkv_dtype kv_dtype, float k_scale, float v_scale,
+                                         float* out, hipStream_t stream);
 
 /* ===== Measurement ==========================================================
  * While profiling is on, every paged_attention_decode call records a pair of

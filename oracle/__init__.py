@@ -17,9 +17,13 @@ Modules and what each follows:
              partition + log-sum-exp form used to pin the reduction
   sizes      byte and block counts printed on the pages
   replay     replays a synthetic workload (prefill recipe, append step)
+  fp8        the OCP E4M3 codec of the FP8 cache (nearest, ties to even)
+  prefix     prefix caching: block index by (parent block, tokens), LRU
+  preempt    block swap to a host pool, sliding-window block release
 
 Parity status: every function is pinned by the CPU tests (page fixtures,
 closed forms, invariants, an independent library routine); none is
 "parity unpinned".
 """
-from . import attention, cache, layout, pool, replay, sizes, slots  # noqa: F401
+from . import (attention, cache, fp8, layout, pool, preempt, prefix, replay,  # noqa: F401
+               sizes, slots)

@@ -36,11 +36,25 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndar
     return w @ v
 
 
+def window_start(p: int, window: int) -> int:
+    """First position seen by the query at position p.
+
+    "PagedAttention por dentro" (blog.lo0.es), "Sliding window attention"
+    (under "Lo que vLLM hace hoy"): models such as Mistral 7B attend only to
+    the most recent W tokens (W = 4096 there).  Reading: the W most recent
+    positions including the query's own, p - W + 1 .. p; window 0 means no
+    window (the whole prefix 0 .. p)."""
+    return max(0, p - window + 1) if window > 0 else 0
+
+
 def decode(q_stored: np.ndarray, cache: CacheModel, tables: np.ndarray, lens: np.ndarray,
-           num_q_heads: int, num_kv_heads: int, scale: float, seqs=None) -> np.ndarray:
+           num_q_heads: int, num_kv_heads: int, scale: float, seqs=None,
+           window: int = 0) -> np.ndarray:
     """out [B][Hq][D] float64 for the sequences in ``seqs`` (default all;
     rows of other sequences stay zero).  Each sequence's K/V are gathered
-    block by block through its table."""
+    block by block through its table; with a sliding window only positions
+    window_start(L - 1, window) .. L - 1 are gathered (table entries before
+    that block are never looked at)."""
     B = q_stored.shape[0]
     D = q_stored.shape[2]
     group = num_q_heads // num_kv_heads
@@ -48,8 +62,9 @@ def decode(q_stored: np.ndarray, cache: CacheModel, tables: np.ndarray, lens: np
     out = np.zeros((B, num_q_heads, D), dtype=np.float64)
     for b in (range(B) if seqs is None else seqs):
         L = int(lens[b])
+        lo = window_start(L - 1, window) if L > 0 else 0
         for kvh in range(num_kv_heads):
-            k, v = cache.gather(tables[b], L, kvh)
+            k, v = cache.gather(tables[b], L, kvh, start=lo)
             for h in range(kvh * group, (kvh + 1) * group):
                 out[b, h] = attend(q[b, h], k, v, scale)
     return out
@@ -86,7 +101,7 @@ def attend_partitioned(q, k, v, scale, partition_tokens: int) -> np.ndarray:
 
 def prefill(q_stored: np.ndarray, cache: CacheModel, tables: np.ndarray, lens: np.ndarray,
             query_start: np.ndarray, num_q_heads: int, num_kv_heads: int,
-            scale: float) -> np.ndarray:
+            scale: float, window: int = 0) -> np.ndarray:
     """Multi-query attention over the paged cache (chunked prefill).
 
     "PagedAttention por dentro" (blog.lo0.es), "Chunked prefill integrado con
@@ -96,8 +111,8 @@ def prefill(q_stored: np.ndarray, cache: CacheModel, tables: np.ndarray, lens: n
     [T][Hq][D]; they are the last n_b of its L_b cached tokens, so chunk row
     i is the token at position p = L_b - n_b + i and attends to positions
     0..p only (the causal rule of a language model, applied inside the
-    chunk).  With n_b = 1 this is ``decode``.  Returns out [T][Hq][D]
-    float64."""
+    chunk).  With a sliding window the row sees window_start(p, window) ..
+    p.  With n_b = 1 this is ``decode``.  Returns out [T][Hq][D] float64."""
     T, _, D = q_stored.shape
     group = num_q_heads // num_kv_heads
     q = widen(q_stored, "bf16" if cache.dtype == "fp8" else cache.dtype)
@@ -105,10 +120,15 @@ def prefill(q_stored: np.ndarray, cache: CacheModel, tables: np.ndarray, lens: n
     for b in range(len(lens)):
         r0, r1 = int(query_start[b]), int(query_start[b + 1])
         n, L = r1 - r0, int(lens[b])
+        if n == 0:
+            continue
+        first = window_start(L - n, window)  # the earliest position any row sees
         for kvh in range(num_kv_heads):
-            k, v = cache.gather(tables[b], L, kvh)
+            k, v = cache.gather(tables[b], L, kvh, start=first)
             for i in range(n):
                 p = L - n + i
+                lo = window_start(p, window) - first
                 for h in range(kvh * group, (kvh + 1) * group):
-                    out[r0 + i, h] = attend(q[r0 + i, h], k[:p + 1], v[:p + 1], scale)
+                    out[r0 + i, h] = attend(q[r0 + i, h], k[lo:p + 1 - first],
+                                            v[lo:p + 1 - first], scale)
     return out

@@ -73,15 +73,23 @@ class CacheModel:
                 self.k[dst] = self.k[src]
                 self.v[dst] = self.v[src]
 
-    def gather(self, table_row, length: int, kv_head: int):
-        """K and V of tokens 0..length-1 of one sequence and kv head, as
-        float64 [length][D], read block by block through the table."""
-        t = np.arange(length)
+    def gather(self, table_row, length: int, kv_head: int, start: int = 0):
+        """K and V of tokens start..length-1 of one sequence and kv head, as
+        float64 [length - start][D], read block by block through the table
+        (entries before token start's block are not read)."""
+        t = np.arange(start, length)
         blk = np.asarray(table_row, dtype=np.int64)[t // BLOCK_SIZE]
         slot = t % BLOCK_SIZE
         k = self.k[blk[:, None], kv_head, self.koff[slot]]
         v = self.v[blk[:, None], kv_head, self.voff[slot]]
         return widen(k, self.dtype, self.k_scale), widen(v, self.dtype, self.v_scale)
+
+    def copy_blocks_to(self, other: "CacheModel", pairs):
+        """Block swap: copy whole blocks of this cache into another cache of the
+        same block shape (every head and slot, K and V), src -> dst."""
+        for src, dst in pairs:
+            other.k[dst] = self.k[src]
+            other.v[dst] = self.v[src]
 
     def stored_bytes(self):
         return self.k.tobytes(), self.v.tobytes()

@@ -49,6 +49,9 @@ _SIGS = {
     "pkv_prefix_match": (C.c_int, [_vp, _i32p, C.c_int32, C.c_int32, _i32p, _i32p]),
     "pkv_prefix_register": (C.c_int, [_vp, _i32p, C.c_int32, _i32p]),
     "pkv_prefix_stats": (C.c_int, [_vp, _i32p, _i32p]),
+    "kv_block_swap": (C.c_int, [_vp, _vp, C.c_int32, _i32p, _i32p, _i32p, _i32p]),
+    "pkv_window_release": (C.c_int, [_vp, C.c_int32, C.c_int32, _i32p, _i32p, C.c_int32, _i32p,
+                                     C.c_int32, _i32p]),
     "paged_kv_append_slots": (C.c_int, [_vp, C.c_int32, C.c_int32, _i32p, _i32p, _i32p, _i64p,
                                         C.c_int64, _i32p, C.c_int32, _i32p, _i32p, C.c_int32,
                                         _i32p]),
@@ -66,7 +69,14 @@ _SIGS = {
                                          C.c_int32, _vp, C.c_size_t, C.c_int, _vp, _vp]),
     "paged_attention_prefill": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
                                           C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
-                                          C.c_int32, C.c_float, C.c_int, _vp, _vp]),
+                                          C.c_int32, C.c_float, C.c_int32, C.c_int, _vp, _vp]),
+    "paged_attention_decode_window": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
+                                                C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                                C.c_int32, C.c_float, C.c_int32, C.c_int32, _vp,
+                                                C.c_size_t, C.c_int, C.c_float, C.c_float, _vp,
+                                                _vp]),
+    "paged_kv_swap_blocks": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32, C.c_int32,
+                                       C.c_int32, C.c_int32, C.c_int, _vp]),
     "paged_attention_decode_fp8": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
                                              C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                              C.c_float, C.c_float, C.c_float, _vp, C.c_size_t, _vp,
@@ -203,6 +213,35 @@ def pkv_prefix_stats(pool: Pool):
     return a.value, b.value
 
 
+def kv_block_swap(from_pool: Pool, to_pool: Pool, ids):
+    """Moves the references ids (held in from_pool) to fresh blocks of
+    to_pool.  Returns (new ids int32 [n], pairs int32 [k][2] of (old, new))."""
+    arr, ptr = _i32(ids)
+    n = arr.size
+    out = np.empty(max(n, 1), dtype=np.int32)
+    pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+    k = C.c_int32()
+    _check(_lib.kv_block_swap(from_pool.handle, to_pool.handle, n, ptr,
+                              out.ctypes.data_as(_i32p), pairs.ctypes.data_as(_i32p),
+                              C.byref(k)), "kv_block_swap")
+    return out[:n].copy(), pairs[:k.value].copy()
+
+
+def pkv_window_release(pool: Pool, block_tables: np.ndarray, context_lens, window: int):
+    """block_tables int32 [B][max_blocks] is updated in place.  Returns the
+    table updates int32 [n][2] of (flat index, -1)."""
+    assert block_tables.dtype == np.int32 and block_tables.flags.c_contiguous
+    B, mb = block_tables.shape
+    lens, lptr = _i32(context_lens)
+    cap = int(np.count_nonzero(block_tables >= 0))
+    upd = np.empty((max(cap, 1), 2), dtype=np.int32)
+    nu = C.c_int32()
+    _check(_lib.pkv_window_release(pool.handle, B, mb, block_tables.ctypes.data_as(_i32p), lptr,
+                                   window, upd.ctypes.data_as(_i32p), cap, C.byref(nu)),
+           "pkv_window_release")
+    return upd[:nu.value].copy()
+
+
 def paged_kv_append_slots(pool: Pool, block_tables: np.ndarray, context_lens: np.ndarray,
                           num_new=None):
     """block_tables int32 [B][max_blocks] and context_lens int32 [B] are
@@ -241,6 +280,13 @@ def _stream(stream):
 def _dev(t, name):
     if not (t.is_cuda and t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous device tensor")
+    return t.data_ptr()
+
+
+def _dev_or_pinned(t, name):
+    """Device tensor, or host tensor in pinned (device-accessible) memory."""
+    if not t.is_contiguous() or not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a contiguous device or pinned host tensor")
     return t.data_ptr()
 
 
@@ -300,6 +346,22 @@ def paged_kv_copy_blocks(k_cache, v_cache, pairs, num_kv_heads: int, head_dim: i
            "paged_kv_copy_blocks")
 
 
+def paged_kv_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, num_kv_heads: int, head_dim: int,
+                         src_num_blocks: int, dst_num_blocks: int, stream=None) -> None:
+    """Copies blocks pairs[i][0] of (src_k, src_v) to pairs[i][1] of (dst_k,
+    dst_v); caches and pairs on the device or in pinned host memory."""
+    n = pairs.shape[0]
+    if n == 0:
+        return
+    if _dtype_code(src_k) != _dtype_code(dst_k):
+        raise ValueError("source and destination caches differ in dtype")
+    _check(_lib.paged_kv_swap_blocks(_dev_or_pinned(src_k, "src_k"), _dev_or_pinned(src_v, "src_v"),
+                                     _dev_or_pinned(dst_k, "dst_k"), _dev_or_pinned(dst_v, "dst_v"),
+                                     _dev_or_pinned(pairs, "pairs"), n, num_kv_heads, head_dim,
+                                     src_num_blocks, dst_num_blocks, _dtype_code(src_k),
+                                     _stream(stream)), "paged_kv_swap_blocks")
+
+
 def paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                    max_context_len, partition_size=0) -> int:
     return int(_lib.paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
@@ -324,9 +386,10 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, out,
 
 def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, out, *,
                             num_kv_heads: int, num_blocks: int, max_context_len: int,
-                            max_query_len: int, scale: float, stream=None) -> None:
+                            max_query_len: int, scale: float, window: int = 0,
+                            stream=None) -> None:
     """q [T][Hq][D] (chunk rows of all sequences, in order), query_start
-    int32 [B + 1]; out [T][Hq][D] fp32."""
+    int32 [B + 1]; out [T][Hq][D] fp32; window 0 = no sliding window."""
     T, Hq, D = q.shape
     B = context_lens.shape[0]
     mb = block_tables.shape[1]
@@ -335,7 +398,8 @@ def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, que
                                         _dev(context_lens, "context_lens"),
                                         _dev(query_start, "query_start"), B, Hq, num_kv_heads, D,
                                         num_blocks, mb, max_context_len, max_query_len, scale,
-                                        _dtype_code(k_cache), _dev(out, "out"), _stream(stream)),
+                                        window, _dtype_code(k_cache), _dev(out, "out"),
+                                        _stream(stream)),
            "paged_attention_prefill")
 
 
@@ -367,6 +431,26 @@ def paged_attention_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, 
                                            D, num_blocks, mb, max_context_len, scale, k_scale,
                                            v_scale, ws_ptr, ws_bytes, _dev(out, "out"),
                                            _stream(stream)), "paged_attention_decode_fp8")
+
+
+def paged_attention_decode_window(q, k_cache, v_cache, block_tables, context_lens, out, *,
+                                  num_kv_heads: int, num_blocks: int, max_context_len: int,
+                                  scale: float, window: int, partition_size: int = 0,
+                                  k_scale: float = 1.0, v_scale: float = 1.0, workspace=None,
+                                  stream=None) -> None:
+    B, Hq, D = q.shape
+    mb = block_tables.shape[1]
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.paged_attention_decode_window(_dev(q, "q"), _dev(k_cache, "k_cache"),
+                                              _dev(v_cache, "v_cache"),
+                                              _dev(block_tables, "block_tables"),
+                                              _dev(context_lens, "context_lens"), B, Hq,
+                                              num_kv_heads, D, num_blocks, mb, max_context_len,
+                                              scale, window, partition_size, ws_ptr, ws_bytes,
+                                              _dtype_code(k_cache), k_scale, v_scale,
+                                              _dev(out, "out"), _stream(stream)),
+           "paged_attention_decode_window")
 
 
 def pkv_profile_begin() -> None:

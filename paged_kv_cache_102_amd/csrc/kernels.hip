@@ -185,6 +185,34 @@ __global__ void copy_blocks_kernel(uint4* __restrict__ kc, uint4* __restrict__ v
   for (int64_t i = threadIdx.x; i < run16; i += blockDim.x) d[i] = s[i];
 }
 
+// ------------------------------------------------------------------ next: block swap
+// Whole-block copies between two caches with the same block shape (the
+// device cache and a swap space in pinned host memory, in either
+// direction): pair i moves block pairs[i][0] of the source to block
+// pairs[i][1] of the destination.  blockIdx.x = pair, blockIdx.y = 0 (K) /
+// 1 (V).  Each lane keeps 4 loads in flight before their stores, so that
+// the reads over the host link (long latency) overlap.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    const uint4* __restrict__ sk, const uint4* __restrict__ sv, uint4* __restrict__ dk,
+    uint4* __restrict__ dv, const int32_t* __restrict__ pairs, int64_t run16, int src_blocks,
+    int dst_blocks) {
+  const int32_t src = pairs[2 * blockIdx.x];
+  const int32_t dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const uint4* s = (blockIdx.y ? sv : sk) + int64_t(src) * run16;
+  uint4* d = (blockIdx.y ? dv : dk) + int64_t(dst) * run16;
+  constexpr int U = 4;
+  int64_t i = threadIdx.x;
+  for (; i + (U - 1) * 256 < run16; i += U * 256) {
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = s[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[i + u * 256] = w[u];
+  }
+  for (; i < run16; i += 256) d[i] = s[i];
+}
+
 // ------------------------------------------------------------------ A5: decode, bf16
 struct DecodeArgs {
   const void* q;
@@ -212,12 +240,22 @@ struct DecodeArgs {
   float* cu_over;
   int static_permille, chunk_min;
   float out_scale;  // FP8 cache: the V tensor scale (1 otherwise)
+  int window;       // sliding window in tokens (0: the whole context)
 };
 
 // Length check shared by the kernels: a bad length poisons the sequence.
 __device__ inline bool len_ok(int L, const DecodeArgs& a) {
   return L >= 0 && L <= a.max_ctx && int64_t(L) <= int64_t(a.max_blocks) * kBlock;
 }
+
+// Sliding window: the query at position L-1 sees only the last `window`
+// positions, [win_lo, L).  Blocks wholly before win_lo are never read (their
+// table entries may already be released); the walk starts at the block
+// holding win_lo and masks the positions before it.
+__device__ inline int win_lo(const DecodeArgs& a, int L) {
+  return (a.window > 0 && L > a.window) ? L - a.window : 0;
+}
+__device__ inline int first_block_of(const DecodeArgs& a, int L) { return win_lo(a, L) / kBlock; }
 
 // Buffer resource over one cache tile: loads at byte offsets below `bytes`
 // read memory; with bytes == 0 every load returns zeros without a memory
@@ -261,9 +299,12 @@ void decode_bf16_kernel(DecodeArgs a) {
     }
     return;
   }
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  // partitions tile [base, L), base = the window start rounded down to a block
+  const int wlo = win_lo(a, L);
+  const int base = wlo / kBlock * kBlock;
+  const int nparts = (L - base + a.part_tokens - 1) / a.part_tokens;
   if (part >= nparts) return;
-  const int t_begin = part * a.part_tokens;
+  const int t_begin = base + part * a.part_tokens;
   const int t_end = min(L, t_begin + a.part_tokens);
   const int nblk = (t_end - t_begin + kBlock - 1) / kBlock;
   const int32_t* row = a.tables + int64_t(b) * a.max_blocks + t_begin / kBlock;
@@ -324,7 +365,8 @@ void decode_bf16_kernel(DecodeArgs a) {
     const int tb = t_begin + i * kBlock + grp * 4;
     float sv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = (tb + r < t_end) ? s[r] * a.scale_log2e : -INFINITY;
+    for (int r = 0; r < 4; ++r)
+      sv[r] = (tb + r < t_end && tb + r >= wlo) ? s[r] * a.scale_log2e : -INFINITY;
     float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mloc = group_max(mloc);
     const float mnew = fmaxf(m, mloc);
@@ -352,10 +394,11 @@ void decode_bf16_kernel(DecodeArgs a) {
     }
     const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
     const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
-    if (t_begin + i * kBlock + kBlock > t_end) {
-      // partial block: zero V of slots past the context (they may hold NaN)
-      const uint32_t m01 = (tb + 0 < t_end ? 0x0000FFFFu : 0u) | (tb + 1 < t_end ? 0xFFFF0000u : 0u);
-      const uint32_t m23 = (tb + 2 < t_end ? 0x0000FFFFu : 0u) | (tb + 3 < t_end ? 0xFFFF0000u : 0u);
+    if (t_begin + i * kBlock + kBlock > t_end || t_begin + i * kBlock < wlo) {
+      // partial block: zero V of slots outside [wlo, t_end) (they may hold NaN)
+      auto in = [&](int t) { return t < t_end && t >= wlo; };
+      const uint32_t m01 = (in(tb + 0) ? 0x0000FFFFu : 0u) | (in(tb + 1) ? 0xFFFF0000u : 0u);
+      const uint32_t m23 = (in(tb + 2) ? 0x0000FFFFu : 0u) | (in(tb + 3) ? 0xFFFF0000u : 0u);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         vr[j].x &= m01;
@@ -444,8 +487,9 @@ __device__ inline int load_uniform(const int* p, int64_t i) {
   return *((const_int_ptr)p + i);
 }
 
+// Tiles of a sequence in the work list: its blocks from the window's first.
 __device__ inline int nblocks_of(const DecodeArgs& a, int L) {
-  return len_ok(L, a) ? (L + kBlock - 1) / kBlock : 0;
+  return len_ok(L, a) ? (L + kBlock - 1) / kBlock - first_block_of(a, L) : 0;
 }
 
 // Sum over the wave, returned as a wave-uniform value (scalar register), so
@@ -589,7 +633,8 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
   int64_t l_idx = g0;
   auto issue = [&](int st) {
     const bool live = l_idx < g1;
-    int phys = load_uniform(a.tables, int64_t(l_b) * a.max_blocks + (live ? l_blk : 0));
+    int phys = load_uniform(a.tables, int64_t(l_b) * a.max_blocks +
+                                          (live ? first_block_of(a, l_L) + l_blk : 0));
     bool bad = false;
     int bytes = live ? TILE_BYTES : 0;
     if (live && (phys < 0 || phys >= a.num_blocks)) {
@@ -699,10 +744,14 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
     for (int j = 0; j < NJ; ++j)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[st][j]), qf[j], s,
                                                    0, 0, 0);
-    const int tb = c_blk * kBlock + grp * 4;
+    // block c_blk of the list is block c_first + c_blk of the sequence
+    const int wlo = win_lo(a, c_L);
+    const int c_first = wlo / kBlock;
+    const int tb = (c_first + c_blk) * kBlock + grp * 4;
     float sv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = (tb + r < c_L) ? s[r] * a.scale_log2e : -INFINITY;
+    for (int r = 0; r < 4; ++r)
+      sv[r] = (tb + r < c_L && tb + r >= wlo) ? s[r] * a.scale_log2e : -INFINITY;
     float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mloc = group_max(mloc);
     const float mnew = fmaxf(m, mloc);
@@ -728,9 +777,11 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
     }
     const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
     const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
-    if (c_blk * kBlock + kBlock > c_L) {
-      const uint32_t m01 = (tb + 0 < c_L ? 0x0000FFFFu : 0u) | (tb + 1 < c_L ? 0xFFFF0000u : 0u);
-      const uint32_t m23 = (tb + 2 < c_L ? 0x0000FFFFu : 0u) | (tb + 3 < c_L ? 0xFFFF0000u : 0u);
+    if ((c_first + c_blk) * kBlock + kBlock > c_L || (c_first + c_blk) * kBlock < wlo) {
+      // zero V of slots outside [wlo, c_L) (they may hold NaN)
+      auto in = [&](int t) { return t < c_L && t >= wlo; };
+      const uint32_t m01 = (in(tb + 0) ? 0x0000FFFFu : 0u) | (in(tb + 1) ? 0xFFFF0000u : 0u);
+      const uint32_t m23 = (in(tb + 2) ? 0x0000FFFFu : 0u) | (in(tb + 3) ? 0xFFFF0000u : 0u);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         vr[st][j].x &= m01;
@@ -1142,7 +1193,9 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     rec_idx[st] = l_idx;
     rec_first[st] = l_idx == l_us;
     rec_last[st] = l_idx == l_ue - 1;
-    int phys = live ? load_uniform(a.tables, int64_t(l_b) * a.max_blocks + l_blk) : 0;
+    int phys = live ? load_uniform(a.tables, int64_t(l_b) * a.max_blocks +
+                                                 first_block_of(a, l_L) + l_blk)
+                    : 0;
     bool bad = false;
     int bytes = live ? TILE_BYTES : 0;
     if (live && (phys < 0 || phys >= a.num_blocks)) {
@@ -1286,10 +1339,14 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     for (int j = 0; j < NJ; ++j)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kx[j]), qf[j], s,
                                                    0, 0, 0);
-    const int tb = c_blk * kBlock + grp * 4;
+    // block c_blk of the list is block c_first + c_blk of the sequence
+    const int wlo = win_lo(a, c_L);
+    const int c_first = wlo / kBlock;
+    const int tb = (c_first + c_blk) * kBlock + grp * 4;
     float sv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = (tb + r < c_L) ? s[r] * a.scale_log2e : -INFINITY;
+    for (int r = 0; r < 4; ++r)
+      sv[r] = (tb + r < c_L && tb + r >= wlo) ? s[r] * a.scale_log2e : -INFINITY;
     float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mloc = group_max(mloc);
     const float mnew = fmaxf(m, mloc);
@@ -1315,9 +1372,11 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     }
     const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
     const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
-    if (c_blk * kBlock + kBlock > c_L) {
-      const uint32_t m01 = (tb + 0 < c_L ? 0x0000FFFFu : 0u) | (tb + 1 < c_L ? 0xFFFF0000u : 0u);
-      const uint32_t m23 = (tb + 2 < c_L ? 0x0000FFFFu : 0u) | (tb + 3 < c_L ? 0xFFFF0000u : 0u);
+    if ((c_first + c_blk) * kBlock + kBlock > c_L || (c_first + c_blk) * kBlock < wlo) {
+      // zero V of slots outside [wlo, c_L) (they may hold NaN)
+      auto in = [&](int t) { return t < c_L && t >= wlo; };
+      const uint32_t m01 = (in(tb + 0) ? 0x0000FFFFu : 0u) | (in(tb + 1) ? 0xFFFF0000u : 0u);
+      const uint32_t m23 = (in(tb + 2) ? 0x0000FFFFu : 0u) | (in(tb + 3) ? 0xFFFF0000u : 0u);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         vx[j].x &= m01;
@@ -1517,6 +1576,7 @@ struct PrefillArgs {
   int num_seqs, num_q_heads, num_kv_heads, group, qb;
   int num_blocks, max_blocks, max_ctx;
   float scale_log2e;
+  int window;  // sliding window in tokens: position p sees p-window+1 .. p (0: 0 .. p)
 };
 
 template <int D, int ST, int AUX>
@@ -1558,8 +1618,13 @@ void prefill_bf16_kernel(PrefillArgs a) {
   }
   const int p_last = L - n + q0 + nq - 1;          // last position of the tile
   const int p_col = col_ok ? L - n + q0 + qi : p_last;
-  const int nblk = p_last / kBlock + 1;
-  const int32_t* row = a.tables + int64_t(b) * a.max_blocks;
+  // sliding window: column p_col sees [c_lo, p_col]; the walk starts at the
+  // block holding the earliest c_lo of the tile (its first column's)
+  const int c_lo = a.window > 0 ? max(0, p_col - a.window + 1) : 0;
+  const int t_lo = a.window > 0 ? max(0, L - n + q0 - a.window + 1) : 0;
+  const int i0 = t_lo / kBlock;
+  const int nblk = p_last / kBlock + 1 - i0;
+  const int32_t* row = a.tables + int64_t(b) * a.max_blocks + i0;
 
   // Q^T as B operand: lane holds q[row of column hcol][32j + 8 grp .. +8]
   bf16x8 qf[NJ];
@@ -1614,10 +1679,11 @@ void prefill_bf16_kernel(PrefillArgs a) {
     for (int j = 0; j < NJ; ++j)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[st][j]), qf[j], s,
                                                    0, 0, 0);
-    const int tb = i * kBlock + grp * 4;
+    const int tb = (i0 + i) * kBlock + grp * 4;
     float sv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = (tb + r <= p_col) ? s[r] * a.scale_log2e : -INFINITY;
+    for (int r = 0; r < 4; ++r)
+      sv[r] = (tb + r <= p_col && tb + r >= c_lo) ? s[r] * a.scale_log2e : -INFINITY;
     float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mloc = group_max(mloc);
     const float mnew = fmaxf(m, mloc);
@@ -1645,10 +1711,12 @@ void prefill_bf16_kernel(PrefillArgs a) {
     }
     const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
     const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
-    if (i * kBlock + kBlock > L) {
-      // slots past the context may hold anything: zero their V
-      const uint32_t m01 = (tb + 0 < L ? 0x0000FFFFu : 0u) | (tb + 1 < L ? 0xFFFF0000u : 0u);
-      const uint32_t m23 = (tb + 2 < L ? 0x0000FFFFu : 0u) | (tb + 3 < L ? 0xFFFF0000u : 0u);
+    if ((i0 + i) * kBlock + kBlock > L || (i0 + i) * kBlock < t_lo) {
+      // slots past the context or before the tile's window may hold
+      // anything: zero their V
+      auto in = [&](int t) { return t < L && t >= t_lo; };
+      const uint32_t m01 = (in(tb + 0) ? 0x0000FFFFu : 0u) | (in(tb + 1) ? 0xFFFF0000u : 0u);
+      const uint32_t m23 = (in(tb + 2) ? 0x0000FFFFu : 0u) | (in(tb + 3) ? 0xFFFF0000u : 0u);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         vr[st][j].x &= m01;
@@ -1716,9 +1784,12 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     }
     return;
   }
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  // partitions tile [base, L), base = the window start rounded down to a block
+  const int wlo = win_lo(a, L);
+  const int base = wlo / kBlock * kBlock;
+  const int nparts = (L - base + a.part_tokens - 1) / a.part_tokens;
   if (part >= nparts) return;
-  const int t_begin = part * a.part_tokens;
+  const int t_begin = base + part * a.part_tokens;
   const int t_end = min(L, t_begin + a.part_tokens);
   const int32_t* row = a.tables + int64_t(b) * a.max_blocks;
   const float* q = static_cast<const float*>(a.q) + head * D;
@@ -1733,7 +1804,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
   }
   float m = -INFINITY, lsum = 0.f;
   bool bad = false;
-  for (int t = t_begin; t < t_end; ++t) {
+  for (int t = max(t_begin, wlo); t < t_end; ++t) {
     int phys = __builtin_amdgcn_readfirstlane(row[t / kBlock]);
     if (phys < 0 || phys >= a.num_blocks) {
       bad = true;
@@ -1783,7 +1854,8 @@ __global__ __launch_bounds__(64) void lse_reduce_kernel(DecodeArgs a) {
   const int b = static_cast<int>(blockIdx.x / a.num_kv_heads);
   const int L = a.lens[b];
   if (!len_ok(L, a) || L == 0) return;
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  const int base = first_block_of(a, L) * kBlock;
+  const int nparts = (L - base + a.part_tokens - 1) / a.part_tokens;
   if (nparts <= 1) return;
   const int g = a.group;
   const bool split = (64 % g) == 0;
@@ -2141,6 +2213,26 @@ pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pai
   return launch_status();
 }
 
+pkv_status paged_kv_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                                const int32_t* pairs, int32_t num_pairs, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t src_num_blocks, int32_t dst_num_blocks,
+                                pkv_dtype dtype, hipStream_t stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || src_num_blocks <= 0 ||
+      dst_num_blocks <= 0)
+    return PKV_ERR_INVALID;
+  const int esize = dtype == PKV_FP8_E4M3 ? 1 : elem_size(dtype);
+  if (head_dim % 32 != 0 || esize == 0) return PKV_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PKV_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !pairs) return PKV_ERR_INVALID;
+  if (src_k == dst_k || src_v == dst_v) return PKV_ERR_INVALID;  // in-cache copies: copy_blocks
+  const int64_t run_bytes = int64_t(num_kv_heads) * kBlock * head_dim * esize;
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, stream,
+                     static_cast<const uint4*>(src_k), static_cast<const uint4*>(src_v),
+                     static_cast<uint4*>(dst_k), static_cast<uint4*>(dst_v), pairs, run_bytes / 16,
+                     src_num_blocks, dst_num_blocks);
+  return launch_status();
+}
+
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim,
                                       int32_t max_context_len, int32_t partition_size) {
@@ -2165,9 +2257,10 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t num_blocks, int32_t max_blocks_per_seq,
                                    int32_t max_context_len, int32_t max_query_len, float scale,
-                                   pkv_dtype kv_dtype, float* out, hipStream_t stream) {
+                                   int32_t window, pkv_dtype kv_dtype, float* out,
+                                   hipStream_t stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
-      max_blocks_per_seq <= 0 || max_context_len < 0 || max_query_len < 0)
+      max_blocks_per_seq <= 0 || max_context_len < 0 || max_query_len < 0 || window < 0)
     return PKV_ERR_INVALID;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
@@ -2194,6 +2287,7 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
   a.max_blocks = max_blocks_per_seq;
   a.max_ctx = max_context_len;
   a.scale_log2e = scale * 1.4426950408889634f;
+  a.window = window;
   const int64_t tiles = (int64_t(max_query_len) + a.qb - 1) / a.qb;
   const int64_t grid = tiles * num_seqs * num_kv_heads;
   if (grid > 0x7FFFFFFF) return PKV_ERR_UNSUPPORTED;
@@ -2210,12 +2304,13 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
-                       float scale, int32_t partition_size, void* workspace,
+                       float scale, int32_t window, int32_t partition_size, void* workspace,
                        size_t workspace_bytes, pkv_dtype kv_dtype, float k_scale, float v_scale,
                        float* out, hipStream_t stream) {
   const bool fp8 = kv_dtype == PKV_FP8_E4M3;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || partition_size < 0)
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || partition_size < 0 ||
+      window < 0)
     return PKV_ERR_INVALID;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
   if (partition_size % 32 != 0) return PKV_ERR_INVALID;
@@ -2268,6 +2363,7 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.max_parts = static_cast<int>(max_parts);
   a.scale_log2e = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
   a.out_scale = fp8 ? v_scale : 1.0f;
+  a.window = window;
   a.grid_waves = waves;
   a.bw_o = balanced ? ws : nullptr;
   a.bw_m = balanced ? ws + size_t(waves) * 2 * group * head_dim : nullptr;
@@ -2343,8 +2439,24 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
   if (kv_dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;  // needs the scales
   return decode_impl(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len,
-                     scale, partition_size, workspace, workspace_bytes, kv_dtype, 1.0f, 1.0f, out,
-                     stream);
+                     scale, 0, partition_size, workspace, workspace_bytes, kv_dtype, 1.0f, 1.0f,
+                     out, stream);
+}
+
+pkv_status paged_attention_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                                         float scale, int32_t window, int32_t partition_size,
+                                         void* workspace, size_t workspace_bytes,
+                                         pkv_dtype kv_dtype, float k_scale, float v_scale,
+                                         float* out, hipStream_t stream) {
+  if (kv_dtype != PKV_FP8_E4M3) k_scale = v_scale = 1.0f;
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len,
+                     scale, window, partition_size, workspace, workspace_bytes, kv_dtype, k_scale,
+                     v_scale, out, stream);
 }
 
 pkv_status paged_attention_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -2356,8 +2468,8 @@ pkv_status paged_attention_decode_fp8(const void* q, const void* k_cache, const 
                                       size_t workspace_bytes, float* out, hipStream_t stream) {
   return decode_impl(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len,
-                     scale, 0, workspace, workspace_bytes, PKV_FP8_E4M3, k_scale, v_scale, out,
-                     stream);
+                     scale, 0, 0, workspace, workspace_bytes, PKV_FP8_E4M3, k_scale, v_scale,
+                     out, stream);
 }
 
 pkv_status paged_kv_write_fp8(const void* k_new, const void* v_new, pkv_dtype src_dtype,

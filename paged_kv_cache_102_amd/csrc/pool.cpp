@@ -421,6 +421,82 @@ pkv_status pkv_prefix_register(pkv_pool* p, const int32_t* tokens, int32_t num_t
   return PKV_OK;
 }
 
+pkv_status kv_block_swap(pkv_pool* from, pkv_pool* to, int32_t n, const int32_t* ids,
+                         int32_t* out_ids, int32_t* pairs, int32_t* num_pairs) {
+  if (!from || !to || from == to || n < 0 || !num_pairs) return PKV_ERR_INVALID;
+  if (n > 0 && (!ids || !out_ids || !pairs)) return PKV_ERR_INVALID;
+  // references per distinct block, in first-seen order; validated first
+  std::unordered_map<int32_t, int32_t> occ;
+  std::vector<int32_t> order;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t id = ids[i];
+    if (id < 0 || id >= from->num_blocks) return PKV_ERR_INVALID;
+    int32_t& c = occ[id];
+    if (c == 0) order.push_back(id);
+    if (++c > from->ref[id]) return PKV_ERR_INVALID;
+  }
+  if (order.size() > num_free(to)) return PKV_ERR_OOM;
+  std::unordered_map<int32_t, int32_t> dest;
+  for (size_t k = 0; k < order.size(); ++k) {
+    const int32_t id = order[k];
+    const int32_t nid = pop_block(to);
+    to->ref[nid] = occ[id];
+    dest[id] = nid;
+    pairs[2 * k] = id;
+    pairs[2 * k + 1] = nid;
+  }
+  for (int32_t i = 0; i < n; ++i) out_ids[i] = dest[ids[i]];
+  for (int32_t i = 0; i < n; ++i)
+    if (--from->ref[ids[i]] == 0) release(from, ids[i]);
+  *num_pairs = static_cast<int32_t>(order.size());
+  return PKV_OK;
+}
+
+pkv_status pkv_window_release(pkv_pool* p, int32_t num_seqs, int32_t max_blocks_per_seq,
+                              int32_t* tables, const int32_t* context_lens, int32_t window,
+                              int32_t* table_updates, int32_t update_capacity,
+                              int32_t* num_updates) {
+  if (!p || num_seqs < 0 || max_blocks_per_seq < 1 || window < 1 || !num_updates ||
+      update_capacity < 0)
+    return PKV_ERR_INVALID;
+  if (num_seqs > 0 && (!tables || !context_lens)) return PKV_ERR_INVALID;
+  if (static_cast<int64_t>(num_seqs) * max_blocks_per_seq >= (int64_t(1) << 31))
+    return PKV_ERR_INVALID;
+  const int64_t cap_tokens = int64_t(max_blocks_per_seq) * PKV_BLOCK_SIZE;
+  // blocks wholly before the window start: i < max(0, L - window) / 16
+  auto first_kept = [&](int32_t s) {
+    return std::max<int32_t>(0, context_lens[s] - window) / PKV_BLOCK_SIZE;
+  };
+  std::unordered_map<int32_t, int32_t> drops;
+  int64_t count = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (context_lens[s] < 0 || context_lens[s] > cap_tokens) return PKV_ERR_INVALID;
+    const int32_t* row = tables + int64_t(s) * max_blocks_per_seq;
+    for (int32_t i = 0; i < first_kept(s); ++i) {
+      const int32_t id = row[i];
+      if (id < 0) continue;  // released before
+      if (id >= p->num_blocks || ++drops[id] > p->ref[id]) return PKV_ERR_INVALID;
+      ++count;
+    }
+  }
+  if (count > update_capacity || (count > 0 && !table_updates)) return PKV_ERR_INVALID;
+  int32_t nu = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    int32_t* row = tables + int64_t(s) * max_blocks_per_seq;
+    for (int32_t i = 0; i < first_kept(s); ++i) {
+      const int32_t id = row[i];
+      if (id < 0) continue;
+      if (--p->ref[id] == 0) release(p, id);
+      row[i] = -1;
+      table_updates[2 * nu] = s * max_blocks_per_seq + i;
+      table_updates[2 * nu + 1] = -1;
+      ++nu;
+    }
+  }
+  *num_updates = nu;
+  return PKV_OK;
+}
+
 pkv_status pkv_prefix_stats(const pkv_pool* p, int32_t* num_cached, int32_t* num_cached_free) {
   if (!p || !num_cached || !num_cached_free) return PKV_ERR_INVALID;
   *num_cached = static_cast<int32_t>(p->index.size());

@@ -12,6 +12,11 @@ sequences the C-ABI calls of one decode step:
   5. write the new K/V (paged_kv_write);
   6. attend (paged_attention_decode).
 
+With a sliding window, blocks wholly before every upcoming query's window
+are released before step 1 (pkv_window_release), so the same step can reuse
+them.  A swap space in pinned host memory takes whole sequences out of the
+device cache and brings them back (kv_block_swap + paged_kv_swap_blocks).
+
 Every step runs in libpagedkv; this module only moves arguments.
 """
 from __future__ import annotations
@@ -73,9 +78,11 @@ class PagedKV:
     def __init__(self, *, num_blocks: int, num_seqs: int, max_blocks_per_seq: int,
                  num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
                  device="cuda", init_order=None, fill=None, partition_size: int = 0,
-                 k_scale: float = 1.0, v_scale: float = 1.0):
+                 k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0):
         """dtype "f32", "bf16" or "fp8" (E4M3 codes with tensor scales k_scale,
-        v_scale; appended rows are bf16 or fp32 and quantised on write)."""
+        v_scale; appended rows are bf16 or fp32 and quantised on write).
+        window > 0: sliding-window attention over the last ``window`` tokens,
+        with the blocks before it released as the sequences grow."""
         self.num_blocks, self.num_seqs, self.max_blocks = num_blocks, num_seqs, max_blocks_per_seq
         self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
         self.dtype = dtype
@@ -104,6 +111,9 @@ class PagedKV:
                                                  max_blocks_per_seq * BLOCK, partition_size)
         self.workspace = torch.empty(max(ws // 4, 1), dtype=torch.float32, device=self.device)
         self._staging = None
+        self.window = window
+        self.host_pool = None
+        self.swapped = {}   # sequence -> (host table row, length)
 
     # ------------------------------------------------------------------ host helpers
     def _upload(self, arrays, stream):
@@ -128,7 +138,16 @@ class PagedKV:
         """Appends tokens (k_new, v_new device [T][Hkv][D], rows in order of
         sequence) and returns (slots, table updates, cow pairs) as numpy."""
         stream = stream or torch.cuda.current_stream(self.device)
+        rel = None
+        if self.window > 0:
+            # the earliest query still to run sees context length lens + 1
+            # (a sequence with nothing to append: its current length)
+            nn = np.ones_like(self.lens) if num_new is None else np.asarray(num_new, np.int32)
+            ctx = self.lens + (nn > 0).astype(np.int32)
+            rel = capi.pkv_window_release(self.pool, self.tables, ctx, self.window)
         slots, upd, cows = capi.paged_kv_append_slots(self.pool, self.tables, self.lens, num_new)
+        if rel is not None and len(rel):
+            upd = np.concatenate([rel, upd]) if len(upd) else rel
         d_slots, d_upd, d_cows, d_lens = self._upload([slots, upd, cows, self.lens], stream)
         s = stream.cuda_stream
         # the uploaded lengths become the device lengths (no extra copy)
@@ -158,6 +177,14 @@ class PagedKV:
                                                    max_ctx, ps)
         if need > ws.numel() * 4:
             ws = self.workspace = torch.empty(need // 4, dtype=torch.float32, device=self.device)
+        if self.window > 0:
+            capi.paged_attention_decode_window(
+                q, self.k_cache, self.v_cache, self.tables_d, self.lens_d, out,
+                num_kv_heads=self.num_kv_heads, num_blocks=self.num_blocks,
+                max_context_len=max_ctx, scale=scale, window=self.window,
+                partition_size=0 if self.dtype == "fp8" else ps, k_scale=self.k_scale,
+                v_scale=self.v_scale, workspace=ws, stream=stream.cuda_stream)
+            return out
         if self.dtype == "fp8":
             capi.paged_attention_decode_fp8(q, self.k_cache, self.v_cache, self.tables_d,
                                             self.lens_d, out, num_kv_heads=self.num_kv_heads,
@@ -185,7 +212,7 @@ class PagedKV:
         capi.paged_attention_prefill(q, self.k_cache, self.v_cache, self.tables_d, self.lens_d, qs_d,
                                      out, num_kv_heads=self.num_kv_heads, num_blocks=self.num_blocks,
                                      max_context_len=max_ctx, max_query_len=max_q, scale=scale,
-                                     stream=stream.cuda_stream)
+                                     window=self.window, stream=stream.cuda_stream)
         return out
 
     # ------------------------------------------------------------------ prefix caching
@@ -212,10 +239,71 @@ class PagedKV:
         capi.pkv_prefix_register(self.pool, np.asarray(tokens[:full * BLOCK], np.int32),
                                  self.tables[s, :full])
 
+    # ------------------------------------------------------------------ swap
+    def enable_swap(self, num_host_blocks: int):
+        """A swap space of ``num_host_blocks`` blocks in pinned host memory."""
+        self.host_pool = capi.pkv_pool_create(num_host_blocks, BLOCK)
+        self.num_host_blocks = num_host_blocks
+        n = num_host_blocks * self.num_kv_heads * BLOCK * self.head_dim
+        self.k_host = torch.empty(n, dtype=self.k_cache.dtype, pin_memory=True)
+        self.v_host = torch.empty(n, dtype=self.v_cache.dtype, pin_memory=True)
+
+    def swap_out(self, seqs, stream=None):
+        """Moves the blocks of sequences ``seqs`` to the swap space and frees
+        their device blocks; the sequences leave the batch (length 0) until
+        swap_in.  Blocks shared among ``seqs`` are moved once."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        seqs = [int(s) for s in seqs]
+        rows = [self.tables[s, :-(-int(self.lens[s]) // BLOCK)] for s in seqs]
+        ids = np.concatenate([r[r >= 0] for r in rows]) if rows else np.zeros(0, np.int32)
+        new, pairs = capi.kv_block_swap(self.pool, self.host_pool, ids)
+        k = 0
+        for s, r in zip(seqs, rows):
+            h = np.full(self.max_blocks, -1, np.int32)
+            live = np.nonzero(r >= 0)[0]
+            h[live] = new[k:k + len(live)]
+            k += len(live)
+            self.swapped[s] = (h, int(self.lens[s]))
+            self.tables[s, :] = -1
+            self.lens[s] = 0
+        self._swap_copy(pairs, self.k_cache, self.v_cache, self.num_blocks, self.k_host,
+                        self.v_host, self.num_host_blocks, stream)
+        self.tables_d.copy_(torch.from_numpy(self.tables), non_blocking=False)
+        self.lens_d.copy_(torch.from_numpy(self.lens), non_blocking=False)
+        return pairs
+
+    def swap_in(self, seqs, stream=None):
+        """Brings swapped-out sequences back into fresh device blocks."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        seqs = [int(s) for s in seqs]
+        rows = [self.swapped[s][0] for s in seqs]
+        ids = np.concatenate([r[r >= 0] for r in rows]) if rows else np.zeros(0, np.int32)
+        new, pairs = capi.kv_block_swap(self.host_pool, self.pool, ids)
+        k = 0
+        for s, r in zip(seqs, rows):
+            live = np.nonzero(r >= 0)[0]
+            self.tables[s, :] = -1
+            self.tables[s, live] = new[k:k + len(live)]
+            k += len(live)
+            self.lens[s] = self.swapped.pop(s)[1]
+        self._swap_copy(pairs, self.k_host, self.v_host, self.num_host_blocks, self.k_cache,
+                        self.v_cache, self.num_blocks, stream)
+        self.tables_d.copy_(torch.from_numpy(self.tables), non_blocking=False)
+        self.lens_d.copy_(torch.from_numpy(self.lens), non_blocking=False)
+        return pairs
+
+    def _swap_copy(self, pairs, sk, sv, snb, dk, dv, dnb, stream):
+        if len(pairs) == 0:
+            return
+        (d_pairs,) = self._upload([np.ascontiguousarray(pairs, np.int32)], stream)
+        capi.paged_kv_swap_blocks(sk, sv, dk, dv, d_pairs, self.num_kv_heads, self.head_dim, snb,
+                                  dnb, stream.cuda_stream)
+
     def free_sequence(self, s: int):
         """Returns sequence s's blocks to the pool (one reference each)."""
         n = -(-int(self.lens[s]) // BLOCK)
-        capi.kv_block_free(self.pool, self.tables[s, :n])
+        row = self.tables[s, :n]
+        capi.kv_block_free(self.pool, row[row >= 0])
         self.tables[s, :] = -1
         self.lens[s] = 0
         self.tables_d[s].fill_(-1)

@@ -462,3 +462,233 @@ def test_prefix_cache_reuse_end_to_end():
 def capi_stats(kv):
     from paged_kv_cache_102_amd import _capi as capi
     return capi.pkv_prefix_stats(kv.pool)
+
+
+# ---------------------------------------------------------------- sliding window
+def _release_both(p, W, ctx_ora, ctx_kv):
+    """Window release on both sides (same pool discipline, so the same ids),
+    then NaN in every released block on both sides: a read of one shows."""
+    from oracle import preempt
+    from paged_kv_cache_102_amd import _capi as capi
+    rows = [list(r) for r in p.ora.tables]
+    old = p.ora.tables.copy()
+    preempt.window_release(p.ora.pool, rows, ctx_ora, W)
+    p.ora.tables[:] = np.array(rows, np.int32)
+    upd = capi.pkv_window_release(p.kv.pool, p.kv.tables, ctx_kv, W)
+    if len(upd):
+        capi.paged_block_table_update(p.kv.tables_d, torch.from_numpy(upd).cuda())
+    released = sorted(set(old[(old >= 0) & (p.ora.tables < 0)].tolist()))
+    free = set(capi.kv_pool_free_list(p.kv.pool).tolist())
+    assert set(released) <= free
+    if released:
+        nb = p.w.num_blocks
+        p.kv.k_cache.view(nb, -1)[released] = float("nan")
+        p.kv.v_cache.view(nb, -1)[released] = float("nan")
+        poison = np.uint16(0x7FC0) if p.ora.cache.dtype == "bf16" else np.float32(np.nan)
+        p.ora.cache.k[released] = poison
+        p.ora.cache.v[released] = poison
+    return released
+
+
+@pytest.mark.parametrize("form", ["cu", "wave", "part32", "part512", "f32"])
+@pytest.mark.parametrize("W", [1, 37, 300])
+def test_window_decode_vs_oracle(form, W, monkeypatch):
+    """Sliding-window decode in every decode form, after the blocks before
+    each window were released and poisoned, then one append step (release
+    through the driver) and decode again: caches and tables bit-exact,
+    outputs within the tolerance of the oracle's windowed attention."""
+    from oracle import attention as oatt
+    from oracle import replay as orep
+    from tests.gpu_parity import TOL, to_device
+    if form == "wave":
+        monkeypatch.setenv("PKV_DECODE_SPLIT", "wave")
+    dtype = "f32" if form == "f32" else "bf16"
+    ps = {"part32": 32, "part512": 512}.get(form, 0)
+    w = synth.small_random(500 + W, num_seqs=9, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                           dtype=dtype, max_len=700, fixed=[0, 1, 15, 16, 17, 33, 300])
+    p = _pair(w, partition_size=ps)
+    p.kv.window = W
+    released = _release_both(p, W, p.ora.lens, p.kv.lens)
+    s = w.spec
+    for step in range(2):
+        p.check_state()
+        out = p.kv.decode(p.q, s.scale).cpu().numpy().astype(np.float64)
+        exp = oatt.decode(w.q, p.ora.cache, p.ora.tables, p.ora.lens, s.num_q_heads,
+                          s.num_kv_heads, s.scale, window=W)
+        err = float(np.max(np.abs(out - exp)))
+        print(f"[window] form={form} W={W} step {step}: released {len(released)} blocks, "
+              f"max abs err {err:.2e}", flush=True)
+        assert np.isfinite(out).all() and err <= TOL[dtype]
+        if step == 0:
+            # the driver releases with the next query's context (length + 1)
+            # before planning; the oracle does the same, then appends
+            from oracle import preempt
+            rows = [list(r) for r in p.ora.tables]
+            old = p.ora.tables.copy()
+            preempt.window_release(p.ora.pool, rows, p.ora.lens + 1, W)
+            p.ora.tables[:] = np.array(rows, np.int32)
+            released = sorted(set(old[(old >= 0) & (p.ora.tables < 0)].tolist()))
+            nb = w.num_blocks
+            poison = np.uint16(0x7FC0) if dtype == "bf16" else np.float32(np.nan)
+            p.ora.cache.k[released] = poison
+            p.ora.cache.v[released] = poison
+            p.kv.k_cache.view(nb, -1)[released] = float("nan")
+            p.kv.v_cache.view(nb, -1)[released] = float("nan")
+            orep.append_step(p.ora, w)
+            p.kv.append(to_device(w.k_app), to_device(w.v_app), w.append_counts)
+
+
+def test_window_decode_fp8_vs_oracle():
+    from oracle import attention as oatt
+    from oracle import preempt
+    from paged_kv_cache_102_amd import _capi as capi
+    from tests.gpu_parity import to_device
+    w = synth.small_random(611, num_seqs=7, num_q_heads=16, num_kv_heads=2, head_dim=64,
+                           dtype="bf16", max_len=600, fixed=[0, 1, 16, 17, 40])
+    ora, kv = _fp8_pair(w, 4.0 / 448, 3.5 / 448)
+    W = 45
+    kv.window = W
+    rows = [list(r) for r in ora.tables]
+    old = ora.tables.copy()
+    preempt.window_release(ora.pool, rows, ora.lens, W)
+    ora.tables[:] = np.array(rows, np.int32)
+    upd = capi.pkv_window_release(kv.pool, kv.tables, kv.lens, W)
+    capi.paged_block_table_update(kv.tables_d, torch.from_numpy(upd).cuda())
+    released = sorted(set(old[(old >= 0) & (ora.tables < 0)].tolist()))
+    kv.k_cache.view(w.num_blocks, -1)[released] = 0x7F
+    kv.v_cache.view(w.num_blocks, -1)[released] = 0x7F
+    ora.cache.k[released] = 0x7F
+    ora.cache.v[released] = 0x7F
+    _fp8_check_cache(ora, kv)
+    out = kv.decode(to_device(w.q), w.spec.scale).cpu().numpy().astype(np.float64)
+    exp = oatt.decode(w.q, ora.cache, ora.tables, ora.lens, 16, 2, w.spec.scale, window=W)
+    err = float(np.max(np.abs(out - exp)))
+    print(f"[window fp8] released {len(released)}: max abs err {err:.2e}", flush=True)
+    assert released and np.isfinite(out).all() and err <= 2e-3
+
+
+@pytest.mark.parametrize("W", [1, 20, 100])
+def test_window_prefill_vs_oracle(W):
+    """Chunk rows with a sliding window, after releasing the blocks before
+    the first row's window (context L - n + 1) and poisoning them."""
+    from oracle import attention as oatt
+    from oracle.slots import plan_append
+    from tests.gpu_parity import to_device
+    Hq, Hkv, D, B, maxc = 8, 2, 128, 9, 70
+    w = synth.small_random(700 + W, num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           dtype="bf16", max_len=300, append=maxc, fixed=[0, 0, 1, 16, 17])
+    p = _pair(w)
+    p.kv.window = W
+    rng = np.random.default_rng(W)
+    counts = rng.integers(0, maxc + 1, size=B)
+    counts[:5] = [maxc, 33, 1, 0, 16]
+    T = int(counts.sum())
+    k_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    v_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    q = synth.round_bf16_bits(rng.standard_normal((T, Hq, D)).astype(np.float32))
+    # the oracle appends, then both release for the first chunk row
+    slots, _, cows = plan_append(p.ora.pool, p.ora.tables, p.ora.lens, counts)
+    p.ora.cache.write(k_new, v_new, slots)
+    kv_window, p.kv.window = p.kv.window, 0         # plain append; release below
+    p.kv.append(to_device(k_new), to_device(v_new), counts.astype(np.int32))
+    p.kv.window = kv_window
+    ctx = np.maximum(p.ora.lens - counts + 1, 0).astype(np.int32)
+    ctx[counts == 0] = p.ora.lens[counts == 0]
+    released = _release_both(p, W, ctx, ctx)
+    p.check_state()
+    qstart = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    out = p.kv.prefill_attention(to_device(q), qstart, w.spec.scale).cpu().numpy()
+    exp = oatt.prefill(q, p.ora.cache, p.ora.tables, p.ora.lens, qstart, Hq, Hkv, w.spec.scale,
+                       window=W)
+    err = float(np.max(np.abs(out.astype(np.float64) - exp)))
+    print(f"[window prefill] W={W} released {len(released)}: max abs err {err:.2e}", flush=True)
+    assert np.isfinite(out).all() and err <= 2e-3
+
+
+def test_window_argument_errors():
+    from paged_kv_cache_102_amd import _capi as capi
+    q = torch.zeros(1, 4, 128, dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros(2 * 16 * 128, dtype=torch.bfloat16, device="cuda")
+    t = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
+    ln = torch.ones(1, dtype=torch.int32, device="cuda")
+    out = torch.zeros(1, 4, 128, device="cuda")
+    with pytest.raises(capi.PkvError):
+        capi.paged_attention_decode_window(q, c, c, t, ln, out, num_kv_heads=1, num_blocks=2,
+                                           max_context_len=16, scale=0.1, window=-1,
+                                           partition_size=32)
+    qs = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    with pytest.raises(capi.PkvError):
+        capi.paged_attention_prefill(q, c, c, t, ln, qs, out, num_kv_heads=1, num_blocks=2,
+                                     max_context_len=16, max_query_len=1, scale=0.1, window=-2)
+
+
+# ---------------------------------------------------------------- block swap
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_swap_out_in_bit_exact(dtype):
+    """Swap some sequences out to pinned host memory, let other work poison
+    every free device block, swap them back: the host copy and the restored
+    cache are bit-identical to the oracle's (which does the same swap on its
+    own pools), and decode matches the oracle again."""
+    from oracle import cache as ocache
+    from oracle import preempt
+    from oracle.pool import PoolModel
+    from paged_kv_cache_102_amd import _capi as capi
+    from tests.gpu_parity import cache_bits, oracle_bits
+    w = synth.small_random(900 + (dtype == "f32"), num_seqs=8, num_q_heads=8, num_kv_heads=2,
+                           head_dim=128, dtype=dtype, max_len=400, fixed=[0, 1, 16, 17, 250])
+    p = _pair(w)
+    NH = 80
+    p.kv.enable_swap(NH)
+    hpool = PoolModel(NH)
+    s = w.spec
+    hcache = ocache.CacheModel(NH, s.num_kv_heads, s.head_dim, dtype)
+    p.check_decode()
+    out_seqs = [1, 3, 4, 6]
+    ids = np.concatenate([p.ora.tables[b, :-(-int(p.ora.lens[b]) // 16)] for b in out_seqs])
+    new_m, pairs_m = preempt.swap(p.ora.pool, hpool, [int(x) for x in ids])
+    p.ora.cache.copy_blocks_to(hcache, pairs_m)
+    lens_out = {b: int(p.ora.lens[b]) for b in out_seqs}
+    pairs_c = p.kv.swap_out(out_seqs)
+    assert pairs_c.tolist() == [list(x) for x in pairs_m]
+    torch.cuda.synchronize()
+    got_h = (cache_bits(p.kv.k_host.view(-1)), cache_bits(p.kv.v_host.view(-1)))
+    used = sorted(n for _, n in pairs_m)
+    per = s.num_kv_heads * 16 * s.head_dim
+    for got, exp in zip(got_h, (oracle_bits(hcache.k), oracle_bits(hcache.v))):
+        g, e = got.reshape(NH, per), exp.reshape(NH, per)
+        assert np.array_equal(g[used], e[used])
+    # other work: every free device block is overwritten
+    free = capi.kv_pool_free_list(p.kv.pool).tolist()
+    assert sorted(free) == sorted(p.ora.pool.free_list())
+    p.kv.k_cache.view(w.num_blocks, -1)[free] = float("nan")
+    p.kv.v_cache.view(w.num_blocks, -1)[free] = float("nan")
+    poison = np.uint16(0x7FC0) if dtype == "bf16" else np.float32(np.nan)
+    p.ora.cache.k[free] = poison
+    p.ora.cache.v[free] = poison
+    # the oracle's tables: swapped rows empty
+    htab = {}
+    k = 0
+    for b in out_seqs:
+        n = -(-lens_out[b] // 16)
+        htab[b] = new_m[k:k + n]
+        k += n
+        p.ora.tables[b] = -1
+        p.ora.lens[b] = 0
+    p.check_state()
+    p.check_decode(seqs=[b for b in range(s.num_seqs) if b not in out_seqs])
+    # swap back in, in another order
+    back = [6, 1, 4, 3]
+    hids = [x for b in back for x in htab[b]]
+    new2, pairs2 = preempt.swap(hpool, p.ora.pool, hids)
+    hcache.copy_blocks_to(p.ora.cache, pairs2)
+    k = 0
+    for b in back:
+        n = len(htab[b])
+        p.ora.tables[b, :n] = new2[k:k + n]
+        p.ora.lens[b] = lens_out[b]
+        k += n
+    pairs_c2 = p.kv.swap_in(back)
+    assert pairs_c2.tolist() == [list(x) for x in pairs2]
+    p.check_state()
+    err = p.check_decode()
+    print(f"[swap] {dtype}: {len(pairs_m)} blocks out and back, decode err {err:.2e}", flush=True)

@@ -221,3 +221,43 @@ def test_mutation_prefix_evicts_most_recent(monkeypatch):
         return b
     monkeypatch.setattr(prefix.PrefixPoolModel, "_take", bad_take)
     assert _fails(pc.test_eviction_order_and_descendants)
+
+
+# ---------------------------------------------------------------- sliding window and swap
+from oracle import preempt  # noqa: E402
+from tests import test_window_swap as wpins  # noqa: E402
+
+
+@pytest.mark.parametrize("bad", [lambda p, w: max(0, p - w) if w > 0 else 0,
+                                 lambda p, w: max(0, p - w + 2) if w > 0 else 0])
+def test_mutation_window_off_by_one(monkeypatch, bad):
+    monkeypatch.setattr(attention, "window_start", bad)
+    assert _fails(wpins.test_window_decode_equals_banded_sdpa, 17, "f32")
+    assert _fails(wpins.test_prefill_window_equals_banded_causal_sdpa, 7)
+
+
+def test_mutation_window_ignored_in_prefill(monkeypatch):
+    orig = attention.prefill
+    monkeypatch.setattr(attention, "prefill",
+                        lambda *a, window=0, **k: orig(*a, **k))
+    assert _fails(wpins.test_prefill_window_equals_banded_causal_sdpa, 20)
+
+
+def test_mutation_release_one_block_too_many(monkeypatch):
+    def bad(L, window):
+        lo = attention.window_start(L - 1, window) if L > 0 else 0
+        return [i for i in range(-(-L // 16)) if 16 * i < lo]   # frees the block holding lo
+    monkeypatch.setattr(preempt, "releasable", bad)
+    assert _fails(wpins.test_window_release_frees_only_unneeded_blocks, 17)
+
+
+def test_mutation_swap_unshares(monkeypatch):
+    def bad(src, dst, ids):
+        ids = [int(i) for i in ids]
+        if len(ids) > dst.num_free():
+            raise preempt.PoolError("oom", "")
+        new = dst.alloc(len(ids))                # one host block per reference
+        src.free(ids)
+        return new, list(zip(ids, new))
+    monkeypatch.setattr(preempt, "swap", bad)
+    assert _fails(wpins.test_swap_round_trip_bit_exact)
