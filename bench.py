@@ -205,6 +205,162 @@ def fp8_measure(dev, w, reps: int = 50):
     return res
 
 
+def window_measure(dev, kv, q, scale, windows=(4096, 1024), reps: int = 30):
+    """Sliding-window decode on the headline batch: for each window W, time
+    decode alone (kernel reads only positions max(0, L - W) .. L - 1 of each
+    sequence, from the block holding the window start), then release the
+    blocks wholly before every window and count them.  Windows go from wide
+    to narrow, so each release only adds to the previous one."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_102_amd import _capi as capi
+    s_kv, D = kv.num_kv_heads, kv.head_dim
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    used0 = capi.kv_pool_stats(kv.pool)["num_used"]
+    res = []
+    for W in windows:
+        kv.window = W
+        for _ in range(5):
+            kv.decode(q, scale, out=out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            kv.decode(q, scale, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        lens = kv.lens.astype(np.int64)
+        lo = np.maximum(lens - W, 0)
+        tile_lo = lo // 16 * 16                      # the kernel streams whole blocks
+        attended = int((lens - lo).sum()) * 2 * s_kv * D * 2
+        streamed = int((lens - tile_lo).sum()) * 2 * s_kv * D * 2
+        upd = capi.pkv_window_release(kv.pool, kv.tables, kv.lens, W)
+        if len(upd):
+            capi.paged_block_table_update(kv.tables_d, torch.from_numpy(upd).to(dev))
+        used = capi.kv_pool_stats(kv.pool)["num_used"]
+        res.append({"window": W, "ms": round(ms, 4), "attended_kv_bytes": attended,
+                    "kv_gb_per_s": round(streamed / ms / 1e6, 1),
+                    "frac_of_hbm_peak": round(streamed / ms / 1e6 / HBM_PEAK_GBS, 4),
+                    "blocks_in_use_after_release": int(used),
+                    "blocks_released_frac": round(1 - used / used0, 4)})
+    kv.window = 0
+    return {"workload": f"{WORKLOAD} batch after the timed steps; kv_gb_per_s counts the "
+                        "window's blocks (from the one holding the window start)",
+            "results": res}
+
+
+def swap_measure(dev, kv, frac: float = 0.5, reps: int = 5):
+    """Block swap of about ``frac`` of the batch's blocks: the copy kernel
+    (paged_kv_swap_blocks) device -> pinned host and back, each timed with
+    events on its stream, beside a plain DMA copy of the same byte count
+    between the same kinds of memory (torch copy_, one contiguous run)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_102_amd import _capi as capi
+    order = np.argsort(-kv.lens)
+    n_tot = int(np.sum(-(-kv.lens // 16)))
+    pick, nb = [], 0
+    for b in order:
+        if nb >= frac * n_tot:
+            break
+        pick.append(int(b))
+        nb += -(-int(kv.lens[b]) // 16)
+    ids = np.concatenate([kv.tables[b, :-(-int(kv.lens[b]) // 16)] for b in pick])
+    ids = ids[ids >= 0]
+    NH = len(ids)
+    per_block = kv.num_kv_heads * 16 * kv.head_dim
+    hk = torch.empty(NH * per_block, dtype=kv.k_cache.dtype, pin_memory=True)
+    hv = torch.empty(NH * per_block, dtype=kv.v_cache.dtype, pin_memory=True)
+    # host planning cost, on a pool pair of the same sizes (the batch's own
+    # pool keeps its state: the copies below move its blocks' data to host
+    # slots 0..NH-1 and back onto the same blocks)
+    gp, hpool = capi.pkv_pool_create(kv.num_blocks, 16), capi.pkv_pool_create(NH, 16)
+    held = capi.kv_block_alloc(gp, NH)
+    t0 = time.perf_counter()
+    capi.kv_block_swap(gp, hpool, held)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    pairs = np.stack([ids, np.arange(NH)], axis=1).astype(np.int32)
+    d_pairs = torch.from_numpy(pairs).to(dev)
+    back_pairs = torch.from_numpy(np.ascontiguousarray(pairs[:, ::-1])).to(dev)
+    st = torch.cuda.current_stream(dev)
+    nbytes = 2 * len(pairs) * per_block * kv.k_cache.element_size()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out_ms = timed(lambda: capi.paged_kv_swap_blocks(kv.k_cache, kv.v_cache, hk, hv, d_pairs,
+                                                     kv.num_kv_heads, kv.head_dim, kv.num_blocks,
+                                                     NH, st.cuda_stream))
+    in_ms = timed(lambda: capi.paged_kv_swap_blocks(hk, hv, kv.k_cache, kv.v_cache, back_pairs,
+                                                    kv.num_kv_heads, kv.head_dim, NH,
+                                                    kv.num_blocks, st.cuda_stream))
+    # DMA of the same bytes: device <-> pinned host, one run each way
+    dsrc = kv.k_cache[:nbytes // 2 // kv.k_cache.element_size()]
+    hdst = hk[:dsrc.numel()]
+    d2h_ms = timed(lambda: (hdst.copy_(dsrc, non_blocking=True), hv[:dsrc.numel()].copy_(
+        kv.v_cache[:dsrc.numel()], non_blocking=True)))
+    kscratch = torch.empty_like(dsrc)
+    vscratch = torch.empty_like(dsrc)
+    h2d_ms = timed(lambda: (kscratch.copy_(hdst, non_blocking=True),
+                            vscratch.copy_(hv[:dsrc.numel()], non_blocking=True)))
+    del hk, hv, kscratch, vscratch
+    gbs = lambda ms: round(nbytes / ms / 1e6, 1)
+    return {"workload": f"{len(pick)} longest sequences of the {WORKLOAD} batch, "
+                        f"{len(pairs)} blocks, K and V",
+            "bytes": nbytes, "plan_ms": round(plan_ms, 3),
+            "swap_out_ms": round(out_ms, 3), "swap_out_gb_per_s": gbs(out_ms),
+            "swap_in_ms": round(in_ms, 3), "swap_in_gb_per_s": gbs(in_ms),
+            "dma_d2h_gb_per_s": gbs(d2h_ms), "dma_h2d_gb_per_s": gbs(h2d_ms),
+            "out_frac_of_dma": round(d2h_ms / out_ms, 3), "in_frac_of_dma": round(h2d_ms / in_ms, 3),
+            "round_trip_ms_per_4gb": round((out_ms + in_ms) * 4e9 / nbytes, 1)}
+
+
+def prefix_measure(num_requests: int = 128, prefix_tokens: int = 2048, suffix_max: int = 256):
+    """Prefix caching on the host: requests sharing a 2048-token system
+    prompt, each with its own suffix.  The first request's blocks are
+    registered; every later one matches them (longest indexed prefix), takes
+    fresh blocks for the rest and registers its own.  Reports the host cost
+    per request and the share of blocks (and KV writes) that reuse saves."""
+    import numpy as np
+    from paged_kv_cache_102_amd import _capi as capi
+    rng = np.random.default_rng(55)
+    system = rng.integers(0, 32000, size=prefix_tokens).astype(np.int32)
+    reqs = [np.concatenate([system, rng.integers(0, 32000, size=int(rng.integers(1, suffix_max)))])
+            .astype(np.int32) for _ in range(num_requests)]
+    need = sum(-(-len(r) // 16) for r in reqs)
+    pool = capi.pkv_pool_create(need, 16)
+    capi.pkv_prefix_cache_enable(pool)
+    t_match = t_reg = 0.0
+    reused = 0
+    for r in reqs:
+        t0 = time.perf_counter()
+        got = capi.pkv_prefix_match(pool, r)
+        t1 = time.perf_counter()
+        fresh = capi.kv_block_alloc(pool, -(-len(r) // 16) - len(got))
+        t2 = time.perf_counter()
+        capi.pkv_prefix_register(pool, r, np.concatenate([got, fresh]).astype(np.int32))
+        t3 = time.perf_counter()
+        t_match += t1 - t0
+        t_reg += t3 - t2
+        reused += len(got)
+    return {"workload": f"{num_requests} requests, {prefix_tokens}-token shared prompt + "
+                        f"1..{suffix_max - 1} own tokens",
+            "match_us_per_request": round(t_match / num_requests * 1e6, 2),
+            "register_us_per_request": round(t_reg / num_requests * 1e6, 2),
+            "blocks_reused_frac": round(reused / need, 4),
+            "blocks_in_use": int(capi.kv_pool_stats(pool)["num_used"]),
+            "blocks_without_reuse": need}
+
+
 def kv_bytes(lens, num_kv_heads, head_dim, elem=2) -> int:
     return int(lens.astype("int64").sum()) * 2 * num_kv_heads * head_dim * elem
 
@@ -251,6 +407,8 @@ def main():
                     help="skip the FP8 cache decode measurement")
     ap.add_argument("--no-prefill", dest="prefill", action="store_false",
                     help="skip the multi-query (chunked prefill) measurement")
+    ap.add_argument("--no-extras", dest="extras", action="store_false",
+                    help="skip the sliding-window, swap and prefix-cache measurements")
     ap.add_argument("--all-configs", metavar="PATH", default=None,
                     help="also time decode alone on every workload and write them to PATH (JSON)")
     args = ap.parse_args()
@@ -383,6 +541,13 @@ def main():
         ceiling = buf.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         del buf, sink
 
+    stats = capi.kv_pool_stats(kv.pool)
+    waste = float(np.sum(-(-kv.lens // 16) * 16 - kv.lens) / np.sum(-(-kv.lens // 16) * 16))
+    swap = window = prefix = None
+    if args.extras:
+        swap = swap_measure(dev, kv)
+        window = window_measure(dev, kv, q, s.scale)   # releases blocks: after the rest
+        prefix = prefix_measure()
     fp8 = fp8_measure(dev, w) if args.fp8 else None
     prefill = None
     if args.prefill:
@@ -390,8 +555,6 @@ def main():
         prefill = prefill_measure(dev)
 
     traffic = committed_traffic()
-    stats = capi.kv_pool_stats(kv.pool)
-    waste = float(np.sum(-(-kv.lens // 16) * 16 - kv.lens) / np.sum(-(-kv.lens // 16) * 16))
     result = {
         "metric": "paged decode attn: effective KV GB/s & % of HBM peak; sequences/s",
         "value": round(value, 1),
@@ -425,6 +588,9 @@ def main():
         "paged_vs_contiguous": paged_vs_contig,
         "prefill_chunked": prefill,
         "fp8_decode": fp8,
+        "sliding_window_decode": window,
+        "block_swap": swap,
+        "prefix_cache_host": prefix,
         "hbm_read_ceiling_gbs": round(ceiling, 1) if ceiling else None,
         "decode_frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None,
     }

@@ -252,10 +252,15 @@ __device__ inline bool len_ok(int L, const DecodeArgs& a) {
 // positions, [win_lo, L).  Blocks wholly before win_lo are never read (their
 // table entries may already be released); the walk starts at the block
 // holding win_lo and masks the positions before it.
+// WIN = false compiles the window out (a kernel instance for window 0).
+template <bool WIN = true>
 __device__ inline int win_lo(const DecodeArgs& a, int L) {
-  return (a.window > 0 && L > a.window) ? L - a.window : 0;
+  return (WIN && a.window > 0 && L > a.window) ? L - a.window : 0;
 }
-__device__ inline int first_block_of(const DecodeArgs& a, int L) { return win_lo(a, L) / kBlock; }
+template <bool WIN = true>
+__device__ inline int first_block_of(const DecodeArgs& a, int L) {
+  return win_lo<WIN>(a, L) / kBlock;
+}
 
 // Buffer resource over one cache tile: loads at byte offsets below `bytes`
 // read memory; with bytes == 0 every load returns zeros without a memory
@@ -488,8 +493,9 @@ __device__ inline int load_uniform(const int* p, int64_t i) {
 }
 
 // Tiles of a sequence in the work list: its blocks from the window's first.
+template <bool WIN = true>
 __device__ inline int nblocks_of(const DecodeArgs& a, int L) {
-  return len_ok(L, a) ? (L + kBlock - 1) / kBlock - first_block_of(a, L) : 0;
+  return len_ok(L, a) ? (L + kBlock - 1) / kBlock - first_block_of<WIN>(a, L) : 0;
 }
 
 // Sum over the wave, returned as a wave-uniform value (scalar register), so
@@ -1032,7 +1038,8 @@ __host__ __device__ inline int cu_lds_slots(int group, int head_dim) {
 
 // F8: the cache holds FP8 E4M3 codes (tiles of 16 D bytes, converted to
 // bf16 in registers; scales folded into the score scale and out_scale).
-template <int D, int ST, int AUX, bool F8 = false>
+// WIN: sliding window on (a.window > 0); off, the window code compiles out.
+template <int D, int ST, int AUX, bool F8 = false, bool WIN = false>
 __global__ __launch_bounds__(64 * kCuWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_bf16_cu_kernel(DecodeArgs a) {
   constexpr int NJ = D / 32;
@@ -1080,7 +1087,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     for (int k = 0; k < 4; ++k)
       lenv[k] = __builtin_amdgcn_raw_buffer_load_b32(rl, (lane * 4 + k) * 4, 0, 0);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) cnt[k] = nblocks_of(a, lenv[k]);
+    for (int k = 0; k < 4; ++k) cnt[k] = nblocks_of<WIN>(a, lenv[k]);
   }
   auto pick = [](const int (&v)[4], int k) {
     return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
@@ -1138,7 +1145,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     b = __builtin_amdgcn_readfirstlane(pos * 4 + k);
     blk = __builtin_amdgcn_readfirstlane(r);
     L = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(pick(lenv, k), pos));
-    nb = nblocks_of(a, L);
+    nb = nblocks_of<WIN>(a, L);
   };
   auto advance = [&](int& kvh, int& b, int& blk, int& L, int& nb) {
     ++blk;
@@ -1153,7 +1160,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
         }
       }
       L = load_uniform(a.lens, b);
-      nb = nblocks_of(a, L);
+      nb = nblocks_of<WIN>(a, L);
     }
   };
   // claims the next chunk of the CU's range: [s, e), empty when none is left
@@ -1194,7 +1201,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     rec_first[st] = l_idx == l_us;
     rec_last[st] = l_idx == l_ue - 1;
     int phys = live ? load_uniform(a.tables, int64_t(l_b) * a.max_blocks +
-                                                 first_block_of(a, l_L) + l_blk)
+                                                 first_block_of<WIN>(a, l_L) + l_blk)
                     : 0;
     bool bad = false;
     int bytes = live ? TILE_BYTES : 0;
@@ -1340,7 +1347,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kx[j]), qf[j], s,
                                                    0, 0, 0);
     // block c_blk of the list is block c_first + c_blk of the sequence
-    const int wlo = win_lo(a, c_L);
+    const int wlo = win_lo<WIN>(a, c_L);
     const int c_first = wlo / kBlock;
     const int tb = (c_first + c_blk) * kBlock + grp * 4;
     float sv[4];
@@ -2089,19 +2096,28 @@ void launch_decode_bf16_balanced(unsigned grid, hipStream_t stream, const Decode
   }
 }
 
-void launch_decode_bf16_cu(unsigned grid, hipStream_t stream, const DecodeArgs& a, int head_dim,
-                           bool fp8) {
+template <bool WIN>
+void launch_decode_bf16_cu_w(unsigned grid, hipStream_t stream, const DecodeArgs& a, int head_dim,
+                             bool fp8) {
   const dim3 block(64 * kCuWaves);
   if (fp8) {
     if (head_dim == 64)
-      hipLaunchKernelGGL((decode_bf16_cu_kernel<64, 3, 2, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_bf16_cu_kernel<64, 3, 2, true, WIN>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_bf16_cu_kernel<128, 2, 2, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_bf16_cu_kernel<128, 2, 2, true, WIN>), grid, block, 0, stream, a);
   } else if (head_dim == 64) {
-    hipLaunchKernelGGL((decode_bf16_cu_kernel<64, 3, 2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_bf16_cu_kernel<64, 3, 2, false, WIN>), grid, block, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_bf16_cu_kernel<128, 2, 2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_bf16_cu_kernel<128, 2, 2, false, WIN>), grid, block, 0, stream, a);
   }
+}
+
+void launch_decode_bf16_cu(unsigned grid, hipStream_t stream, const DecodeArgs& a, int head_dim,
+                           bool fp8) {
+  if (a.window > 0)
+    launch_decode_bf16_cu_w<true>(grid, stream, a, head_dim, fp8);
+  else
+    launch_decode_bf16_cu_w<false>(grid, stream, a, head_dim, fp8);
 }
 
 void launch_prefill_bf16(unsigned grid, hipStream_t stream, const PrefillArgs& a, int head_dim) {
