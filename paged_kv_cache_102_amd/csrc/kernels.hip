@@ -51,6 +51,8 @@ constexpr int kDefaultPartition = 512;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ in-tile order
 __host__ __device__ inline int k_elem(int t, int d) { return (d >> 3) * 128 + t * 8 + (d & 7); }
@@ -1567,11 +1569,28 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
 // Several new query tokens per sequence over the same paged cache: sequence
 // b's chunk of n_b tokens holds the last n_b of its L_b cached positions
 // (their K/V written before the call); chunk token i sits at position
-// p = L_b - n_b + i and attends to positions 0..p (causal inside the chunk).
-// A decode step is the case n_b = 1.  One wavefront per (kv head, sequence,
-// tile of query positions): the 16 columns of the score tile are
-// (position, head-in-group) pairs, QB = 16 / g positions per tile, so one
-// load of a K/V tile serves 16 query rows (g for decode).
+// p = L_b - n_b + i and attends to positions 0..p (causal inside the chunk;
+// with a sliding window of W tokens, p-W+1..p).  A decode step is the case
+// n_b = 1.
+//
+// One workgroup of 8 wavefronts per (sequence, kv head, tile of query
+// positions), two per SIMD.  The tile's score columns are (position,
+// head-in-group) pairs, 256 of them (32 per wavefront, as two 16-column MFMA
+// tiles), so 256 / g positions per tile.  The K and V tiles of two consecutive blocks
+// (one stage) are loaded once per workgroup into LDS (double-buffered, the
+// next stage's global loads in flight during this stage's compute) and every
+// wavefront reads them from there:
+//   S^T = K . Q^T   v_mfma_f32_16x16x32_bf16, A = K piece j (16 tokens x 32
+//                   channels, the cache's lane order), B = Q^T chunk j;
+//   O  += P . V     v_mfma_f32_16x16x32_bf16 over the stage's 32 tokens: a
+//                   lane's k-index i < 4 is token 4(l/16)+i of the first
+//                   block, i >= 4 the same token of the second block -- the
+//                   layout S^T comes out in, and the halves of the V tile's
+//                   lane pieces of the two blocks;
+// with P carried as a bf16 high part plus a bf16 residual.  The running max
+// is raised only when a block's max exceeds it by more than 2^8 (the
+// normaliser uses the same reference, so the result is unchanged, and the
+// accumulator is rescaled rarely).
 struct PrefillArgs {
   const void* q;          // [T][Hq][D] bf16, T = qstart[B]
   const void* kc;
@@ -1580,191 +1599,305 @@ struct PrefillArgs {
   const int32_t* lens;
   const int32_t* qstart;  // [B + 1] first chunk row of each sequence
   float* out;             // [T][Hq][D] fp32
-  int num_seqs, num_q_heads, num_kv_heads, group, qb;
+  int num_seqs, num_q_heads, num_kv_heads, group;
+  int qtp;                // query positions per workgroup tile: 256 / group
+  int tiles;              // tiles per sequence: ceil(max_query_len / qtp)
   int num_blocks, max_blocks, max_ctx;
   float scale_log2e;
   int window;  // sliding window in tokens: position p sees p-window+1 .. p (0: 0 .. p)
 };
 
-template <int D, int ST, int AUX>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
-void prefill_bf16_kernel(PrefillArgs a) {
-  constexpr int NJ = D / 32;
-  constexpr int NT = D / 16;
-  constexpr int64_t TILE = int64_t(kBlock) * D;
-  constexpr int TILE_BYTES = static_cast<int>(TILE * 2);
+constexpr int kPfWaves = 8;
+constexpr int kPfColTiles = 2;                       // 16-column tiles per wavefront
+constexpr int kPfCols = kPfWaves * kPfColTiles * 16;  // score columns per workgroup
+constexpr float kPfRescale = 8.0f;                   // lazy max threshold (log2 domain)
 
-  const int lane = threadIdx.x;
-  const int64_t wid = blockIdx.x;  // kv head fastest, then sequence, then query tile
-  const int kvh = static_cast<int>(wid % a.num_kv_heads);
-  const int b = static_cast<int>((wid / a.num_kv_heads) % a.num_seqs);
-  const int qt = static_cast<int>(wid / (int64_t(a.num_kv_heads) * a.num_seqs));
+template <int D, bool WIN>
+__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_bf16_kernel(PrefillArgs a) {
+  constexpr int NJ = D / 32;                  // K / V pieces per tile
+  constexpr int NT = D / 16;                  // 16-channel output tiles
+  constexpr int NQ = kPfColTiles;
+  constexpr int TILE_BYTES = kBlock * D * 2;
+  constexpr int STAGE_BYTES = 4 * TILE_BYTES;  // blocks 0, 1 x (K, V)
+  constexpr int PIECES = STAGE_BYTES / 16;     // 16-byte loads per stage
+  constexpr int PT = PIECES / (64 * kPfWaves);  // per thread
+  constexpr int TILE_PIECES = TILE_BYTES / 16;
+  constexpr int NBUF = 2;  // stage s, and stage s + 1 being filled
+  __shared__ __align__(16) unsigned char lds[NBUF * STAGE_BYTES];
+
+  // Work item: workgroup i runs on XCD i % 8.  Each XCD takes a contiguous
+  // run of items (query tile fastest), so the tiles of one (sequence, kv
+  // head) read its K/V through one L2.
+  const int N = gridDim.x, id = blockIdx.x;
+  const int full = N / 8 * 8;
+  const int w = id < full ? (id % 8) * (N / 8) + id / 8 : id;
+  const int qt = w % a.tiles;
+  const int kvh = (w / a.tiles) % a.num_kv_heads;
+  const int b = w / (a.tiles * a.num_kv_heads);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hcol = lane & 15;
   const int grp = lane >> 4;
   const int g = a.group;
-  const int QB = a.qb;
+  const int QTP = a.qtp;
   const int qs = load_uniform(a.qstart, b);
   const int n = load_uniform(a.qstart, b + 1) - qs;
-  const int q0 = qt * QB;
+  const int q0 = qt * QTP;
   if (q0 >= n || n <= 0) return;
   const int L = load_uniform(a.lens, b);
-  const int nq = min(QB, n - q0);  // positions in this tile
-  // column c = (position qi, head hh); columns past the tile are padding
-  const int qi = hcol / g, hh = hcol % g;
-  const bool col_ok = hcol < nq * g;
-
+  const int nq = min(QTP, n - q0);  // positions in this tile
+  const int ncol = nq * g;          // live columns
   auto out_row = [&](int c) -> float* {  // output row of column c
     return a.out + ((int64_t(qs) + q0 + c / g) * a.num_q_heads + int64_t(kvh) * g + c % g) * D;
   };
   const bool len_bad = L < 0 || L > a.max_ctx || int64_t(L) > int64_t(a.max_blocks) * kBlock ||
                        n > L;
   if (len_bad) {
-    for (int c = 0; c < nq * g; ++c)
+    for (int c = wave; c < ncol; c += kPfWaves)
       for (int e = lane; e < D; e += 64) out_row(c)[e] = __builtin_nanf("");
     return;
   }
-  const int p_last = L - n + q0 + nq - 1;          // last position of the tile
-  const int p_col = col_ok ? L - n + q0 + qi : p_last;
-  // sliding window: column p_col sees [c_lo, p_col]; the walk starts at the
-  // block holding the earliest c_lo of the tile (its first column's)
-  const int c_lo = a.window > 0 ? max(0, p_col - a.window + 1) : 0;
-  const int t_lo = a.window > 0 ? max(0, L - n + q0 - a.window + 1) : 0;
+  const int p_first = L - n + q0;  // first and last position of the tile
+  const int p_last = p_first + nq - 1;
+  const int t_lo = WIN ? max(0, p_first - a.window + 1) : 0;  // earliest visible position
   const int i0 = t_lo / kBlock;
   const int nblk = p_last / kBlock + 1 - i0;
+  const int nst = (nblk + 1) / 2;
   const int32_t* row = a.tables + int64_t(b) * a.max_blocks + i0;
 
-  // Q^T as B operand: lane holds q[row of column hcol][32j + 8 grp .. +8]
-  bf16x8 qf[NJ];
+  // this lane's columns: c = 16 (NQ wave + t) + hcol -> (position, head)
+  int pos[NQ], lo_c[NQ];
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+    const int c = (NQ * wave + t) * 16 + hcol;
+    pos[t] = c < ncol ? p_first + c / g : p_last;
+    lo_c[t] = WIN ? pos[t] - a.window + 1 : 0;
+  }
+
+  // Q^T as B operands: lane holds q[row of column hcol][32j + 8 grp .. +8];
+  // one resource over the tile's query rows, padding columns read past it (0)
+  bf16x8 qf[NQ][NJ];
   {
-    // one resource over the tile's query rows; padding columns read past it (zeros)
     const int row_bytes = a.num_q_heads * D * 2;
     const char* qb = static_cast<const char*>(a.q) + (int64_t(qs) + q0) * row_bytes;
     const __amdgpu_buffer_rsrc_t rq = tile_rsrc(qb, nq * row_bytes);
-    const int qoff = col_ok ? qi * row_bytes + (kvh * g + hh) * D * 2 : nq * row_bytes;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      qf[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + (32 * j + grp * 8) * 2, 0, 0));
+    for (int t = 0; t < NQ; ++t) {
+      const int c = (NQ * wave + t) * 16 + hcol;
+      const int qoff = c < ncol ? (c / g) * row_bytes + (kvh * g + c % g) * D * 2 : nq * row_bytes;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        qf[t][j] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + (32 * j + grp * 8) * 2, 0, 0));
+    }
   }
 
   const char* kc = static_cast<const char*>(a.kc) + int64_t(kvh) * TILE_BYTES;
   const char* vc = static_cast<const char*>(a.vc) + int64_t(kvh) * TILE_BYTES;
   const int64_t block_bytes = int64_t(a.num_kv_heads) * TILE_BYTES;
-  const int loff = lane * 16;
-
-  f32x4 o[NT];
-#pragma unroll
-  for (int k = 0; k < NT; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
   bool bad = false;
 
-  uint4 kr[ST][NJ], vr[ST][NJ];
-  auto issue = [&](int i, int st) {
-    int bytes = TILE_BYTES;
-    int phys = 0;
-    if (i >= nblk) {
-      bytes = 0;
-    } else {
-      phys = load_uniform(row, i);
-      if (phys < 0 || phys >= a.num_blocks) {
-        bad = true;
-        bytes = 0;
+  // Stage loader: thread tid moves pieces 512 u + tid (u < PT) of the stage's
+  // four tiles (block 0 K, block 0 V, block 1 K, block 1 V); a wavefront's 64
+  // pieces lie in one tile, so the tile (and its block id, read once per
+  // stage through the scalar cache) is wave-uniform.  V slots outside
+  // [t_lo, L) are zeroed on the way (they may hold anything).
+  uint4 st[PT];
+  auto gload = [&](int s) {
+    int ph[2], by[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int rel = 2 * s + k;
+      ph[k] = 0;
+      by[k] = 0;
+      if (rel < nblk) {
+        ph[k] = load_uniform(row, rel);
+        if (ph[k] < 0 || ph[k] >= a.num_blocks)
+          bad = true;
+        else
+          by[k] = TILE_BYTES;
       }
     }
-    const int64_t off = int64_t(bytes ? phys : 0) * block_bytes;
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + off, bytes);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + off, bytes);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      kr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + 1024 * j, 0, AUX));
-      vr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + 1024 * j, 0, AUX));
+    for (int u = 0; u < PT; ++u) {
+      // the wavefront's 64 pieces: a 1 KiB run at a uniform offset of its tile
+      const int first = 64 * kPfWaves * u + 64 * wave;
+      const int tile = first / TILE_PIECES;
+      const int off0 = (first % TILE_PIECES) * 16;
+      const int rel = 2 * s + (tile >> 1);
+      const int phys = (tile >> 1) ? ph[1] : ph[0];
+      const int bytes = (tile >> 1) ? by[1] : by[0];
+      const char* base = ((tile & 1) ? vc : kc) + (bytes ? int64_t(phys) * block_bytes : 0) + off0;
+      const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, bytes ? bytes - off0 : 0);
+      uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, 0));
+      if (tile & 1) {
+        // V piece: lane l of a 1 KiB run holds tokens 4 (l / 16) .. + 3
+        const int t0 = (i0 + rel) * kBlock + 4 * grp;
+        if (t0 < t_lo || t0 + 4 > L) {
+          auto in = [&](int t) { return t < L && t >= t_lo; };
+          const uint32_t m01 = (in(t0) ? 0x0000FFFFu : 0u) | (in(t0 + 1) ? 0xFFFF0000u : 0u);
+          const uint32_t m23 = (in(t0 + 2) ? 0x0000FFFFu : 0u) | (in(t0 + 3) ? 0xFFFF0000u : 0u);
+          x.x &= m01;
+          x.y &= m23;
+          x.z &= m01;
+          x.w &= m23;
+        }
+      }
+      st[u] = x;
+    }
+  };
+  auto lwrite = [&](int s) {
+    unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int first = 64 * kPfWaves * u + 64 * wave;  // same run as in gload
+      *reinterpret_cast<uint4*>(sb + (first / TILE_PIECES) * TILE_BYTES +
+                                (first % TILE_PIECES) * 16 + lane * 16) = st[u];
     }
   };
 
-  auto compute_block = [&](int i, int st) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  f32x4 o[NQ][NT];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[st][j]), qf[j], s,
-                                                   0, 0, 0);
-    const int tb = (i0 + i) * kBlock + grp * 4;
-    float sv[4];
+  for (int t = 0; t < NQ; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      sv[r] = (tb + r <= p_col && tb + r >= c_lo) ? s[r] * a.scale_log2e : -INFINITY;
-    float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mloc = group_max(mloc);
-    const float mnew = fmaxf(m, mloc);
-    // a column whose positions all lie past this block keeps m = -inf
-    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
-    float p[4];
+    for (int k = 0; k < NT; ++k) o[t][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // running max per column (log2 domain; a finite floor, so that a column
+  // with nothing visible yet gets weights exp2(-inf - floor) = 0) and this
+  // lane's share of the normaliser
+  float m[NQ], lsum[NQ];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      p[r] = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r] - mnew);
-    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m = mnew;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, grp * 4 + r);
-#pragma unroll
-        for (int k = 0; k < NT; ++k) o[k][r] *= ar;
-      }
-    }
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      hi[r] = bf16_bits_rne(p[r]);
-      lo[r] = bf16_bits_rne(p[r] - __uint_as_float(hi[r] << 16));
-    }
-    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
-    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
-    if ((i0 + i) * kBlock + kBlock > L || (i0 + i) * kBlock < t_lo) {
-      // slots past the context or before the tile's window may hold
-      // anything: zero their V
-      auto in = [&](int t) { return t < L && t >= t_lo; };
-      const uint32_t m01 = (in(tb + 0) ? 0x0000FFFFu : 0u) | (in(tb + 1) ? 0xFFFF0000u : 0u);
-      const uint32_t m23 = (in(tb + 2) ? 0x0000FFFFu : 0u) | (in(tb + 3) ? 0xFFFF0000u : 0u);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        vr[st][j].x &= m01;
-        vr[st][j].y &= m23;
-        vr[st][j].z &= m01;
-        vr[st][j].w &= m23;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const s16x4 v0 = __builtin_bit_cast(s16x4, make_uint2(vr[st][j].x, vr[st][j].y));
-      const s16x4 v1 = __builtin_bit_cast(s16x4, make_uint2(vr[st][j].z, vr[st][j].w));
-      o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, v0, o[2 * j], 0, 0, 0);
-      o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, v0, o[2 * j], 0, 0, 0);
-      o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, v1, o[2 * j + 1], 0, 0, 0);
-      o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, v1, o[2 * j + 1], 0, 0, 0);
-    }
-  };
-
-  // ST-stage pipeline; every trip issues the same loads (empty past the end)
-#pragma unroll
-  for (int st = 0; st < ST; ++st) issue(st, st);
-  for (int i0 = 0; i0 < nblk; i0 += ST) {
-#pragma unroll
-    for (int st = 0; st < ST; ++st) {
-      const int i = i0 + st;
-      if (i < nblk) compute_block(i, st);
-      issue(i + ST, st);
-    }
+  for (int t = 0; t < NQ; ++t) {
+    m[t] = -1e30f;
+    lsum[t] = 0.f;
   }
 
-  lsum = group_sum(lsum);
+  // weights of the stage being processed (bf16 high parts and residuals)
+  uint32_t phi[NQ][4], plo[NQ][4];
+  // O += P . V over stage s's 32 tokens (k < 4: first block, k >= 4:
+  // second); each V piece is read once and used by all column tiles
+  auto pv = [&](int s) {
+    const unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int c = grp * 4 + r;  // output row = score column
-    const float lr = __shfl(lsum, c);
-    const float inv = bad ? __builtin_nanf("") : 1.0f / lr;
-    if (c < nq * g) {
-      float* dst = out_row(c) + hcol;
+    for (int j = 0; j < NJ; ++j) {
+      const uint4 v0 = *reinterpret_cast<const uint4*>(sb + 1 * TILE_BYTES + 1024 * j + lane * 16);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(sb + 3 * TILE_BYTES + 1024 * j + lane * 16);
+      const bf16x8 vlo = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+      const bf16x8 vhi = __builtin_bit_cast(bf16x8, make_uint4(v0.z, v0.w, v1.z, v1.w));
 #pragma unroll
-      for (int k = 0; k < NT; ++k) dst[16 * k] = o[k][r] * inv;
+      for (int t = 0; t < NQ; ++t) {
+        const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(phi[t][0], phi[t][1], phi[t][2], phi[t][3]));
+        const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(plo[t][0], plo[t][1], plo[t][2], plo[t][3]));
+        o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vlo, o[t][2 * j], 0, 0, 0);
+        o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vlo, o[t][2 * j], 0, 0, 0);
+        o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vhi, o[t][2 * j + 1], 0, 0, 0);
+        o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vhi, o[t][2 * j + 1], 0, 0, 0);
+      }
+    }
+  };
+
+  // scores of stage s, softmax update, weights into phi / plo
+  auto score = [&](int s) {
+    const unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
+    const int tb0 = (i0 + 2 * s) * kBlock;  // first position of the stage
+    // scores of both blocks for every column tile
+    f32x4 sc[NQ][2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      bf16x8 kx[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        kx[j] = *reinterpret_cast<const bf16x8*>(sb + (2 * bb) * TILE_BYTES + 1024 * j + lane * 16);
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx[j], qf[t][j], acc, 0, 0, 0);
+        sc[t][bb] = acc;
+      }
+    }
+    // masks are needed only where the stage reaches past the tile's first
+    // position (causal) or before its last column's window start
+    const bool edge = tb0 + 2 * kBlock - 1 > p_first || (WIN && tb0 < p_last - a.window + 1);
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) {
+      float sv[8];
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[4 * bb + r] = sc[t][bb][r] * a.scale_log2e;
+      if (edge) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tp = tb0 + (e >> 2) * kBlock + grp * 4 + (e & 3);
+          if (tp > pos[t] || tp < lo_c[t]) sv[e] = -INFINITY;
+        }
+      }
+      float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mloc = group_max(mloc);
+      // lazy max: raise it only when the stage max exceeds it by 2^8
+      const bool raise = mloc > m[t] + kPfRescale;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m[t] - mloc) : 1.0f;
+        m[t] = raise ? mloc : m[t];
+        lsum[t] *= alpha;
+        // output rows are columns 4 grp + r of the tile; their factors sit in lanes 4 grp + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(alpha, grp * 4 + r);
+#pragma unroll
+          for (int k = 0; k < NT; ++k) o[t][k][r] *= ar;
+        }
+      }
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] - m[t]);
+      lsum[t] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 h = __builtin_convertvector((f32x2{p[2 * e], p[2 * e + 1]}), bf16x2);
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+        const f32x2 rest = {p[2 * e] - __uint_as_float(hb << 16),
+                            p[2 * e + 1] - __uint_as_float(hb & 0xFFFF0000u)};
+        phi[t][e] = hb;
+        plo[t][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
+      }
+    }
+  };
+
+  // Pipeline: stage s is in LDS buffer s % 2.  At the top of each trip the
+  // barrier makes stage s visible and frees buffer (s + 1) % 2 (every
+  // wavefront has finished stage s - 1), which then takes stage s + 1 from
+  // registers while stage s + 2's global loads go out.
+  gload(0);
+  lwrite(0);
+  gload(1);
+  for (int s = 0; s < nst; ++s) {
+    __syncthreads();
+    if (s + 1 < nst) {
+      lwrite(s + 1);
+      gload(s + 2);
+    }
+    score(s);
+    pv(s);
+  }
+
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+    const float lt = group_sum(lsum[t]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int cl = grp * 4 + r;  // output row = column of the tile
+      const int c = (NQ * wave + t) * 16 + cl;
+      const float inv = bad ? __builtin_nanf("") : 1.0f / __shfl(lt, cl);
+      if (c < ncol) {
+        float* dst = out_row(c) + hcol;
+#pragma unroll
+        for (int k = 0; k < NT; ++k) dst[16 * k] = o[t][k][r] * inv;
+      }
     }
   }
 }
@@ -2121,10 +2254,18 @@ void launch_decode_bf16_cu(unsigned grid, hipStream_t stream, const DecodeArgs& 
 }
 
 void launch_prefill_bf16(unsigned grid, hipStream_t stream, const PrefillArgs& a, int head_dim) {
-  if (head_dim == 64)
-    hipLaunchKernelGGL((prefill_bf16_kernel<64, 3, 2>), grid, dim3(64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, 2, 2>), grid, dim3(64), 0, stream, a);
+  const dim3 block(64 * kPfWaves);
+  const bool win = a.window > 0;
+  if (head_dim == 64) {
+    if (win)
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, stream, a);
+  } else if (win) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, a);
+  }
 }
 
 // ============================================================================ C ABI
@@ -2298,15 +2439,16 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.group = group;
-  a.qb = 16 / group;
+  a.qtp = kPfCols / group;
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.max_ctx = max_context_len;
   a.scale_log2e = scale * 1.4426950408889634f;
   a.window = window;
-  const int64_t tiles = (int64_t(max_query_len) + a.qb - 1) / a.qb;
+  const int64_t tiles = (int64_t(max_query_len) + a.qtp - 1) / a.qtp;
   const int64_t grid = tiles * num_seqs * num_kv_heads;
   if (grid > 0x7FFFFFFF) return PKV_ERR_UNSUPPORTED;
+  a.tiles = static_cast<int>(tiles);
   launch_prefill_bf16(static_cast<unsigned>(grid), stream, a, head_dim);
   return launch_status();
 }

@@ -692,3 +692,41 @@ def test_swap_out_in_bit_exact(dtype):
     p.check_state()
     err = p.check_decode()
     print(f"[swap] {dtype}: {len(pairs_m)} blocks out and back, decode err {err:.2e}", flush=True)
+
+
+def test_prefill_full_size_sampled():
+    """The measured prefill shape (8 sequences, 512-token chunks on 1024..2048
+    cached tokens, 32 query / 8 kv heads, head_dim 128) in the same launch
+    configuration: sampled chunk rows (first, second, a block edge, the
+    middle, the last two) of every sequence and every head against the
+    oracle's attention over the rows each one sees."""
+    from oracle import attention as oatt
+    from tests.gpu_parity import to_device
+    n = 512
+    w = synth.small_random(4242, num_seqs=8, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           dtype="bf16", max_len=2048, min_len=1024, append=n)
+    p = _pair(w)
+    p.append()
+    p.check_state()
+    s = w.spec
+    rng = np.random.default_rng(9)
+    T = n * s.num_seqs
+    q = synth.round_bf16_bits(rng.standard_normal((T, s.num_q_heads, s.head_dim)).astype(np.float32))
+    qstart = np.arange(0, T + 1, n, dtype=np.int32)
+    out = p.kv.prefill_attention(to_device(q), qstart, s.scale).cpu().numpy().astype(np.float64)
+    assert np.isfinite(out).all()
+    qf = synth.bf16_bits_to_f32(q).astype(np.float64)
+    g = s.num_q_heads // s.num_kv_heads
+    err = 0.0
+    for b in range(s.num_seqs):
+        L = int(p.ora.lens[b])
+        kv = [p.ora.cache.gather(p.ora.tables[b], L, h) for h in range(s.num_kv_heads)]
+        for i in (0, 1, 15, 16, 255, 510, 511):
+            pos = L - n + i
+            r = qstart[b] + i
+            for h in range(s.num_q_heads):
+                k, v = kv[h // g]
+                exp = oatt.attend(qf[r, h], k[:pos + 1], v[:pos + 1], s.scale)
+                err = max(err, float(np.max(np.abs(out[r, h] - exp))))
+    print(f"[prefill full size] sampled max abs err {err:.2e}", flush=True)
+    assert err <= 2e-3
