@@ -1050,7 +1050,6 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   constexpr int64_t TILE = int64_t(kBlock) * D;
   constexpr int TILE_BYTES = static_cast<int>(TILE * (F8 ? 1 : 2));
   constexpr int NW = kCuWaves;
-  constexpr int NKMAX = 16 * D / 64;  // folded elements per lane: group * D / 64
 
   __shared__ __align__(16) unsigned char smem[kCuLdsBytes];
   const int g = a.group;
@@ -1431,136 +1430,175 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   // channel (64 k + lane) of the group's heads, head (64 k + lane) / D.
   const int nsl = hdr[1];
   const int nk = g * D / 64;
+  // Partial states of other CUs are read with the agent-coherent cache policy
+  // (sc1, as a device-scope relaxed atomic load is) but as plain buffer
+  // loads, so that all of a partner's values are in flight together.
+  constexpr int kSc1 = 16;
+  const __amdgpu_buffer_rsrc_t r_bo = tile_rsrc(a.bw_o, 0x7FFFFFF0);
+  const __amdgpu_buffer_rsrc_t r_bm = tile_rsrc(a.bw_m, 0x7FFFFFF0);
+  const __amdgpu_buffer_rsrc_t r_bl = tile_rsrc(a.bw_l, 0x7FFFFFF0);
+  // Two passes: items that cross the CU's range first (their cross-CU
+  // exchange has the longest latency), then the rest.  The fold runs once
+  // per wavefront, at the end, from a cold instruction cache: its loops are
+  // rolled over groups of 8 elements (unrolled inside for independent loads)
+  // so that the same short code serves every group, slot and partner.
+  for (int pass = 0; pass < 2; ++pass)
   for (int s = wave; s < nsl; s += NW) {
     const int item = s_item[s];
+    const int s0 = s_s0[s], nbs = s_nb[s];
+    const bool cross_start = s0 < R0, cross_end = s0 + nbs > R1;
+    const bool crossing = cross_start || cross_end;
+    if (crossing != (pass == 0)) continue;
     bool dup = false;
     for (int j0 = 0; j0 < s && !dup; j0 += 64) {
       const int j = j0 + lane;
       dup = __builtin_amdgcn_ballot_w64(j < s && s_item[j] == item) != 0;
     }
     if (dup) continue;
-    float acc[NKMAX], M[NKMAX], den[NKMAX];
+    // the item's slots from s on (slot indices below kCuSlots: 3 masks)
+    const int c0 = s & ~63;
+    uint64_t msk[3];
 #pragma unroll
-    for (int k = 0; k < NKMAX; ++k) {
-      acc[k] = 0.f;
-      M[k] = -INFINITY;
-      den[k] = 0.f;
+    for (int c = 0; c < 3; ++c) {
+      const int jl = c0 + 64 * c + lane;
+      msk[c] = __builtin_amdgcn_ballot_w64(jl >= s && jl < nsl && s_item[jl] == item);
     }
-    bool bad = false;
-    for (int j = s; j < nsl; ++j) {
-      if (s_item[j] != item) continue;
-#pragma unroll
-      for (int k = 0; k < NKMAX; ++k) {
-        if (k < nk) {
-          const int e = 64 * k + lane;
-          const int h = (64 * k) / D;
-          float mj, lj, oj;
-          if (j < cap) {
-            mj = s_m[j * g + h];
-            lj = s_l[j * g + h];
-            oj = s_o[j * g * D + e];
-          } else {
-            const float* base = o_base + (j - cap) * cu_state_floats(g, D);
-            mj = base[h];
-            lj = base[g + h];
-            oj = base[2 * g + e];
-          }
-          bad |= (mj != mj);
-          const float mn = fmaxf(M[k], mj);
-          const float fo = __builtin_amdgcn_exp2f(M[k] - mn);
-          const float fn = __builtin_amdgcn_exp2f(mj - mn);
-          acc[k] = acc[k] * fo + oj * fn;
-          den[k] = den[k] * fo + lj * fn;
-          M[k] = mn;
-        }
-      }
-    }
-    const int s0 = s_s0[s], nbs = s_nb[s];
     const int b = item / Hkv, kvh = item % Hkv;
     const int64_t head0 = int64_t(b) * a.num_q_heads + int64_t(kvh) * g;
-    const bool cross_start = s0 < R0, cross_end = s0 + nbs > R1;
-    if (!cross_start && !cross_end) {
+    // this CU's share of a crossing item goes to slot 0 when the item begins
+    // at or before the range start, else slot 1
+    const int64_t slot = int64_t(wg) * 2 + (s0 <= R0 ? 0 : 1);
+    bool bad = false;
+#pragma unroll 1
+    for (int k0 = 0; k0 < nk; k0 += 8) {
+      float acc[8], M[8], den[8];
 #pragma unroll
-      for (int k = 0; k < NKMAX; ++k)
-        if (k < nk) a.out[head0 * D + 64 * k + lane] = bad ? __builtin_nanf("") : acc[k] / den[k] * a.out_scale;
-    } else {
-      // this CU's share of a sequence that crosses its range: slot 0 when
-      // the sequence begins at or before the range start, else slot 1
-      const int64_t slot = int64_t(wg) * 2 + (s0 <= R0 ? 0 : 1);
+      for (int u = 0; u < 8; ++u) {
+        acc[u] = 0.f;
+        M[u] = -INFINITY;
+        den[u] = 0.f;
+      }
+#pragma unroll 1
+      for (int c = 0; c < 3; ++c) {
+        uint64_t mk = msk[c];
+        while (mk) {
+          const int j = c0 + 64 * c + static_cast<int>(__builtin_ctzll(mk));
+          mk &= mk - 1;
+          float mj[8], lj[8], oj[8];
 #pragma unroll
-      for (int k = 0; k < NKMAX; ++k) {
+          for (int u = 0; u < 8; ++u) {
+            const int k = k0 + u < nk ? k0 + u : nk - 1;
+            const int e = 64 * k + lane;
+            const int h = (64 * k) / D;
+            if (j < cap) {
+              mj[u] = s_m[j * g + h];
+              lj[u] = s_l[j * g + h];
+              oj[u] = s_o[j * g * D + e];
+            } else {
+              const float* base = o_base + (j - cap) * cu_state_floats(g, D);
+              mj[u] = base[h];
+              lj[u] = base[g + h];
+              oj[u] = base[2 * g + e];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            bad |= (mj[u] != mj[u]);
+            const float mn = fmaxf(M[u], mj[u]);
+            const float fo = __builtin_amdgcn_exp2f(M[u] - mn);
+            const float fn = __builtin_amdgcn_exp2f(mj[u] - mn);
+            acc[u] = acc[u] * fo + oj[u] * fn;
+            den[u] = den[u] * fo + lj[u] * fn;
+            M[u] = mn;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u;
         if (k < nk) {
           const int e = 64 * k + lane;
           const int h = (64 * k) / D;
-          __hip_atomic_store(a.bw_o + slot * g * D + e, acc[k], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-          if ((e % D) == 0) {
-            __hip_atomic_store(a.bw_m + slot * g + h, bad ? __builtin_nanf("") : M[k],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.bw_l + slot * g + h, den[k], __ATOMIC_RELAXED,
+          if (!crossing) {
+            a.out[head0 * D + e] = bad ? __builtin_nanf("") : acc[u] / den[u] * a.out_scale;
+          } else {
+            __hip_atomic_store(a.bw_o + slot * g * D + e, acc[u], __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
+            if ((e % D) == 0) {
+              __hip_atomic_store(a.bw_m + slot * g + h, bad ? __builtin_nanf("") : M[u],
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(a.bw_l + slot * g + h, den[u], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
         }
       }
-      // once the stores have completed, count this CU's arrival
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      // arrival: the CU that brings the count to the number of CU ranges
-      // covering the sequence merges their partial states
-      const int w0 = s0 / pc, w1 = (s0 + nbs - 1) / pc;
-      const unsigned need = static_cast<unsigned>(w1 - w0 + 1);
-      unsigned arrived = 0;
-      if (lane == 0) {
-        unsigned long long* cp = a.bw_count + item;
-        unsigned long long old = __hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        unsigned long long nv = 0;
-        for (int tries = 0; tries < (1 << 20); ++tries) {
-          nv = (unsigned(old >> 32) == a.epoch)
-                   ? old + 1
-                   : ((static_cast<unsigned long long>(a.epoch) << 32) | 1ull);
-          if (__hip_atomic_compare_exchange_weak(cp, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT))
-            break;
-        }
-        arrived = static_cast<unsigned>(nv);
+    }
+    if (!crossing) continue;
+    // once the stores have completed, count this CU's arrival
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // arrival: the CU that brings the count to the number of CU ranges
+    // covering the sequence merges their partial states
+    const int w0 = s0 / pc, w1 = (s0 + nbs - 1) / pc;
+    const unsigned need = static_cast<unsigned>(w1 - w0 + 1);
+    unsigned arrived = 0;
+    if (lane == 0) {
+      unsigned long long* cp = a.bw_count + item;
+      unsigned long long old = __hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned long long nv = 0;
+      for (int tries = 0; tries < (1 << 20); ++tries) {
+        nv = (unsigned(old >> 32) == a.epoch)
+                 ? old + 1
+                 : ((static_cast<unsigned long long>(a.epoch) << 32) | 1ull);
+        if (__hip_atomic_compare_exchange_weak(cp, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+          break;
       }
-      arrived = __builtin_amdgcn_readlane(arrived, 0);
-      if (arrived != need) continue;
-      __asm__ volatile("" ::: "memory");
-      float gacc[NKMAX], gM[NKMAX], gden[NKMAX];
+      arrived = static_cast<unsigned>(nv);
+    }
+    arrived = __builtin_amdgcn_readlane(arrived, 0);
+    if (arrived != need) continue;
+    __asm__ volatile("" ::: "memory");
+    // merge every CU's share (this one's included, read back like the
+    // others): each partner's 8 elements of a group in one round of loads
+    bool gbad = false;
+#pragma unroll 1
+    for (int k0 = 0; k0 < nk; k0 += 8) {
+      float acc[8], M[8], den[8];
 #pragma unroll
-      for (int k = 0; k < NKMAX; ++k) {
-        gacc[k] = 0.f;
-        gM[k] = -INFINITY;
-        gden[k] = 0.f;
+      for (int u = 0; u < 8; ++u) {
+        acc[u] = 0.f;
+        M[u] = -INFINITY;
+        den[u] = 0.f;
       }
-      bool gbad = false;
+#pragma unroll 1
       for (int w = w0; w <= w1; ++w) {
-        const int64_t gs = int64_t(w) * 2 + ((w == w0 && int64_t(w0) * pc < s0) ? 1 : 0);
+        const int gs = w * 2 + ((w == w0 && int64_t(w0) * pc < s0) ? 1 : 0);
+        float mj[8], lj[8], oj[8];
 #pragma unroll
-        for (int k = 0; k < NKMAX; ++k) {
-          if (k < nk) {
-            const int e = 64 * k + lane;
-            const int h = (64 * k) / D;
-            const float mj = __hip_atomic_load(a.bw_m + gs * g + h, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-            const float lj = __hip_atomic_load(a.bw_l + gs * g + h, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-            const float oj = __hip_atomic_load(a.bw_o + gs * g * D + e, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-            gbad |= (mj != mj);
-            const float mn = fmaxf(gM[k], mj);
-            const float fo = __builtin_amdgcn_exp2f(gM[k] - mn);
-            const float fn = __builtin_amdgcn_exp2f(mj - mn);
-            gacc[k] = gacc[k] * fo + oj * fn;
-            gden[k] = gden[k] * fo + lj * fn;
-            gM[k] = mn;
-          }
+        for (int u = 0; u < 8; ++u) {
+          const int k = k0 + u < nk ? k0 + u : nk - 1;
+          const int e = 64 * k + lane;
+          const int h = (64 * k) / D;
+          oj[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_bo, (gs * g * D + e) * 4, 0, kSc1));
+          mj[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_bm, (gs * g + h) * 4, 0, kSc1));
+          lj[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_bl, (gs * g + h) * 4, 0, kSc1));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          gbad |= (mj[u] != mj[u]);
+          const float mn = fmaxf(M[u], mj[u]);
+          const float fo = __builtin_amdgcn_exp2f(M[u] - mn);
+          const float fn = __builtin_amdgcn_exp2f(mj[u] - mn);
+          acc[u] = acc[u] * fo + oj[u] * fn;
+          den[u] = den[u] * fo + lj[u] * fn;
+          M[u] = mn;
         }
       }
 #pragma unroll
-      for (int k = 0; k < NKMAX; ++k)
-        if (k < nk)
-          a.out[head0 * D + 64 * k + lane] = gbad ? __builtin_nanf("") : gacc[k] / gden[k] * a.out_scale;
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < nk)
+          a.out[head0 * D + 64 * (k0 + u) + lane] = gbad ? __builtin_nanf("") : acc[u] / den[u] * a.out_scale;
     }
   }
 }
