@@ -1802,14 +1802,34 @@ void prefill_bf16_kernel(PrefillArgs a) {
   for (int t = 0; t < NQ; ++t)
 #pragma unroll
     for (int k = 0; k < NT; ++k) o[t][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // running max per column (log2 domain; a finite floor, so that a column
-  // with nothing visible yet gets weights exp2(-inf - floor) = 0) and this
-  // lane's share of the normaliser
-  float m[NQ], lsum[NQ];
+  // running max per column (log2 domain, scaled; a finite floor, so that a
+  // column with nothing visible yet gets weights exp2(-inf - floor) = 0),
+  // and the normalisers: row sums of the same bf16 weight parts that P.V
+  // uses, formed by the matrix cores (P times a column of ones) in the
+  // output layout, so numerator and denominator share every rounding
+  float m[NQ];
+  f32x4 lacc[NQ];
 #pragma unroll
   for (int t = 0; t < NQ; ++t) {
     m[t] = -1e30f;
-    lsum[t] = 0.f;
+    lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  // weights exp2(cs * s - m) with cs >= 0: a negative scale negates Q
+  // instead (exact in bf16), so the scaled max is the raw max times cs
+  const float cs = fabsf(a.scale_log2e);
+  if (a.scale_log2e < 0.f) {
+#pragma unroll
+    for (int t = 0; t < NQ; ++t)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        uint4 x = __builtin_bit_cast(uint4, qf[t][j]);
+        x.x ^= 0x80008000u;
+        x.y ^= 0x80008000u;
+        x.z ^= 0x80008000u;
+        x.w ^= 0x80008000u;
+        qf[t][j] = __builtin_bit_cast(bf16x8, x);
+      }
   }
 
   // weights of the stage being processed (bf16 high parts and residuals)
@@ -1833,6 +1853,13 @@ void prefill_bf16_kernel(PrefillArgs a) {
         o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vhi, o[t][2 * j + 1], 0, 0, 0);
         o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vhi, o[t][2 * j + 1], 0, 0, 0);
       }
+    }
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) {
+      const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(phi[t][0], phi[t][1], phi[t][2], phi[t][3]));
+      const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(plo[t][0], plo[t][1], plo[t][2], plo[t][3]));
+      lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ones, lacc[t], 0, 0, 0);
+      lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, ones, lacc[t], 0, 0, 0);
     }
   };
 
@@ -1861,11 +1888,12 @@ void prefill_bf16_kernel(PrefillArgs a) {
     const bool edge = tb0 + 2 * kBlock - 1 > p_first || (WIN && tb0 < p_last - a.window + 1);
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
+      // raw scores; masked ones become -inf (exp2 of them is 0)
       float sv[8];
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sv[4 * bb + r] = sc[t][bb][r] * a.scale_log2e;
+        for (int r = 0; r < 4; ++r) sv[4 * bb + r] = sc[t][bb][r];
       if (edge) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -1875,25 +1903,32 @@ void prefill_bf16_kernel(PrefillArgs a) {
       }
       float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                          fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      mloc = group_max(mloc);
+      mloc = group_max(mloc) * cs;
       // lazy max: raise it only when the stage max exceeds it by 2^8
       const bool raise = mloc > m[t] + kPfRescale;
       if (__builtin_amdgcn_ballot_w64(raise)) {
         const float alpha = raise ? __builtin_amdgcn_exp2f(m[t] - mloc) : 1.0f;
         m[t] = raise ? mloc : m[t];
-        lsum[t] *= alpha;
         // output rows are columns 4 grp + r of the tile; their factors sit in lanes 4 grp + r
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float ar = __shfl(alpha, grp * 4 + r);
+          lacc[t][r] *= ar;
 #pragma unroll
           for (int k = 0; k < NT; ++k) o[t][k][r] *= ar;
         }
       }
+      // (a column's masked scores are -inf, its unmasked ones finite: the
+      // fma gives -inf or a finite value for any cs >= 0 except cs = 0,
+      // where -inf * 0 is NaN; masks therefore select 0 after exp2)
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] - m[t]);
-      lsum[t] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], cs, -m[t]));
+      if (edge) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (sv[e] == -INFINITY) p[e] = 0.f;
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bf16x2 h = __builtin_convertvector((f32x2{p[2 * e], p[2 * e + 1]}), bf16x2);
@@ -1925,12 +1960,11 @@ void prefill_bf16_kernel(PrefillArgs a) {
 
 #pragma unroll
   for (int t = 0; t < NQ; ++t) {
-    const float lt = group_sum(lsum[t]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int cl = grp * 4 + r;  // output row = column of the tile
       const int c = (NQ * wave + t) * 16 + cl;
-      const float inv = bad ? __builtin_nanf("") : 1.0f / __shfl(lt, cl);
+      const float inv = bad ? __builtin_nanf("") : 1.0f / lacc[t][r];
       if (c < ncol) {
         float* dst = out_row(c) + hcol;
 #pragma unroll
