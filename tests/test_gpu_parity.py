@@ -730,3 +730,88 @@ def test_prefill_full_size_sampled():
                 err = max(err, float(np.max(np.abs(out[r, h] - exp))))
     print(f"[prefill full size] sampled max abs err {err:.2e}", flush=True)
     assert err <= 2e-3
+
+
+def test_swap_after_window_release():
+    """Sliding window and swap together: blocks before each window are
+    released (table entries -1), some sequences are swapped out (only their
+    live blocks move), every free device block is overwritten, they come back,
+    and windowed decode matches the oracle, which did the same on its pools."""
+    from oracle import attention as oatt
+    from oracle import cache as ocache
+    from oracle import preempt
+    from oracle.pool import PoolModel
+    from paged_kv_cache_102_amd import _capi as capi
+    W = 40
+    w = synth.small_random(950, num_seqs=6, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                           dtype="bf16", max_len=300, fixed=[0, 1, 39, 40, 41, 299])
+    p = _pair(w)
+    p.kv.window = W
+    _release_both(p, W, p.ora.lens, p.kv.lens)
+    s = w.spec
+    NH = 40
+    p.kv.enable_swap(NH)
+    hpool = PoolModel(NH)
+    hcache = ocache.CacheModel(NH, s.num_kv_heads, s.head_dim, "bf16")
+    out_seqs = [3, 5, 1]
+    rows = {b: p.ora.tables[b, :-(-int(p.ora.lens[b]) // 16)].copy() for b in out_seqs}
+    ids = [int(x) for b in out_seqs for x in rows[b] if x >= 0]
+    new_m, pairs_m = preempt.swap(p.ora.pool, hpool, ids)
+    p.ora.cache.copy_blocks_to(hcache, pairs_m)
+    lens_out = {b: int(p.ora.lens[b]) for b in out_seqs}
+    pairs_c = p.kv.swap_out(out_seqs)
+    assert pairs_c.tolist() == [list(x) for x in pairs_m]
+    k = 0
+    htab = {}
+    for b in out_seqs:
+        h = np.full(p.ora.tables.shape[1], -1, np.int32)
+        live = np.nonzero(rows[b] >= 0)[0]
+        h[live] = new_m[k:k + len(live)]
+        k += len(live)
+        htab[b] = h
+        p.ora.tables[b] = -1
+        p.ora.lens[b] = 0
+    free = capi.kv_pool_free_list(p.kv.pool).tolist()
+    p.kv.k_cache.view(w.num_blocks, -1)[free] = float("nan")
+    p.kv.v_cache.view(w.num_blocks, -1)[free] = float("nan")
+    p.ora.cache.k[free] = np.uint16(0x7FC0)
+    p.ora.cache.v[free] = np.uint16(0x7FC0)
+    back = [1, 3, 5]
+    hids = [int(x) for b in back for x in htab[b] if x >= 0]
+    new2, pairs2 = preempt.swap(hpool, p.ora.pool, hids)
+    hcache.copy_blocks_to(p.ora.cache, pairs2)
+    k = 0
+    for b in back:
+        live = np.nonzero(htab[b] >= 0)[0]
+        p.ora.tables[b] = -1
+        p.ora.tables[b, live] = new2[k:k + len(live)]
+        p.ora.lens[b] = lens_out[b]
+        k += len(live)
+    p.kv.swap_in(back)
+    p.check_state()
+    out = p.kv.decode(p.q, s.scale).cpu().numpy().astype(np.float64)
+    exp = oatt.decode(w.q, p.ora.cache, p.ora.tables, p.ora.lens, s.num_q_heads, s.num_kv_heads,
+                      s.scale, window=W)
+    err = float(np.max(np.abs(out - exp)))
+    print(f"[swap + window] {len(pairs_m)} blocks out and back, max abs err {err:.2e}", flush=True)
+    assert np.isfinite(out).all() and err <= 2e-3
+
+
+def test_swap_copy_argument_errors():
+    from paged_kv_cache_102_amd import _capi as capi
+    c = torch.zeros(4 * 2 * 16 * 128, dtype=torch.bfloat16, device="cuda")
+    h = torch.zeros(4 * 2 * 16 * 128, dtype=torch.bfloat16, pin_memory=True)
+    pairs = torch.tensor([[0, 1]], dtype=torch.int32, device="cuda")
+    with pytest.raises(capi.PkvError):          # source and destination the same buffers
+        capi.paged_kv_swap_blocks(c, c, c, c, pairs, 2, 128, 4, 4)
+    with pytest.raises(capi.PkvError):          # head_dim not a multiple of 32
+        capi.paged_kv_swap_blocks(c, c, h, h, pairs, 2, 48, 4, 4)
+    with pytest.raises(ValueError):             # dtypes differ
+        capi.paged_kv_swap_blocks(c, c, h.view(torch.int16).to(torch.float16), h, pairs, 2, 128, 4, 4)
+    # out-of-range pairs are skipped: the destination keeps its bytes
+    h.fill_(3.0)
+    h2 = torch.full_like(h, 3.0).pin_memory()
+    bad = torch.tensor([[7, 0], [0, 9]], dtype=torch.int32, device="cuda")
+    capi.paged_kv_swap_blocks(c, c.clone(), h, h2, bad, 2, 128, 4, 4)
+    torch.cuda.synchronize()
+    assert bool((h == 3.0).all()) and bool((h2 == 3.0).all())
