@@ -309,13 +309,24 @@ pkv_status paged_kv_append_slots(pkv_pool* pool, int32_t num_seqs, int32_t max_b
                                  int32_t update_capacity, int32_t* num_updates,
                                  int32_t* cow_pairs, int32_t cow_capacity, int32_t* num_cow);
 
-/* ===== Device calls ========================================================= */
+/* ===== Device calls =========================================================
+ * The small index inputs of the cache-update calls below (slot_mapping,
+ * table updates, block pairs) may be in device memory or in pinned host
+ * memory (hipHostMalloc or any other device-accessible host allocation).  The
+ * kernels read them with system-scope loads, which are never served from a
+ * stale cached copy, so a caller may refill one pinned buffer for every step
+ * once the stream has passed the call that read it (an event recorded
+ * after the call and waited on before the refill).  A step then needs no
+ * separate upload. */
 
 /* The block tables live in device memory next to the cache, not on the host
  * [P5 "La tabla de paginas": a host-side table would cost a PCIe round trip
- * per decode step].  Applies `updates` (device int32 [num_updates][2] of
+ * per decode step].  Applies `updates` (int32 [num_updates][2] of
  * (flat index, block id)) to block_tables (device int32 [table_elems]).
- * Pairs whose index is outside [0, table_elems) are skipped. */
+ * Pairs whose index is outside [0, table_elems) are skipped.  Any flat int32
+ * device array works: with the context lengths stored right after the
+ * tables ([num_seqs][max_blocks] then [num_seqs]), a step's new lengths
+ * travel as pairs (num_seqs * max_blocks + s, length) in the same launch. */
 pkv_status paged_block_table_update(int32_t* block_tables, int64_t table_elems,
                                     const int32_t* updates, int32_t num_updates,
                                     hipStream_t stream);
@@ -330,7 +341,7 @@ pkv_status paged_block_table_update(int32_t* block_tables, int64_t table_elems,
  * PKV_ERR_INVALID when the environment variable PKV_DEBUG=1, which also
  * checks uniqueness; that check synchronizes the stream).  Slots must be
  * unique: two rows for one slot race.  Bytes are copied unchanged.
- * k_new, v_new, slot_mapping, k_cache, v_cache: device. */
+ * k_new, v_new, k_cache, v_cache: device; slot_mapping: device or pinned host. */
 pkv_status paged_kv_write(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                           void* k_cache, void* v_cache, int32_t num_tokens,
                           int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
@@ -350,7 +361,8 @@ pkv_status paged_kv_append(const void* k_new, const void* v_new, const int64_t* 
 
 /* Copy whole blocks (all kv heads, all 16 slots, K and V) for copy-on-write
  * [P5 "Copy-on-write para sampling paralelo": only the last affected block
- * is copied].  pairs: device int32 [num_pairs][2] = (src block, dst block).
+ * is copied].  pairs: int32 [num_pairs][2] = (src block, dst block), device
+ * or pinned host memory.
  * Pairs with an id outside [0, num_blocks) are skipped.  Destinations must
  * be distinct and must not be sources of other pairs in the same call.
  * Enqueue before paged_kv_write on the same stream so the copy sees the
@@ -444,7 +456,7 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
  * code, ties to the even mantissa; magnitudes from 448 up clamp to 448, NaN
  * gives 0x7F with the input's sign.  k_cache / v_cache hold uint8 codes in
  * the FP8 tile order above.  Scales must be positive and finite, else
- * PKV_ERR_INVALID; other errors as paged_kv_write. */
+ * PKV_ERR_INVALID; argument placement and other errors as paged_kv_write. */
 pkv_status paged_kv_write_fp8(const void* k_new, const void* v_new, pkv_dtype src_dtype,
                               const int64_t* slot_mapping, void* k_cache, void* v_cache,
                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,

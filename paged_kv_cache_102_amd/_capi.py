@@ -306,7 +306,7 @@ def paged_block_table_update(block_tables, updates, stream=None) -> None:
     if n == 0:
         return
     _check(_lib.paged_block_table_update(_dev(block_tables, "block_tables"), block_tables.numel(),
-                                         _dev(updates, "updates"), n, _stream(stream)),
+                                         _dev_or_pinned(updates, "updates"), n, _stream(stream)),
            "paged_block_table_update")
 
 
@@ -316,9 +316,10 @@ def paged_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache, num_kv_heads: i
     if n == 0:
         return
     _check(_lib.paged_kv_write(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
-                               _dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"),
-                               _dev(v_cache, "v_cache"), n, num_kv_heads, head_dim, num_blocks,
-                               _dtype_code(k_cache), _stream(stream)), "paged_kv_write")
+                               _dev_or_pinned(slot_mapping, "slot_mapping"),
+                               _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), n,
+                               num_kv_heads, head_dim, num_blocks, _dtype_code(k_cache),
+                               _stream(stream)), "paged_kv_write")
 
 
 def paged_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, num_kv_heads: int,
@@ -328,11 +329,12 @@ def paged_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, num_kv_heads: 
     if n == 0 and nu == 0:
         return
     _check(_lib.paged_kv_append(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
-                                _dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"),
-                                _dev(v_cache, "v_cache"), n, num_kv_heads, head_dim, num_blocks,
-                                _dtype_code(k_cache), _dev(block_tables, "block_tables"),
-                                block_tables.numel(), _dev(updates, "updates") if nu else None,
-                                nu, _stream(stream)), "paged_kv_append")
+                                _dev_or_pinned(slot_mapping, "slot_mapping"),
+                                _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), n,
+                                num_kv_heads, head_dim, num_blocks, _dtype_code(k_cache),
+                                _dev(block_tables, "block_tables"), block_tables.numel(),
+                                _dev_or_pinned(updates, "updates") if nu else None, nu,
+                                _stream(stream)), "paged_kv_append")
 
 
 def paged_kv_copy_blocks(k_cache, v_cache, pairs, num_kv_heads: int, head_dim: int,
@@ -341,8 +343,8 @@ def paged_kv_copy_blocks(k_cache, v_cache, pairs, num_kv_heads: int, head_dim: i
     if n == 0:
         return
     _check(_lib.paged_kv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-                                     _dev(pairs, "pairs"), n, num_kv_heads, head_dim, num_blocks,
-                                     _dtype_code(k_cache), _stream(stream)),
+                                     _dev_or_pinned(pairs, "pairs"), n, num_kv_heads, head_dim,
+                                     num_blocks, _dtype_code(k_cache), _stream(stream)),
            "paged_kv_copy_blocks")
 
 
@@ -411,9 +413,10 @@ def paged_kv_write_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, num_kv_head
     if n == 0:
         return
     _check(_lib.paged_kv_write_fp8(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new),
-                                   _dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"),
-                                   _dev(v_cache, "v_cache"), n, num_kv_heads, head_dim, num_blocks,
-                                   k_scale, v_scale, _stream(stream)), "paged_kv_write_fp8")
+                                   _dev_or_pinned(slot_mapping, "slot_mapping"),
+                                   _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), n,
+                                   num_kv_heads, head_dim, num_blocks, k_scale, v_scale,
+                                   _stream(stream)), "paged_kv_write_fp8")
 
 
 def paged_attention_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, out, *,

@@ -88,13 +88,25 @@ __device__ inline uint32_t bf16_bits_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Small index inputs of the cache-update kernels (slots, table deltas, block
+// pairs) may sit in pinned host memory that the host refills between
+// launches.  System-scope loads are never served from a cached copy, so a
+// refilled buffer is seen as the host wrote it; within a wave, lanes reading
+// the same word share one request.
+__device__ inline int64_t ld_sys(const int64_t* p) {
+  return __hip_atomic_load(const_cast<int64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ inline int32_t ld_sys(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // ------------------------------------------------------------------ A2: table deltas
 __global__ void table_update_kernel(int32_t* __restrict__ tables, int64_t elems,
                                     const int32_t* __restrict__ upd, int n) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  int64_t idx = upd[2 * i];
-  if (idx >= 0 && idx < elems) tables[idx] = upd[2 * i + 1];
+  const int64_t idx = ld_sys(upd + 2 * i);
+  if (idx >= 0 && idx < elems) tables[idx] = ld_sys(upd + 2 * i + 1);
 }
 
 // ------------------------------------------------------------------ A3: cache write
@@ -111,7 +123,7 @@ __global__ void kv_write_kernel(const T* __restrict__ k_new, const T* __restrict
   const int64_t ih = idx / chunks;
   const int h = static_cast<int>(ih % num_kv_heads);
   const int64_t i = ih / num_kv_heads;
-  const int64_t slot = slots[i];
+  const int64_t slot = ld_sys(slots + i);
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot >> 4;
   const int t = static_cast<int>(slot & 15);
@@ -132,7 +144,7 @@ __global__ void kv_write_kernel(const T* __restrict__ k_new, const T* __restrict
 
 // ------------------------------------------------------------------ A2 + A3 fused
 // Workgroups [0, table_wgs) apply table deltas; the rest scatter K/V rows
-// exactly as kv_write_kernel does.
+// to the same places as kv_write_kernel, with streaming stores.
 template <typename T>
 __global__ void append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
                               const int64_t* __restrict__ slots, T* __restrict__ kc,
@@ -142,8 +154,8 @@ __global__ void append_kernel(const T* __restrict__ k_new, const T* __restrict__
   if (static_cast<int>(blockIdx.x) < table_wgs) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n_upd) {
-      const int64_t idx = upd[2 * i];
-      if (idx >= 0 && idx < elems) tables[idx] = upd[2 * i + 1];
+      const int64_t idx = ld_sys(upd + 2 * i);
+      if (idx >= 0 && idx < elems) tables[idx] = ld_sys(upd + 2 * i + 1);
     }
     return;
   }
@@ -154,7 +166,7 @@ __global__ void append_kernel(const T* __restrict__ k_new, const T* __restrict__
   const int64_t ih = idx / chunks;
   const int h = static_cast<int>(ih % num_kv_heads);
   const int64_t i = ih / num_kv_heads;
-  const int64_t slot = slots[i];
+  const int64_t slot = ld_sys(slots + i);
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot >> 4;
   const int t = static_cast<int>(slot & 15);
@@ -166,10 +178,14 @@ __global__ void append_kernel(const T* __restrict__ k_new, const T* __restrict__
     kv[e] = k_new[src + e];
     vv[e] = v_new[src + e];
   }
+  // Streaming stores: the rows are read again only by the next launch, and
+  // lines left dirty in the L2 of each XCD slow that launch's start.
 #pragma unroll
-  for (int e = 0; e < 8; ++e) kc[tile + k_elem(t, c * 8 + e)] = kv[e];
+  for (int e = 0; e < 8; ++e)
+    __builtin_nontemporal_store(kv[e], &kc[tile + k_elem(t, c * 8 + e)]);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) vc[tile + v_elem(t, c * 8 + e)] = vv[e];
+  for (int e = 0; e < 8; ++e)
+    __builtin_nontemporal_store(vv[e], &vc[tile + v_elem(t, c * 8 + e)]);
 }
 
 // ------------------------------------------------------------------ A4: block copies
@@ -178,8 +194,8 @@ __global__ void append_kernel(const T* __restrict__ k_new, const T* __restrict__
 __global__ void copy_blocks_kernel(uint4* __restrict__ kc, uint4* __restrict__ vc,
                                    const int32_t* __restrict__ pairs, int64_t run16,
                                    int num_blocks) {
-  const int32_t src = pairs[2 * blockIdx.x];
-  const int32_t dst = pairs[2 * blockIdx.x + 1];
+  const int32_t src = ld_sys(pairs + 2 * blockIdx.x);
+  const int32_t dst = ld_sys(pairs + 2 * blockIdx.x + 1);
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
   uint4* base = blockIdx.y ? vc : kc;
   const uint4* s = base + int64_t(src) * run16;
@@ -198,8 +214,8 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(
     const uint4* __restrict__ sk, const uint4* __restrict__ sv, uint4* __restrict__ dk,
     uint4* __restrict__ dv, const int32_t* __restrict__ pairs, int64_t run16, int src_blocks,
     int dst_blocks) {
-  const int32_t src = pairs[2 * blockIdx.x];
-  const int32_t dst = pairs[2 * blockIdx.x + 1];
+  const int32_t src = ld_sys(pairs + 2 * blockIdx.x);
+  const int32_t dst = ld_sys(pairs + 2 * blockIdx.x + 1);
   if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
   const uint4* s = (blockIdx.y ? sv : sk) + int64_t(src) * run16;
   uint4* d = (blockIdx.y ? dv : dk) + int64_t(dst) * run16;
@@ -983,7 +999,7 @@ __global__ void kv_write_fp8_kernel(const T* __restrict__ k_new, const T* __rest
   const int64_t ih = idx / chunks;
   const int h = static_cast<int>(ih % num_kv_heads);
   const int64_t i = ih / num_kv_heads;
-  const int64_t slot = slots[i];
+  const int64_t slot = ld_sys(slots + i);
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot >> 4;
   const int t = static_cast<int>(slot & 15);

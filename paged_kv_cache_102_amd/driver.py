@@ -30,48 +30,71 @@ BLOCK = capi.BLOCK_SIZE
 
 
 class _Staging:
-    """A ring of pinned host buffers so that uploads stay asynchronous.
+    """A ring of pinned host buffers for each step's small inputs (slots,
+    table and length deltas, block pairs).  The kernels read them in place
+    over the host link (system-scope loads), so a step needs no copy launch
+    and no second stream.  A buffer is refilled only once an event recorded
+    behind its last reader has completed.  Recording an event puts a marker
+    with a system-wide release between two kernels (several microseconds),
+    so one event is recorded per ``every`` releases and covers all buffers
+    released since the previous one (the stream runs in order)."""
 
-    The copy runs on its own stream (default priority): a step's slots,
-    table deltas and lengths depend only on the host plan, not on the
-    previous step's attention, so their upload overlaps the previous decode
-    and the compute stream only waits on the copy's event."""
-
-    def __init__(self, nbytes: int, device, depth: int = 4):
+    def __init__(self, nbytes: int, depth: int = 8, every: int = 4):
+        assert 0 < every < depth
         self.bufs = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(depth)]
         self.events = [None] * depth
+        self.every = every
+        self.pending = []      # released buffers no event covers yet
+        self.stream = None     # stream of the last release
         self.i = 0
-        self.copy_stream = torch.cuda.Stream(device)
+        self.cur = None
 
-    def put(self, arrays, device, stream):
+    def _cover(self):
+        ev = torch.cuda.Event()
+        ev.record(self.stream)
+        for k in self.pending:
+            self.events[k] = ev
+        self.pending = []
+
+    def put(self, arrays):
         """Packs numpy arrays (8-byte aligned pieces) into the next pinned
-        buffer and copies them to ``device``; returns device views that
-        ``stream`` may use (it waits for the copy)."""
+        buffer and returns pinned tensor views of them; ``release`` must
+        follow once their readers are enqueued."""
         k = self.i
-        self.i = (self.i + 1) % len(self.bufs)
+        self.i = (k + 1) % len(self.bufs)
+        if k in self.pending:
+            self._cover()
         if self.events[k] is not None:
             self.events[k].synchronize()
+            self.events[k] = None
         buf = self.bufs[k]
         host = buf.numpy()
-        offs, off = [], 0
+        views, off = [], 0
         for a in arrays:
-            offs.append(off)
             n = a.nbytes
             host[off:off + n] = np.ascontiguousarray(a).view(np.uint8).ravel()
-            off += (n + 7) & ~7
-        with torch.cuda.stream(self.copy_stream):
-            dev = buf[:max(off, 8)].to(device, non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record(self.copy_stream)
-        dev.record_stream(stream)
-        stream.wait_event(ev)
-        self.events[k] = ev
-        views = []
-        for a, o in zip(arrays, offs):
-            t = dev[o:o + a.nbytes]
             dt = {np.dtype(np.int64): torch.int64, np.dtype(np.int32): torch.int32}[a.dtype]
-            views.append(t.view(dt).view(*a.shape) if a.size else t.view(dt))
+            t = buf[off:off + n].view(dt)
+            views.append(t.view(*a.shape) if a.size else t)
+            off += (n + 7) & ~7
+        self.cur = k
         return views
+
+    def release(self, stream):
+        """The last ``put`` buffer is free once ``stream`` passes this point."""
+        if self.stream is not None and stream != self.stream and self.pending:
+            self._cover()
+        self.stream = stream
+        self.pending.append(self.cur)
+        if len(self.pending) >= self.every:
+            self._cover()
+
+    def drain(self):
+        if self.pending:
+            self._cover()
+        for ev in self.events:
+            if ev is not None:
+                ev.synchronize()
 
 
 class PagedKV:
@@ -105,8 +128,16 @@ class PagedKV:
             self.v_cache.fill_(fill)
         self.tables = np.full((num_seqs, max_blocks_per_seq), -1, dtype=np.int32)
         self.lens = np.zeros(num_seqs, dtype=np.int32)
-        self.tables_d = torch.from_numpy(self.tables).to(self.device)
-        self.lens_d = torch.from_numpy(self.lens).to(self.device)
+        # device tables and lengths share one int32 buffer, so that a step's
+        # length changes travel as table deltas at flat index S*mb + s
+        nt = num_seqs * max_blocks_per_seq
+        if nt + num_seqs >= 2 ** 31:
+            raise ValueError("num_seqs * (max_blocks_per_seq + 1) must be < 2^31")
+        self.state_d = torch.empty(nt + num_seqs, dtype=torch.int32, device=self.device)
+        self.tables_d = self.state_d[:nt].view(num_seqs, max_blocks_per_seq)
+        self.lens_d = self.state_d[nt:]
+        self.tables_d.copy_(torch.from_numpy(self.tables))
+        self.lens_d.copy_(torch.from_numpy(self.lens))
         ws = capi.paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                  max_blocks_per_seq * BLOCK, partition_size)
         self.workspace = torch.empty(max(ws // 4, 1), dtype=torch.float32, device=self.device)
@@ -116,11 +147,13 @@ class PagedKV:
         self.swapped = {}   # sequence -> (host table row, length)
 
     # ------------------------------------------------------------------ host helpers
-    def _upload(self, arrays, stream):
+    def _stage(self, arrays):
         need = sum((a.nbytes + 7) & ~7 for a in arrays) + 8
         if self._staging is None or self._staging.bufs[0].numel() < need:
-            self._staging = _Staging(max(need, 1 << 16), self.device)
-        return self._staging.put(arrays, self.device, stream)
+            if self._staging is not None:
+                self._staging.drain()  # pending kernels may still read the old ring
+            self._staging = _Staging(max(need, 1 << 16))
+        return self._staging.put(arrays)
 
     def share_prefix(self, src: int, dsts, num_blocks: int):
         """Sequences ``dsts`` take the first ``num_blocks`` blocks of ``src``
@@ -138,31 +171,37 @@ class PagedKV:
         """Appends tokens (k_new, v_new device [T][Hkv][D], rows in order of
         sequence) and returns (slots, table updates, cow pairs) as numpy."""
         stream = stream or torch.cuda.current_stream(self.device)
+        nn = np.ones_like(self.lens) if num_new is None else np.asarray(num_new, np.int32)
         rel = None
         if self.window > 0:
             # the earliest query still to run sees context length lens + 1
             # (a sequence with nothing to append: its current length)
-            nn = np.ones_like(self.lens) if num_new is None else np.asarray(num_new, np.int32)
             ctx = self.lens + (nn > 0).astype(np.int32)
             rel = capi.pkv_window_release(self.pool, self.tables, ctx, self.window)
         slots, upd, cows = capi.paged_kv_append_slots(self.pool, self.tables, self.lens, num_new)
         if rel is not None and len(rel):
             upd = np.concatenate([rel, upd]) if len(upd) else rel
-        d_slots, d_upd, d_cows, d_lens = self._upload([slots, upd, cows, self.lens], stream)
+        # new lengths of the sequences that grew, as deltas into the state buffer
+        grown = np.flatnonzero(nn)
+        lupd = np.empty((len(grown), 2), dtype=np.int32)
+        lupd[:, 0] = self.tables.size + grown
+        lupd[:, 1] = self.lens[grown]
+        h_slots, h_upd, h_cows = self._stage([slots, np.concatenate([upd, lupd]), cows])
         s = stream.cuda_stream
-        # the uploaded lengths become the device lengths (no extra copy)
-        self.lens_d = d_lens
-        capi.paged_kv_copy_blocks(self.k_cache, self.v_cache, d_cows, self.num_kv_heads,
-                                  self.head_dim, self.num_blocks, s)
-        if self.dtype == "fp8":
-            capi.paged_block_table_update(self.tables_d, d_upd, s)
-            capi.paged_kv_write_fp8(k_new, v_new, d_slots, self.k_cache, self.v_cache,
-                                    self.num_kv_heads, self.head_dim, self.num_blocks,
-                                    self.k_scale, self.v_scale, s)
-        else:
-            capi.paged_kv_append(k_new, v_new, d_slots, self.k_cache, self.v_cache,
-                                 self.num_kv_heads, self.head_dim, self.num_blocks, self.tables_d,
-                                 d_upd, s)
+        try:
+            capi.paged_kv_copy_blocks(self.k_cache, self.v_cache, h_cows, self.num_kv_heads,
+                                      self.head_dim, self.num_blocks, s)
+            if self.dtype == "fp8":
+                capi.paged_block_table_update(self.state_d, h_upd, s)
+                capi.paged_kv_write_fp8(k_new, v_new, h_slots, self.k_cache, self.v_cache,
+                                        self.num_kv_heads, self.head_dim, self.num_blocks,
+                                        self.k_scale, self.v_scale, s)
+            else:
+                capi.paged_kv_append(k_new, v_new, h_slots, self.k_cache, self.v_cache,
+                                     self.num_kv_heads, self.head_dim, self.num_blocks,
+                                     self.state_d, h_upd, s)
+        finally:
+            self._staging.release(stream)
         return slots, upd, cows
 
     def decode(self, q, scale: float, out=None, stream=None, partition_size=None):
@@ -295,9 +334,12 @@ class PagedKV:
     def _swap_copy(self, pairs, sk, sv, snb, dk, dv, dnb, stream):
         if len(pairs) == 0:
             return
-        (d_pairs,) = self._upload([np.ascontiguousarray(pairs, np.int32)], stream)
-        capi.paged_kv_swap_blocks(sk, sv, dk, dv, d_pairs, self.num_kv_heads, self.head_dim, snb,
-                                  dnb, stream.cuda_stream)
+        (h_pairs,) = self._stage([np.ascontiguousarray(pairs, np.int32)])
+        try:
+            capi.paged_kv_swap_blocks(sk, sv, dk, dv, h_pairs, self.num_kv_heads, self.head_dim,
+                                      snb, dnb, stream.cuda_stream)
+        finally:
+            self._staging.release(stream)
 
     def free_sequence(self, s: int):
         """Returns sequence s's blocks to the pool (one reference each)."""
