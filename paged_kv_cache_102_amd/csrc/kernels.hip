@@ -938,25 +938,23 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ FP8 E4M3 (OCP) codes
-// Decode: gfx950's v_cvt_pk_f32_fp8 expands two E4M3 codes to float32 (it
-// reads the OCP E4M3 encoding; its output matches the format's definition
-// for all 256 codes, NaN included, on MI355X).  Every E4M3 value has at most
-// 4 significant bits, so the upper 16 bits of the float32 are the exact
-// bf16.
-__device__ inline uint32_t bf16x2_of(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+// Decode: every E4M3 value has at most 4 significant bits and an exponent
+// inside bf16's range, so each code has an exact bf16.  gfx950's
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1 produces it for two codes in one
+// instruction; it reads the OCP E4M3 encoding, and on MI355X its output
+// equals the format's definition for all 256 codes (NaN codes give NaN).
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+template <bool HIGH>  // bytes 2, 3 of w when set, else bytes 0, 1
+__device__ inline uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
 }
 // 8 codes (bytes of lo then hi) -> 8 bf16 in the same order
 __device__ inline uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), false);  // bytes 0, 1
-  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), true);   // bytes 2, 3
-  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), false);
-  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), true);
   uint4 r;
-  r.x = bf16x2_of(a[0], a[1]);
-  r.y = bf16x2_of(b[0], b[1]);
-  r.z = bf16x2_of(c[0], c[1]);
-  r.w = bf16x2_of(d[0], d[1]);
+  r.x = e4m3x2_to_bf16x2<false>(lo);
+  r.y = e4m3x2_to_bf16x2<true>(lo);
+  r.z = e4m3x2_to_bf16x2<false>(hi);
+  r.w = e4m3x2_to_bf16x2<true>(hi);
   return r;
 }
 // Encode y (already divided by the tensor scale) as the nearest E4M3 code,
