@@ -82,10 +82,13 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-__device__ inline uint32_t bf16_bits_rne(float f) {
-  // round to nearest even; inputs here are finite and non-negative weights
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two weights as packed bf16 pairs: hi = the weights rounded to nearest even
+// (gfx950's packed conversion), lo = the rounded remainders, so hi + lo
+// carries each weight to about 16 significant bits.  Inputs are finite.
+__device__ inline void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+  const f32x2 rest = {a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
 }
 
 // Small index inputs of the cache-update kernels (slots, table deltas, block
@@ -409,14 +412,11 @@ void decode_bf16_kernel(DecodeArgs a) {
       }
     }
     // P as A operand (rows = heads hcol, k = tokens 4*grp+r), high + residual
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      hi[r] = bf16_bits_rne(p[r]);
-      lo[r] = bf16_bits_rne(p[r] - __uint_as_float(hi[r] << 16));
-    }
-    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
-    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
+    uint32_t hi01, lo01, hi23, lo23;
+    split_bf16x2(p[0], p[1], hi01, lo01);
+    split_bf16x2(p[2], p[3], hi23, lo23);
+    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi01, hi23));
+    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo01, lo23));
     if (t_begin + i * kBlock + kBlock > t_end || t_begin + i * kBlock < wlo) {
       // partial block: zero V of slots outside [wlo, t_end) (they may hold NaN)
       auto in = [&](int t) { return t < t_end && t >= wlo; };
@@ -793,14 +793,11 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
         for (int n = 0; n < NT; ++n) o[n][r] *= ar;
       }
     }
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      hi[r] = bf16_bits_rne(p[r]);
-      lo[r] = bf16_bits_rne(p[r] - __uint_as_float(hi[r] << 16));
-    }
-    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
-    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
+    uint32_t hi01, lo01, hi23, lo23;
+    split_bf16x2(p[0], p[1], hi01, lo01);
+    split_bf16x2(p[2], p[3], hi23, lo23);
+    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi01, hi23));
+    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo01, lo23));
     if ((c_first + c_blk) * kBlock + kBlock > c_L || (c_first + c_blk) * kBlock < wlo) {
       // zero V of slots outside [wlo, c_L) (they may hold NaN)
       auto in = [&](int t) { return t < c_L && t >= wlo; };
@@ -1386,14 +1383,11 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
         for (int n = 0; n < NT; ++n) o[n][r] *= ar;
       }
     }
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      hi[r] = bf16_bits_rne(p[r]);
-      lo[r] = bf16_bits_rne(p[r] - __uint_as_float(hi[r] << 16));
-    }
-    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
-    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
+    uint32_t hi01, lo01, hi23, lo23;
+    split_bf16x2(p[0], p[1], hi01, lo01);
+    split_bf16x2(p[2], p[3], hi23, lo23);
+    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi01, hi23));
+    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo01, lo23));
     if ((c_first + c_blk) * kBlock + kBlock > c_L || (c_first + c_blk) * kBlock < wlo) {
       // zero V of slots outside [wlo, c_L) (they may hold NaN)
       auto in = [&](int t) { return t < c_L && t >= wlo; };
@@ -1945,12 +1939,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bf16x2 h = __builtin_convertvector((f32x2{p[2 * e], p[2 * e + 1]}), bf16x2);
-        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-        const f32x2 rest = {p[2 * e] - __uint_as_float(hb << 16),
-                            p[2 * e + 1] - __uint_as_float(hb & 0xFFFF0000u)};
-        phi[t][e] = hb;
-        plo[t][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
+        split_bf16x2(p[2 * e], p[2 * e + 1], phi[t][e], plo[t][e]);
       }
     }
   };
