@@ -55,11 +55,16 @@
  * bf16) does not change the order.
  *
  * FP8 cache (PKV_FP8_E4M3, one byte per element, tile of 16 * D bytes).  The
- * bytes are in the same lane/piece order as the bf16 tile, so a lane's two
- * 16-byte loads expand to the bf16 operand pieces; with W = D / 4:
+ * codes of bf16 piece j of lane l (in the tile above: the 8 elements from
+ * 512 j + 8 l) form an 8-byte piece.  Pieces 2i and 2i + 1 of all 64 lanes
+ * fill bytes [1024 i, 1024 i + 1024), lane l's 16 bytes at 1024 i + 16 l, so
+ * one 16-byte load per lane reads 1 KiB in order and expands to two bf16
+ * operand pieces; a last piece without a partner (D / 32 odd) is stored as
+ * 64 lanes x 8 bytes at 1024 i + 8 l.  With
+ *   piece(l, j) = 1024 * (j / 2) + (j paired ? 16 : 8) * l + 8 * (j % 2):
  *
- *   K:  W * (16 * ((d / 8) % 4) + t) + 8 * (d / 32) + (d % 8)
- *   V:  W * (16 * (t / 4) + d % 16) + 8 * (d / 32) + ((d / 16) % 2) * 4 + (t % 4)
+ *   K:  piece(16 * ((d / 8) % 4) + t, d / 32) + (d % 8)
+ *   V:  piece(16 * (t / 4) + d % 16, d / 32) + ((d / 16) % 2) * 4 + (t % 4)
  *
  * A byte is an OCP FP8 E4M3 code (1 sign, 4 exponent bits with bias 7, 3
  * mantissa bits, subnormals m * 2^-9, no infinity, 0x7F/0xFF = NaN, largest

@@ -10,9 +10,13 @@ Written here again, independently, from that definition:
   K element (t, d): (d // 8) * 128 + t * 8 + d % 8
   V element (t, d): (d // 32) * 512 + (t // 4) * 128 + (d % 16) * 8
                     + ((d // 16) % 2) * 4 + t % 4
-  FP8 tiles (one byte per element), with W = D / 4 bytes per lane:
-  K byte (t, d): W * (16 * ((d // 8) % 4) + t) + 8 * (d // 32) + d % 8
-  V byte (t, d): W * (16 * (t // 4) + d % 16) + 8 * (d // 32)
+  FP8 tiles (one byte per element): the codes of lane l's bf16 piece j
+  (8 channels or 2 x 4 tokens) form an 8-byte piece; pieces 2i and 2i + 1 of
+  every lane make up bytes [1024 i, 1024 i + 1024) as 64 lanes x 16 bytes,
+  and a last piece without a partner (D / 32 odd) takes 64 lanes x 8 bytes:
+  piece(l, j) = 1024 * (j // 2) + (16 if paired else 8) * l + 8 * (j % 2)
+  K byte (t, d): piece(16 * ((d // 8) % 4) + t, d // 32) + d % 8
+  V byte (t, d): piece(16 * (t // 4) + d % 16, d // 32)
                  + ((d // 16) % 2) * 4 + t % 4
 """
 from __future__ import annotations
@@ -30,14 +34,17 @@ def v_offset(t: int, d: int) -> int:
     return (d // 32) * 512 + (t // 4) * 128 + (d % 16) * 8 + ((d // 16) % 2) * 4 + t % 4
 
 
+def _f8_piece(lane: int, piece: int, head_dim: int) -> int:
+    paired = 2 * (piece // 2) + 1 < head_dim // 32
+    return 1024 * (piece // 2) + (16 if paired else 8) * lane + 8 * (piece % 2)
+
+
 def k8_offset(t: int, d: int, head_dim: int) -> int:
-    w = head_dim // 4
-    return w * (16 * ((d // 8) % 4) + t) + 8 * (d // 32) + d % 8
+    return _f8_piece(16 * ((d // 8) % 4) + t, d // 32, head_dim) + d % 8
 
 
 def v8_offset(t: int, d: int, head_dim: int) -> int:
-    w = head_dim // 4
-    return w * (16 * (t // 4) + d % 16) + 8 * (d // 32) + ((d // 16) % 2) * 4 + t % 4
+    return _f8_piece(16 * (t // 4) + d % 16, d // 32, head_dim) + ((d // 16) % 2) * 4 + t % 4
 
 
 def tile_base(block: int, kv_head: int, num_kv_heads: int, head_dim: int) -> int:

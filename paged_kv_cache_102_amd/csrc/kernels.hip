@@ -954,6 +954,16 @@ __device__ inline uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   r.w = e4m3x2_to_bf16x2<true>(hi);
   return r;
 }
+// Byte offset in an FP8 tile of lane `lane`'s 8-byte piece `j` (the codes of
+// its bf16 operand piece j).  Pieces 2i and 2i + 1 of all lanes fill bytes
+// [1024 i, 1024 i + 1024) as 64 lanes x 16 bytes, so one 16-byte load per
+// lane reads 1 KiB in order; a last piece without a partner (D / 32 odd)
+// takes 64 lanes x 8 bytes.
+__device__ inline int f8_piece(int lane, int j, int head_dim) {
+  const bool paired = 2 * (j / 2) + 1 < head_dim / 32;
+  return 1024 * (j / 2) + (paired ? 16 : 8) * lane + 8 * (j % 2);
+}
+
 // Encode y (already divided by the tensor scale) as the nearest E4M3 code,
 // ties to the even mantissa; magnitudes from 448 up clamp to 448 (0x7E);
 // NaN gives the NaN code 0x7F; the sign bit is kept (also for zero).
@@ -971,10 +981,10 @@ __device__ inline uint32_t f32_to_e4m3(float y) {
 
 // FP8 cache write: one thread per (token, kv head, group of 8 channels);
 // the inputs (bf16 or fp32) are multiplied by the inverse tensor scales in
-// float32 and encoded.  FP8 tile order (one byte per element, W = D / 4
-// bytes per lane): K byte (t, d) at W (16 ((d / 8) % 4) + t) + 8 (d / 32) +
-// d % 8; V byte (t, d) at W (16 (t / 4) + d % 16) + 8 (d / 32) +
-// ((d / 16) % 2) 4 + t % 4 -- the bf16 tile's lane and piece order.
+// float32 and encoded.  FP8 tile order (one byte per element): K byte
+// (t, d) at f8_piece(16 ((d / 8) % 4) + t, d / 32) + d % 8; V byte (t, d) at
+// f8_piece(16 (t / 4) + d % 16, d / 32) + ((d / 16) % 2) 4 + t % 4 -- the
+// bf16 tile's lanes and pieces, with a lane's pieces paired into 16 bytes.
 template <typename T>
 __device__ inline float widen_in(T x);
 template <>
@@ -1000,22 +1010,21 @@ __global__ void kv_write_fp8_kernel(const T* __restrict__ k_new, const T* __rest
   const int t = static_cast<int>(slot & 15);
   const int64_t src = (i * num_kv_heads + h) * head_dim + c * 8;
   const int64_t tile = (blk * num_kv_heads + h) * int64_t(kBlock) * head_dim;
-  const int W = head_dim / 4;
   uint32_t kq[8], vq[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     kq[e] = f32_to_e4m3(widen_in<T>(k_new[src + e]) * k_inv);
     vq[e] = f32_to_e4m3(widen_in<T>(v_new[src + e]) * v_inv);
   }
-  // K: the 8 channels of the group are 8 consecutive bytes of one lane piece
+  // K: the 8 channels of the group are the 8 bytes of one lane piece
   const int d0 = c * 8;
-  uint8_t* kd = kc + tile + W * (16 * ((d0 / 8) % 4) + t) + 8 * (d0 / 32);
+  uint8_t* kd = kc + tile + f8_piece(16 * ((d0 / 8) % 4) + t, d0 / 32, head_dim);
   *reinterpret_cast<uint2*>(kd) = make_uint2(kq[0] | (kq[1] << 8) | (kq[2] << 16) | (kq[3] << 24),
                                              kq[4] | (kq[5] << 8) | (kq[6] << 16) | (kq[7] << 24));
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int d = d0 + e;
-    vc[tile + W * (16 * (t / 4) + d % 16) + 8 * (d / 32) + ((d / 16) % 2) * 4 + t % 4] =
+    vc[tile + f8_piece(16 * (t / 4) + d % 16, d / 32, head_dim) + ((d / 16) % 2) * 4 + t % 4] =
         static_cast<uint8_t>(vq[e]);
   }
 }
@@ -1233,8 +1242,8 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     if constexpr (F8) {
 #pragma unroll
       for (int j = 0; j < NJ8; ++j) {
-        kr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane * (D / 4) + 16 * j, 0, AUX));
-        vr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane * (D / 4) + 16 * j, 0, AUX));
+        kr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, loff + 1024 * j, 0, AUX));
+        vr[st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, loff + 1024 * j, 0, AUX));
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j)

@@ -270,6 +270,10 @@ def test_layout_golden_offsets():
         for t, d, ko, vo in rows:
             assert layout.k_offset(t, d) == ko, (D, t, d)
             assert layout.v_offset(t, d) == vo, (D, t, d)
+    for D, rows in g["fp8_cases"].items():
+        for t, d, ko, vo in rows:
+            assert layout.k8_offset(t, d, int(D)) == ko, (D, t, d)
+            assert layout.v8_offset(t, d, int(D)) == vo, (D, t, d)
 
 
 @pytest.mark.parametrize("D", [32, 64, 128, 256])
@@ -586,11 +590,14 @@ def test_fp8_worked_values():
     assert int(ofp8.quantize(np.float32(3.0), 0.5)) == int(ofp8.encode_f32(np.float32(6.0)))
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
 def test_fp8_layout_is_the_bf16_operand_order(D):
     """Every byte of an FP8 tile is used once, and (t, d) sits at the same
     (lane, piece, position) as in the bf16 tile: bf16 16-byte piece j of lane
-    l starts at element 512 j + 8 l, the FP8 8-byte piece at byte D/4 l + 8 j."""
+    l starts at element 512 j + 8 l; FP8 pieces 2i, 2i + 1 of lane l are the
+    16 bytes at 1024 i + 16 l, so one load instruction reads 1 KiB in order
+    (a last unpaired piece: the 8 bytes at 1024 i + 8 l)."""
+    pieces = D // 32
     for k8, k16 in ((layout.k8_offset, layout.k_offset), (layout.v8_offset, layout.v_offset)):
         seen = set()
         for t in range(16):
@@ -598,7 +605,10 @@ def test_fp8_layout_is_the_bf16_operand_order(D):
                 o8, o16 = k8(t, d, D), k16(t, d)
                 seen.add(o8)
                 j, l, w = o16 // 512, (o16 % 512) // 8, o16 % 8
-                assert o8 == (D // 4) * l + 8 * j + w
+                if j // 2 * 2 + 1 < pieces:
+                    assert o8 == 1024 * (j // 2) + 16 * l + 8 * (j % 2) + w
+                else:
+                    assert o8 == 1024 * (j // 2) + 8 * l + w
         assert seen == set(range(16 * D))
 
 
