@@ -498,8 +498,7 @@ def test_window_decode_vs_oracle(form, W, monkeypatch):
     through the driver) and decode again: caches and tables bit-exact,
     outputs within the tolerance of the oracle's windowed attention."""
     from oracle import attention as oatt
-    from oracle import replay as orep
-    from tests.gpu_parity import TOL, to_device
+    from tests.gpu_parity import TOL
     if form == "wave":
         monkeypatch.setenv("PKV_DECODE_SPLIT", "wave")
     dtype = "f32" if form == "f32" else "bf16"
@@ -520,22 +519,31 @@ def test_window_decode_vs_oracle(form, W, monkeypatch):
               f"max abs err {err:.2e}", flush=True)
         assert np.isfinite(out).all() and err <= TOL[dtype]
         if step == 0:
-            # the driver releases with the next query's context (length + 1)
-            # before planning; the oracle does the same, then appends
-            from oracle import preempt
-            rows = [list(r) for r in p.ora.tables]
-            old = p.ora.tables.copy()
-            preempt.window_release(p.ora.pool, rows, p.ora.lens + 1, W)
-            p.ora.tables[:] = np.array(rows, np.int32)
-            released = sorted(set(old[(old >= 0) & (p.ora.tables < 0)].tolist()))
-            nb = w.num_blocks
-            poison = np.uint16(0x7FC0) if dtype == "bf16" else np.float32(np.nan)
-            p.ora.cache.k[released] = poison
-            p.ora.cache.v[released] = poison
-            p.kv.k_cache.view(nb, -1)[released] = float("nan")
-            p.kv.v_cache.view(nb, -1)[released] = float("nan")
-            orep.append_step(p.ora, w)
-            p.kv.append(to_device(w.k_app), to_device(w.v_app), w.append_counts)
+            released = _window_append_step(p, W)
+
+
+def _window_append_step(p, W):
+    """One append step with a window: the driver releases with the next
+    query's context (length + 1) before planning; the oracle does the same,
+    then appends.  Released blocks are poisoned on both sides."""
+    from oracle import preempt
+    from oracle import replay as orep
+    from tests.gpu_parity import to_device
+    w = p.w
+    rows = [list(r) for r in p.ora.tables]
+    old = p.ora.tables.copy()
+    preempt.window_release(p.ora.pool, rows, p.ora.lens + 1, W)
+    p.ora.tables[:] = np.array(rows, np.int32)
+    released = sorted(set(old[(old >= 0) & (p.ora.tables < 0)].tolist()))
+    nb = w.num_blocks
+    poison = np.uint16(0x7FC0) if w.spec.dtype == "bf16" else np.float32(np.nan)
+    p.ora.cache.k[released] = poison
+    p.ora.cache.v[released] = poison
+    p.kv.k_cache.view(nb, -1)[released] = float("nan")
+    p.kv.v_cache.view(nb, -1)[released] = float("nan")
+    orep.append_step(p.ora, w)
+    p.kv.append(to_device(w.k_app), to_device(w.v_app), w.append_counts)
+    return released
 
 
 def test_window_decode_fp8_vs_oracle():
@@ -815,3 +823,59 @@ def test_swap_copy_argument_errors():
     capi.paged_kv_swap_blocks(c, c.clone(), h, h2, bad, 2, 128, 4, 4)
     torch.cuda.synchronize()
     assert bool((h == 3.0).all()) and bool((h2 == 3.0).all())
+
+
+def test_fp8_full_size_sampled():
+    """The measured FP8 decode: the gqa-8b batch (256 sequences, 32 query / 8
+    kv heads, head_dim 128, 1.5 K mean context) quantised into an FP8 cache
+    with the bench's scales, decoded in the bench's launch configuration.
+    Every cache byte against the oracle's codes; every 4th sequence and the
+    last against the oracle's attention on the codes' values; one quantised
+    append step, then again."""
+    from oracle import attention as oatt
+    from oracle import replay as orep
+    from tests.gpu_parity import to_device
+    w = synth.generate("gqa-8b-bf16")
+    s = w.spec
+    print("[fp8 full size] prefill", flush=True)
+    ora, kv = _fp8_pair(w, 6.0 / 448, 6.0 / 448)
+    q = to_device(w.q)
+    sample = list(range(0, s.num_seqs, 4)) + [s.num_seqs - 1]
+    for step in range(2):
+        _fp8_check_cache(ora, kv)
+        out = kv.decode(q, s.scale).cpu().numpy().astype(np.float64)
+        exp = oatt.decode(w.q, ora.cache, ora.tables, ora.lens, s.num_q_heads, s.num_kv_heads,
+                          s.scale, seqs=sample)
+        err = max(float(np.max(np.abs(out[b] - exp[b]))) for b in sample)
+        print(f"[fp8 full size] step {step}: sampled max abs err {err:.2e}", flush=True)
+        assert np.isfinite(out[sample]).all() and err <= 2e-3
+        orep.append_step(ora, w)
+        kv.append(to_device(w.k_app), to_device(w.v_app), w.append_counts)
+
+
+@pytest.mark.parametrize("W", [1024, 4096])
+def test_window_full_size_sampled(W):
+    """The measured sliding-window decode: the gqa-8b batch with window W after
+    the blocks before every window were released and poisoned, decoded in
+    the bench's launch configuration; caches and tables bit-exact, every 4th
+    sequence and the last against the oracle's windowed attention; one
+    append step (release through the driver), then again."""
+    from oracle import attention as oatt
+    w = synth.generate("gqa-8b-bf16")
+    s = w.spec
+    print(f"[window full size] W={W}", flush=True)
+    p = _pair(w)
+    p.kv.window = W
+    released = _release_both(p, W, p.ora.lens, p.kv.lens)
+    sample = list(range(0, s.num_seqs, 4)) + [s.num_seqs - 1]
+    for step in range(2):
+        p.check_state()
+        out = p.kv.decode(p.q, s.scale).cpu().numpy().astype(np.float64)
+        exp = oatt.decode(w.q, p.ora.cache, p.ora.tables, p.ora.lens, s.num_q_heads,
+                          s.num_kv_heads, s.scale, window=W, seqs=sample)
+        err = max(float(np.max(np.abs(out[b] - exp[b]))) for b in sample)
+        print(f"[window full size] W={W} step {step}: released {len(released)} blocks, "
+              f"sampled max abs err {err:.2e}", flush=True)
+        assert np.isfinite(out[sample]).all() and err <= 2e-3
+        if step == 0:
+            released = _window_append_step(p, W)
