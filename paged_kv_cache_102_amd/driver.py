@@ -238,15 +238,22 @@ class PagedKV:
                                     workspace=ws, stream=stream.cuda_stream)
         return out
 
-    def prefill_attention(self, q, query_start, scale: float, out=None, stream=None):
+    def prefill_attention(self, q, query_start, scale: float, out=None, stream=None,
+                          max_query_len=None):
         """Multi-query attention for chunk rows q [T][Hq][D] (their K/V already
-        appended); query_start int32 [B + 1] (numpy, uploaded here)."""
+        appended); query_start int32 [B + 1]: numpy (uploaded here), or a
+        device tensor that stays resident (then max_query_len is required)."""
         stream = stream or torch.cuda.current_stream(self.device)
-        qs = np.ascontiguousarray(query_start, dtype=np.int32)
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
-        qs_d = torch.from_numpy(qs).to(self.device)
-        max_q = int(np.max(np.diff(qs))) if qs.size > 1 else 0
+        if isinstance(query_start, torch.Tensor):
+            if max_query_len is None:
+                raise ValueError("max_query_len is required with a device query_start")
+            qs_d, max_q = query_start, int(max_query_len)
+        else:
+            qs = np.ascontiguousarray(query_start, dtype=np.int32)
+            qs_d = torch.from_numpy(qs).to(self.device)
+            max_q = int(np.max(np.diff(qs))) if qs.size > 1 else 0
         max_ctx = int(self.lens.max()) if self.lens.size else 0
         capi.paged_attention_prefill(q, self.k_cache, self.v_cache, self.tables_d, self.lens_d, qs_d,
                                      out, num_kv_heads=self.num_kv_heads, num_blocks=self.num_blocks,

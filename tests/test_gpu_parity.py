@@ -721,7 +721,9 @@ def test_prefill_full_size_sampled():
     T = n * s.num_seqs
     q = synth.round_bf16_bits(rng.standard_normal((T, s.num_q_heads, s.head_dim)).astype(np.float32))
     qstart = np.arange(0, T + 1, n, dtype=np.int32)
-    out = p.kv.prefill_attention(to_device(q), qstart, s.scale).cpu().numpy().astype(np.float64)
+    # device-resident row offsets, as the bench passes them
+    out = p.kv.prefill_attention(to_device(q), torch.from_numpy(qstart).cuda(), s.scale,
+                                 max_query_len=n).cpu().numpy().astype(np.float64)
     assert np.isfinite(out).all()
     qf = synth.bf16_bits_to_f32(q).astype(np.float64)
     g = s.num_q_heads // s.num_kv_heads
