@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "gqa-8b-bf16"
+PROFILE_EVERY = 5   # decode launches timed with events: one in five of the timed steps
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_cu_gqa-8b_traffic.txt")
 
 
@@ -492,14 +493,19 @@ def main():
     for _ in range(warm):
         step()
     torch.cuda.synchronize()
-    # timed region: K whole steps
-    bytes_total = 0
-    capi.pkv_profile_begin()
+    # timed region: K whole steps.  The library times decode launches 0,
+    # PROFILE_EVERY, 2 PROFILE_EVERY, ... with HIP events on the step's
+    # stream; each recorded pair adds two markers to its step.
+    bytes_total = bytes_prof = 0
+    capi.pkv_profile_begin(PROFILE_EVERY)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
         step()
-        bytes_total += kv_bytes(kv.lens, s.num_kv_heads, s.head_dim)
+        b = kv_bytes(kv.lens, s.num_kv_heads, s.head_dim)
+        bytes_total += b
+        if i % PROFILE_EVERY == 0:
+            bytes_prof += b
     t_issued = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -507,7 +513,7 @@ def main():
     dt = t1 - t0
     ms_per_step = dt * 1e3 / steps
     value = bytes_total / dt / 1e9
-    bytes_per_launch = bytes_total / steps
+    bytes_per_launch = bytes_prof / max(nlaunch, 1)   # of the timed launches
     avg_kernel_ms = kern_ms / max(nlaunch, 1)
     achieved = bytes_per_launch / (avg_kernel_ms * 1e-3) / 1e9
 
@@ -585,6 +591,7 @@ def main():
                      "traffic": traffic,
                      "kernel": kernel_name(args.partition),
                      "avg_launch_ms": round(avg_kernel_ms, 5), "launches": nlaunch,
+                     "launches_sampled_every": PROFILE_EVERY,
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
         "paged_vs_contiguous": paged_vs_contig,
         "prefill_chunked": prefill,

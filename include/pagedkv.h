@@ -537,13 +537,17 @@ pkv_status paged_attention_decode_window(const void* q, const void* k_cache, con
                                          float* out, hipStream_t stream);
 
 /* ===== Measurement ==========================================================
- * While profiling is on, every paged_attention_decode call records a pair of
- * HIP events around its main (block-walking) kernel on the caller's stream.
- * pkv_profile_end synchronizes on the recorded events and returns how many
- * launches were timed and their total duration in milliseconds.  At most
- * 8192 launches are kept per session (later ones are not timed).  Not
- * thread-safe. */
-pkv_status pkv_profile_begin(void);
+ * While profiling is on, decode calls number 0, every, 2 every, ... since
+ * pkv_profile_begin (each paged_attention_decode* call that gets past its
+ * argument checks counts) record a pair
+ * of HIP events around their main (block-walking) kernel on the caller's
+ * stream.  The events are created without the system-scope fence (they only
+ * time), and sampling with every > 1 keeps their markers out of most steps
+ * of a timed loop.  pkv_profile_end synchronizes on the recorded events and
+ * returns how many launches were timed and their total duration in
+ * milliseconds.  At most 8192 launches are kept per session (later ones are
+ * not timed).  every < 1 -> PKV_ERR_INVALID.  Not thread-safe. */
+pkv_status pkv_profile_begin(int32_t every);
 pkv_status pkv_profile_end(int32_t* num_launches, double* total_ms);
 
 /* Streaming-read reference: reads `bytes` (rounded down to 16) of device

@@ -83,7 +83,7 @@ _SIGS = {
                                              _vp]),
     "paged_kv_write_fp8": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, _vp, C.c_int32, C.c_int32,
                                      C.c_int32, C.c_int32, C.c_float, C.c_float, _vp]),
-    "pkv_profile_begin": (C.c_int, []),
+    "pkv_profile_begin": (C.c_int, [C.c_int32]),
     "pkv_profile_end": (C.c_int, [_i32p, C.POINTER(C.c_double)]),
     "pkv_stream_read": (C.c_int, [_vp, C.c_size_t, _vp, _vp]),
 }
@@ -456,8 +456,9 @@ def paged_attention_decode_window(q, k_cache, v_cache, block_tables, context_len
            "paged_attention_decode_window")
 
 
-def pkv_profile_begin() -> None:
-    _check(_lib.pkv_profile_begin(), "pkv_profile_begin")
+def pkv_profile_begin(every: int = 1) -> None:
+    """Times decode calls 0, every, 2 every, ... until pkv_profile_end."""
+    _check(_lib.pkv_profile_begin(every), "pkv_profile_begin")
 
 
 def pkv_profile_end():

@@ -2271,6 +2271,8 @@ struct Profiler {
   bool on = false;
   std::vector<hipEvent_t> pool;  // pairs: 2k = start, 2k+1 = stop
   size_t used = 0;
+  int every = 1;      // time calls 0, every, 2 every, ... since begin
+  int64_t calls = 0;  // decode calls since begin
 };
 Profiler g_prof;
 constexpr size_t kMaxProfiled = 8192;
@@ -2630,7 +2632,8 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                        cus > 0 && cus <= waves;
   if (fp8 && !cu_form) return PKV_ERR_UNSUPPORTED;
 
-  const bool prof = g_prof.on && g_prof.used + 2 <= g_prof.pool.size();
+  const bool prof = g_prof.on && g_prof.calls++ % g_prof.every == 0 &&
+                    g_prof.used + 2 <= g_prof.pool.size();
   if (prof) (void)hipEventRecord(g_prof.pool[g_prof.used], stream);
   if (balanced) {
     if (cu_form)
@@ -2761,16 +2764,21 @@ pkv_status pkv_stream_read(const void* buf, size_t bytes, void* sink, hipStream_
   return launch_status();
 }
 
-pkv_status pkv_profile_begin(void) {
+pkv_status pkv_profile_begin(int32_t every) {
+  if (every < 1) return PKV_ERR_INVALID;
   if (g_prof.pool.empty()) {
     g_prof.pool.resize(2 * kMaxProfiled);
+    // timing only: no system-scope fence when an event is reached, so a
+    // recorded pair costs the stream little more than its two markers
     for (auto& e : g_prof.pool)
-      if (hipEventCreate(&e) != hipSuccess) {
+      if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
         g_prof.pool.clear();
         return PKV_ERR_HIP;
       }
   }
   g_prof.used = 0;
+  g_prof.calls = 0;
+  g_prof.every = every;
   g_prof.on = true;
   return PKV_OK;
 }

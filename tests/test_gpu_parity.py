@@ -163,6 +163,14 @@ def test_profile_hooks_count_launches():
         p.kv.decode(p.q, w.spec.scale)
     n, ms = capi.pkv_profile_end()
     assert n == 3 and ms > 0
+    # sampled: calls 0, 3 and 6 of 7
+    capi.pkv_profile_begin(3)
+    for _ in range(7):
+        p.kv.decode(p.q, w.spec.scale)
+    n, ms = capi.pkv_profile_end()
+    assert n == 3 and ms > 0
+    with pytest.raises(capi.PkvError):
+        capi.pkv_profile_begin(0)
 
 
 def test_table_update_and_fused_append():
