@@ -39,7 +39,7 @@ class _Staging:
     so one event is recorded per ``every`` releases and covers all buffers
     released since the previous one (the stream runs in order)."""
 
-    def __init__(self, nbytes: int, depth: int = 8, every: int = 4):
+    def __init__(self, nbytes: int, depth: int = 16, every: int = 8):
         assert 0 < every < depth
         self.bufs = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(depth)]
         self.events = [None] * depth
