@@ -1681,15 +1681,28 @@ void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int NBUF = 2;  // stage s, and stage s + 1 being filled
   __shared__ __align__(16) unsigned char lds[NBUF * STAGE_BYTES];
 
-  // Work item: workgroup i runs on XCD i % 8.  Each XCD takes a contiguous
-  // run of items (query tile fastest), so the tiles of one (sequence, kv
-  // head) read its K/V through one L2.
+  // Work item: workgroup i runs on XCD i % 8, and all query tiles of one
+  // (sequence, kv head) pair run on one XCD, so they read its K/V through
+  // one L2.  When the pairs are a multiple of 8, XCD x takes the pairs
+  // p = x (mod 8) -- with 8 kv heads, head x of every sequence -- so every
+  // XCD gets the same mix of context lengths; inside an XCD the later (longer)
+  // query tiles go first, so the shorter ones fill in at the end.  Otherwise
+  // each XCD takes a contiguous run of items.
   const int N = gridDim.x, id = blockIdx.x;
-  const int full = N / 8 * 8;
-  const int w = id < full ? (id % 8) * (N / 8) + id / 8 : id;
-  const int qt = w % a.tiles;
-  const int kvh = (w / a.tiles) % a.num_kv_heads;
-  const int b = w / (a.tiles * a.num_kv_heads);
+  const int npairs = a.num_seqs * a.num_kv_heads;
+  int pair, qt;
+  if (npairs % 8 == 0) {
+    const int j = id / 8;
+    pair = id % 8 + 8 * (j / a.tiles);
+    qt = a.tiles - 1 - j % a.tiles;
+  } else {
+    const int full = N / 8 * 8;
+    const int w = id < full ? (id % 8) * (N / 8) + id / 8 : id;
+    qt = w % a.tiles;
+    pair = w / a.tiles;
+  }
+  const int kvh = pair % a.num_kv_heads;
+  const int b = pair / a.num_kv_heads;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
