@@ -416,7 +416,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path "
-              "is single-GPU in this build.", file=sys.stderr)
+              "runs on a single GPU.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

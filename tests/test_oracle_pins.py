@@ -578,7 +578,7 @@ def test_fp8_encode_matches_torch_in_range():
 
 
 def test_fp8_worked_values():
-    """Values fixed by the OCP E4M3 definition, and this build's clamp."""
+    """Values fixed by the OCP E4M3 definition, and the library's clamp at 448."""
     cases = [(448.0, 0x7E), (2.0 ** -6, 0x08), (2.0 ** -9, 0x01), (1.0, 0x38), (-2.0, 0xC0),
              (0.0, 0x00), (-0.0, 0x80), (1 + 1 / 16, 0x38), (1 + 3 / 16, 0x3A), (1e6, 0x7E),
              (-1e6, 0xFE), (464.0, 0x7E), (3 * 2.0 ** -10, 0x02), (2.0 ** -10, 0x00)]
