@@ -1685,16 +1685,46 @@ void prefill_bf16_kernel(PrefillArgs a) {
   // (sequence, kv head) pair run on one XCD, so they read its K/V through
   // one L2.  When the pairs are a multiple of 8, XCD x takes the pairs
   // p = x (mod 8) -- with 8 kv heads, head x of every sequence -- so every
-  // XCD gets the same mix of context lengths; inside an XCD the later (longer)
-  // query tiles go first, so the shorter ones fill in at the end.  Otherwise
-  // each XCD takes a contiguous run of items.
+  // XCD gets the same mix of context lengths; inside an XCD the longer items
+  // go first, so the shorter ones fill in at the end.  Otherwise each XCD
+  // takes a contiguous run of items.
   const int N = gridDim.x, id = blockIdx.x;
   const int npairs = a.num_seqs * a.num_kv_heads;
   int pair, qt;
   if (npairs % 8 == 0) {
-    const int j = id / 8;
-    pair = id % 8 + 8 * (j / a.tiles);
-    qt = a.tiles - 1 - j % a.tiles;
+    const int x = id % 8, j = id / 8;
+    const int items = npairs / 8 * a.tiles;  // of this XCD: pairs x + 8 m, all tiles
+    if (items <= 64) {
+      // Longest first: lane i holds item i's stage count (the same arithmetic
+      // as below), ranks by descending count with ties by index (a
+      // permutation, identical in every workgroup), and this workgroup takes
+      // the item of rank j.
+      const int i = threadIdx.x & 63;
+      int work = -1;
+      if (i < items) {
+        const int ib = (x + 8 * (i / a.tiles)) / a.num_kv_heads;
+        const int iq0 = (i % a.tiles) * a.qtp;
+        const int ins = a.qstart[ib], in = a.qstart[ib + 1] - ins, iL = a.lens[ib];
+        work = 0;
+        if (iq0 < in && in > 0 && iL >= in) {
+          const int pf = iL - in + iq0, pl = pf + min(a.qtp, in - iq0) - 1;
+          const int i0w = (WIN ? max(0, pf - a.window + 1) : 0) / kBlock;
+          work = pl / kBlock + 1 - i0w;
+        }
+      }
+      int rank = 0;
+      for (int k = 0; k < items; ++k) {
+        const int wk = __builtin_amdgcn_readlane(work, k);
+        rank += (wk > work || (wk == work && k < i)) ? 1 : 0;
+      }
+      const int sel = static_cast<int>(__builtin_ctzll(
+          __builtin_amdgcn_ballot_w64(i < items && rank == j)));
+      pair = x + 8 * (sel / a.tiles);
+      qt = sel % a.tiles;
+    } else {
+      pair = x + 8 * (j / a.tiles);
+      qt = a.tiles - 1 - j % a.tiles;
+    }
   } else {
     const int full = N / 8 * 8;
     const int w = id < full ? (id % 8) * (N / 8) + id / 8 : id;
