@@ -889,3 +889,39 @@ def test_window_full_size_sampled(W):
         assert np.isfinite(out[sample]).all() and err <= 2e-3
         if step == 0:
             released = _window_append_step(p, W)
+
+
+def test_staging_ring_wraps_and_regrows():
+    """The step indices staged in pinned memory and read in place: 20
+    one-token steps (the ring of 16 buffers wraps and reuses buffers behind
+    its events), one append of 1 800 tokens per sequence whose indices exceed a
+    ring buffer (the ring is drained and regrown), 20 one-token steps more;
+    caches, tables and lengths bit-exact after every step, decode at the end."""
+    import dataclasses
+    from oracle import replay as orep
+    from tests.gpu_parity import to_device
+    w = synth.small_random(77, num_seqs=6, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                           dtype="bf16", max_len=40, append=1900)
+    p = _pair(w)
+    B = w.spec.num_seqs
+    off = 0
+
+    def step(n):
+        nonlocal off
+        T = n * B
+        sub = dataclasses.replace(w, append_counts=np.full(B, n, np.int32),
+                                  k_app=w.k_app[off:off + T], v_app=w.v_app[off:off + T])
+        off += T
+        orep.append_step(p.ora, sub)
+        p.kv.append(to_device(sub.k_app), to_device(sub.v_app), sub.append_counts)
+        p.check_state()
+
+    for _ in range(20):
+        step(1)
+    ring = p.kv._staging
+    step(1800)
+    assert p.kv._staging is not ring
+    for _ in range(20):
+        step(1)
+    err = p.check_decode()
+    print(f"[staging] after {off // B} tokens per sequence: max abs err {err:.2e}", flush=True)
