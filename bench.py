@@ -163,7 +163,7 @@ def prefill_measure(dev, reps: int = 20):
     tflops = flops / (ms * 1e-3) / 1e12
     return {"workload": "8 sequences x 512-token chunks on 1024..2048 cached tokens, 32 q / 8 kv heads, "
                         "head_dim 128, bf16",
-            "kernel": "prefill_bf16_kernel<128,false> (8 wavefronts, 256 score columns, K/V staged in LDS)", "ms": round(ms, 4),
+            "kernel": "prefill_bf16_kernel<128,false,4> (8 wavefronts, 256 score columns, 4-block K/V stages in LDS)", "ms": round(ms, 4),
             "tflops": round(tflops, 2), "bound": "mfma", "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
             "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
             "unique_kv_gb_per_s": round(kv_unique / ms / 1e6, 1)}

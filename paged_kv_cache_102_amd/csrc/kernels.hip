@@ -1666,15 +1666,18 @@ constexpr int kPfWaves = 8;
 constexpr int kPfColTiles = 2;                       // 16-column tiles per wavefront
 constexpr int kPfCols = kPfWaves * kPfColTiles * 16;  // score columns per workgroup
 constexpr float kPfRescale = 8.0f;                   // lazy max threshold (log2 domain)
+constexpr int kPfStageBlocks = 4;                    // default blocks per pipeline stage
 
-template <int D, bool WIN>
+// SB: blocks per pipeline stage (even: P.V takes them in pairs).
+template <int D, bool WIN, int SB>
 __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillArgs a) {
+  static_assert(SB % 2 == 0, "blocks per stage come in pairs");
   constexpr int NJ = D / 32;                  // K / V pieces per tile
   constexpr int NT = D / 16;                  // 16-channel output tiles
   constexpr int NQ = kPfColTiles;
   constexpr int TILE_BYTES = kBlock * D * 2;
-  constexpr int STAGE_BYTES = 4 * TILE_BYTES;  // blocks 0, 1 x (K, V)
+  constexpr int STAGE_BYTES = 2 * SB * TILE_BYTES;  // blocks 0 .. SB-1 x (K, V)
   constexpr int PIECES = STAGE_BYTES / 16;     // 16-byte loads per stage
   constexpr int PT = PIECES / (64 * kPfWaves);  // per thread
   constexpr int TILE_PIECES = TILE_BYTES / 16;
@@ -1763,7 +1766,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
   const int t_lo = WIN ? max(0, p_first - a.window + 1) : 0;  // earliest visible position
   const int i0 = t_lo / kBlock;
   const int nblk = p_last / kBlock + 1 - i0;
-  const int nst = (nblk + 1) / 2;
+  const int nst = (nblk + SB - 1) / SB;
   const int32_t* row = a.tables + int64_t(b) * a.max_blocks + i0;
 
   // this lane's columns: c = 16 (NQ wave + t) + hcol -> (position, head)
@@ -1805,10 +1808,10 @@ void prefill_bf16_kernel(PrefillArgs a) {
   // [t_lo, L) are zeroed on the way (they may hold anything).
   uint4 st[PT];
   auto gload = [&](int s) {
-    int ph[2], by[2];
+    int ph[SB], by[SB];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int rel = 2 * s + k;
+    for (int k = 0; k < SB; ++k) {
+      const int rel = SB * s + k;
       ph[k] = 0;
       by[k] = 0;
       if (rel < nblk) {
@@ -1825,9 +1828,14 @@ void prefill_bf16_kernel(PrefillArgs a) {
       const int first = 64 * kPfWaves * u + 64 * wave;
       const int tile = first / TILE_PIECES;
       const int off0 = (first % TILE_PIECES) * 16;
-      const int rel = 2 * s + (tile >> 1);
-      const int phys = (tile >> 1) ? ph[1] : ph[0];
-      const int bytes = (tile >> 1) ? by[1] : by[0];
+      const int rel = SB * s + (tile >> 1);
+      int phys = 0, bytes = 0;  // selected, not indexed: ph and by stay in registers
+#pragma unroll
+      for (int k = 0; k < SB; ++k)
+        if ((tile >> 1) == k) {
+          phys = ph[k];
+          bytes = by[k];
+        }
       const char* base = ((tile & 1) ? vc : kc) + (bytes ? int64_t(phys) * block_bytes : 0) + off0;
       const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, bytes ? bytes - off0 : 0);
       uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, 0));
@@ -1893,44 +1901,52 @@ void prefill_bf16_kernel(PrefillArgs a) {
   }
 
   // weights of the stage being processed (bf16 high parts and residuals)
-  uint32_t phi[NQ][4], plo[NQ][4];
-  // O += P . V over stage s's 32 tokens (k < 4: first block, k >= 4:
-  // second); each V piece is read once and used by all column tiles
+  uint32_t phi[NQ][2 * SB], plo[NQ][2 * SB];
+  // O += P . V over each pair of blocks of stage s (k < 4: the pair's first
+  // block, k >= 4: its second); each V piece is read once and used by all
+  // column tiles
   auto pv = [&](int s) {
     const unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const uint4 v0 = *reinterpret_cast<const uint4*>(sb + 1 * TILE_BYTES + 1024 * j + lane * 16);
-      const uint4 v1 = *reinterpret_cast<const uint4*>(sb + 3 * TILE_BYTES + 1024 * j + lane * 16);
-      const bf16x8 vlo = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-      const bf16x8 vhi = __builtin_bit_cast(bf16x8, make_uint4(v0.z, v0.w, v1.z, v1.w));
+    for (int pp = 0; pp < SB / 2; ++pp) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint4 v0 = *reinterpret_cast<const uint4*>(sb + (4 * pp + 1) * TILE_BYTES + 1024 * j + lane * 16);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(sb + (4 * pp + 3) * TILE_BYTES + 1024 * j + lane * 16);
+        const bf16x8 vlo = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+        const bf16x8 vhi = __builtin_bit_cast(bf16x8, make_uint4(v0.z, v0.w, v1.z, v1.w));
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) {
+          const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
+                                                                  phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
+          const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(plo[t][4 * pp], plo[t][4 * pp + 1],
+                                                                  plo[t][4 * pp + 2], plo[t][4 * pp + 3]));
+          o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vlo, o[t][2 * j], 0, 0, 0);
+          o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vlo, o[t][2 * j], 0, 0, 0);
+          o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vhi, o[t][2 * j + 1], 0, 0, 0);
+          o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vhi, o[t][2 * j + 1], 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int t = 0; t < NQ; ++t) {
-        const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(phi[t][0], phi[t][1], phi[t][2], phi[t][3]));
-        const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(plo[t][0], plo[t][1], plo[t][2], plo[t][3]));
-        o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vlo, o[t][2 * j], 0, 0, 0);
-        o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vlo, o[t][2 * j], 0, 0, 0);
-        o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vhi, o[t][2 * j + 1], 0, 0, 0);
-        o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vhi, o[t][2 * j + 1], 0, 0, 0);
+        const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
+                                                                phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
+        const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(plo[t][4 * pp], plo[t][4 * pp + 1],
+                                                                plo[t][4 * pp + 2], plo[t][4 * pp + 3]));
+        lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ones, lacc[t], 0, 0, 0);
+        lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, ones, lacc[t], 0, 0, 0);
       }
-    }
-#pragma unroll
-    for (int t = 0; t < NQ; ++t) {
-      const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(phi[t][0], phi[t][1], phi[t][2], phi[t][3]));
-      const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(plo[t][0], plo[t][1], plo[t][2], plo[t][3]));
-      lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ones, lacc[t], 0, 0, 0);
-      lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, ones, lacc[t], 0, 0, 0);
     }
   };
 
   // scores of stage s, softmax update, weights into phi / plo
   auto score = [&](int s) {
     const unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
-    const int tb0 = (i0 + 2 * s) * kBlock;  // first position of the stage
-    // scores of both blocks for every column tile
-    f32x4 sc[NQ][2];
+    const int tb0 = (i0 + SB * s) * kBlock;  // first position of the stage
+    // scores of all blocks of the stage for every column tile
+    f32x4 sc[NQ][SB];
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
+    for (int bb = 0; bb < SB; ++bb) {
       bf16x8 kx[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
@@ -1945,24 +1961,27 @@ void prefill_bf16_kernel(PrefillArgs a) {
     }
     // masks are needed only where the stage reaches past the tile's first
     // position (causal) or before its last column's window start
-    const bool edge = tb0 + 2 * kBlock - 1 > p_first || (WIN && tb0 < p_last - a.window + 1);
+    const bool edge = tb0 + SB * kBlock - 1 > p_first || (WIN && tb0 < p_last - a.window + 1);
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
       // raw scores; masked ones become -inf (exp2 of them is 0)
-      float sv[8];
+      float sv[4 * SB];
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
+      for (int bb = 0; bb < SB; ++bb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sv[4 * bb + r] = sc[t][bb][r];
       if (edge) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4 * SB; ++e) {
           const int tp = tb0 + (e >> 2) * kBlock + grp * 4 + (e & 3);
           if (tp > pos[t] || tp < lo_c[t]) sv[e] = -INFINITY;
         }
       }
       float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                          fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+#pragma unroll
+      for (int e = 8; e < 4 * SB; e += 4)
+        mloc = fmaxf(mloc, fmaxf(fmaxf(sv[e], sv[e + 1]), fmaxf(sv[e + 2], sv[e + 3])));
       mloc = group_max(mloc) * cs;
       // lazy max: raise it only when the stage max exceeds it by 2^8
       const bool raise = mloc > m[t] + kPfRescale;
@@ -1981,16 +2000,16 @@ void prefill_bf16_kernel(PrefillArgs a) {
       // (a column's masked scores are -inf, its unmasked ones finite: the
       // fma gives -inf or a finite value for any cs >= 0 except cs = 0,
       // where -inf * 0 is NaN; masks therefore select 0 after exp2)
-      float p[8];
+      float p[4 * SB];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], cs, -m[t]));
+      for (int e = 0; e < 4 * SB; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], cs, -m[t]));
       if (edge) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < 4 * SB; ++e)
           if (sv[e] == -INFINITY) p[e] = 0.f;
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 2 * SB; ++e) {
         split_bf16x2(p[2 * e], p[2 * e + 1], phi[t][e], plo[t][e]);
       }
     }
@@ -2382,19 +2401,29 @@ void launch_decode_bf16_cu(unsigned grid, hipStream_t stream, const DecodeArgs& 
     launch_decode_bf16_cu_w<false>(grid, stream, a, head_dim, fp8);
 }
 
-void launch_prefill_bf16(unsigned grid, hipStream_t stream, const PrefillArgs& a, int head_dim) {
+template <int SB>
+void launch_prefill_bf16_sb(unsigned grid, hipStream_t stream, const PrefillArgs& a,
+                            int head_dim) {
   const dim3 block(64 * kPfWaves);
   const bool win = a.window > 0;
   if (head_dim == 64) {
     if (win)
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, true, SB>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, false, SB>), grid, block, 0, stream, a);
   } else if (win) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, true, SB>), grid, block, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, false, SB>), grid, block, 0, stream, a);
   }
+}
+
+// Blocks per pipeline stage: PKV_PF_STAGE_BLOCKS = 2 or 4 (default kPfStageBlocks).
+void launch_prefill_bf16(unsigned grid, hipStream_t stream, const PrefillArgs& a, int head_dim) {
+  if (env_int("PKV_PF_STAGE_BLOCKS", kPfStageBlocks, 2, 4) == 4)
+    launch_prefill_bf16_sb<4>(grid, stream, a, head_dim);
+  else
+    launch_prefill_bf16_sb<2>(grid, stream, a, head_dim);
 }
 
 // ============================================================================ C ABI
