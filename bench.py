@@ -367,6 +367,43 @@ def kv_bytes(lens, num_kv_heads, head_dim, elem=2) -> int:
     return int(lens.astype("int64").sum()) * 2 * num_kv_heads * head_dim * elem
 
 
+def paged_vs_contiguous(dev, w, q, out, reps: int):
+    """Decode alone, back to back, on two fresh pools with the workload's
+    prefill state: the same lengths and values, once in the workload's
+    scattered block order and once with each sequence's blocks consecutive
+    (identity free-list order).  Runs after the timed steps: building and
+    freeing two more pools before them slowed those steps by ~3 %."""
+    import torch
+    from paged_kv_cache_102_amd.driver import PagedKV, replay_prefill
+    import numpy as np
+    s = w.spec
+
+    def to_dev(rows):
+        return torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).to(dev).view(torch.bfloat16)
+    times = {}
+    for name, order in (("paged", w.pool_order), ("contiguous", None)):
+        obj = PagedKV(num_blocks=w.num_blocks, num_seqs=s.num_seqs,
+                      max_blocks_per_seq=w.max_blocks_per_seq, num_q_heads=s.num_q_heads,
+                      num_kv_heads=s.num_kv_heads, head_dim=s.head_dim, dtype=s.dtype, device=dev,
+                      init_order=order)
+        replay_prefill(obj, w, to_dev)
+        obj.decode(q, s.scale, out=out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            obj.decode(q, s.scale, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / reps
+        del obj
+        torch.cuda.empty_cache()
+    return {"paged_ms": round(times["paged"], 4), "contiguous_ms": round(times["contiguous"], 4),
+            "paged_overhead_pct": round(100 * (times["paged"] / times["contiguous"] - 1), 2),
+            "note": "fresh pools after prefill, same lengths and values; contiguous = each "
+                    "sequence's blocks consecutive in the pool"}
+
+
 def cpu_baseline(w, seconds: float = 12.0):
     """The oracle, as it stands, on this host: decode over the whole batch,
     repeated until ``seconds`` of CPU work, single-threaded BLAS."""
@@ -454,38 +491,6 @@ def main():
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    # paged vs contiguous: the same lengths and values with the blocks of
-    # each sequence consecutive in the pool (identity free-list order), decode
-    # alone, back to back
-    paged_vs_contig = None
-    if args.contiguous and args.decode_only_steps > 0:
-        kc = PagedKV(num_blocks=w.num_blocks, num_seqs=s.num_seqs,
-                     max_blocks_per_seq=w.max_blocks_per_seq, num_q_heads=s.num_q_heads,
-                     num_kv_heads=s.num_kv_heads, head_dim=s.head_dim, dtype=s.dtype, device=dev,
-                     init_order=None, partition_size=args.partition)
-        replay_prefill(kc, w, to_dev)
-        kv.decode(q, s.scale, out=out)
-        kc.decode(q, s.scale, out=out)
-        times = {}
-        for name, obj in (("paged", kv), ("contiguous", kc)):
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(args.decode_only_steps):
-                obj.decode(q, s.scale, out=out)
-            e1.record()
-            torch.cuda.synchronize()
-            times[name] = e0.elapsed_time(e1) / args.decode_only_steps
-        paged_vs_contig = {"paged_ms": round(times["paged"], 4),
-                           "contiguous_ms": round(times["contiguous"], 4),
-                           "paged_overhead_pct": round(100 * (times["paged"] / times["contiguous"] - 1),
-                                                       2),
-                           "note": "after prefill, same lengths and values; contiguous = each "
-                                   "sequence's blocks consecutive in the pool"}
-        del kc
-        torch.cuda.empty_cache()
-
-
     def step():
         kv.append(k_new, v_new)
         kv.decode(q, s.scale, out=out)
@@ -531,6 +536,11 @@ def main():
         db = kv_bytes(kv.lens, s.num_kv_heads, s.head_dim)
         dec = {"ms": round(dms, 4), "kv_gb_per_s": round(db / dms / 1e6, 1),
                "frac_of_peak": round(db / dms / 1e6 / HBM_PEAK_GBS, 4)}
+
+    # paged vs contiguous block placement, on fresh pools
+    paged_vs_contig = None
+    if args.contiguous and args.decode_only_steps > 0:
+        paged_vs_contig = paged_vs_contiguous(dev, w, q, out, args.decode_only_steps)
 
     # measured streaming-read ceiling on this GPU (2 GiB, 16-byte loads)
     ceiling = None
