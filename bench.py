@@ -119,11 +119,13 @@ def all_configs(path: str, dev):
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
-def prefill_measure(dev, reps: int = 20):
+def prefill_measure(dev, reps: int = 20, cache: str = "bf16"):
     """Multi-query (chunked prefill) attention: 8 sequences of the gqa-8b
     shape with 1024..2048 cached tokens each take a 512-token chunk, causal
-    inside the chunk.  Returns the kernel time and its rate against the bf16
-    matrix-core peak (4 * D flops per (query row, attended token))."""
+    inside the chunk, over a bf16 or an FP8 (E4M3, tensor scales) cache.
+    Returns the kernel time and its rate against the bf16 matrix-core peak
+    (4 * D flops per (query row, attended token); the products run in bf16
+    for both caches)."""
     import numpy as np
     import torch
     from paged_kv_cache_102_amd.driver import PagedKV, replay_prefill
@@ -137,8 +139,8 @@ def prefill_measure(dev, reps: int = 20):
         return torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).to(dev).view(torch.bfloat16)
     kv = PagedKV(num_blocks=w.num_blocks, num_seqs=s.num_seqs,
                  max_blocks_per_seq=w.max_blocks_per_seq, num_q_heads=s.num_q_heads,
-                 num_kv_heads=s.num_kv_heads, head_dim=s.head_dim, dtype=s.dtype, device=dev,
-                 init_order=w.pool_order)
+                 num_kv_heads=s.num_kv_heads, head_dim=s.head_dim, dtype=cache, device=dev,
+                 init_order=w.pool_order, k_scale=6.0 / 448, v_scale=6.0 / 448)
     replay_prefill(kv, w, to_dev)
     kv.append(to_dev(w.k_app), to_dev(w.v_app), w.append_counts)
     T = n * s.num_seqs
@@ -159,11 +161,15 @@ def prefill_measure(dev, reps: int = 20):
     lens = kv.lens.astype(np.int64)
     attended = int(sum(int(L) * n - n * (n - 1) // 2 for L in lens))   # sum over rows of (p + 1)
     flops = 4.0 * s.head_dim * s.num_q_heads * attended
-    kv_unique = int(lens.sum()) * 2 * s.num_kv_heads * s.head_dim * 2
+    kv_unique = int(lens.sum()) * 2 * s.num_kv_heads * s.head_dim * (1 if cache == "fp8" else 2)
     tflops = flops / (ms * 1e-3) / 1e12
+    f8 = cache == "fp8"
     return {"workload": "8 sequences x 512-token chunks on 1024..2048 cached tokens, 32 q / 8 kv heads, "
-                        "head_dim 128, bf16",
-            "kernel": "prefill_bf16_kernel<128,false,4> (8 wavefronts, 256 score columns, 4-block K/V stages in LDS)", "ms": round(ms, 4),
+                        "head_dim 128, " + ("FP8 E4M3 cache" if f8 else "bf16"),
+            "kernel": f"prefill_bf16_kernel<128,false,4{',F8' if f8 else ''}> (8 wavefronts, 256 score "
+                      "columns, 4-block K/V stages in LDS" + (", codes expanded to bf16 on the way in)"
+                                                            if f8 else ")"),
+            "ms": round(ms, 4),
             "tflops": round(tflops, 2), "bound": "mfma", "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
             "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
             "unique_kv_gb_per_s": round(kv_unique / ms / 1e6, 1)}
@@ -566,10 +572,11 @@ def main():
         window = window_measure(dev, kv, q, s.scale)   # releases blocks: after the rest
         prefix = prefix_measure()
     fp8 = fp8_measure(dev, w) if args.fp8 else None
-    prefill = None
+    prefill = prefill_fp8 = None
     if args.prefill:
         torch.cuda.synchronize()
         prefill = prefill_measure(dev)
+        prefill_fp8 = prefill_measure(dev, cache="fp8") if args.fp8 else None
 
     traffic = committed_traffic()
     result = {
@@ -605,6 +612,7 @@ def main():
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
         "paged_vs_contiguous": paged_vs_contig,
         "prefill_chunked": prefill,
+        "prefill_chunked_fp8": prefill_fp8,
         "fp8_decode": fp8,
         "sliding_window_decode": window,
         "block_swap": swap,

@@ -503,7 +503,8 @@ pkv_status paged_attention_decode_fp8(const void* q, const void* k_cache, const 
  *   query_start: device int32 [num_seqs + 1], non-decreasing, query_start[0] = 0
  *   out: device fp32 [T][num_q_heads][head_dim], written for every chunk row
  *   max_query_len: host-side upper bound of n_s (sizes the grid)
- * bf16 caches only; head_dim 64 or 128; at most 16 query heads per kv head.
+ * bf16 caches (kv_dtype PKV_BF16; FP8: paged_attention_prefill_fp8);
+ * head_dim 64 or 128; at most 16 query heads per kv head.
  * Errors: as paged_attention_decode (PKV_ERR_INVALID / PKV_ERR_UNSUPPORTED);
  * on the device a sequence with a bad length, n_s > L, or a table entry
  * outside [0, num_blocks) gets NaN rows instead of out-of-range reads. */
@@ -515,6 +516,23 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
                                    int32_t max_context_len, int32_t max_query_len, float scale,
                                    int32_t window, pkv_dtype kv_dtype, float* out,
                                    hipStream_t stream);
+
+/* Chunked prefill over an FP8 E4M3 cache: paged_attention_prefill's result
+ * for K, V = code value x k_scale, v_scale ["KV cache: la memoria de
+ * trabajo...", «Cuantización del KV cache»: the cache is read at half the
+ * bytes].  q is bf16, out fp32, as above.  The codes are expanded to bf16
+ * exactly on their way into LDS; k_scale folds into the score scale and
+ * v_scale into the output.  Scales must be positive and finite, else
+ * PKV_ERR_INVALID; other arguments and errors as paged_attention_prefill. */
+pkv_status paged_attention_prefill_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       const int32_t* query_start, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len,
+                                       int32_t max_query_len, float scale, int32_t window,
+                                       float k_scale, float v_scale, float* out,
+                                       hipStream_t stream);
 
 /* Decode with a sliding window, for every cache dtype [P5 "Sliding window
  * attention": the model attends only to the last W tokens].  The query of

@@ -70,6 +70,10 @@ _SIGS = {
     "paged_attention_prefill": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
                                           C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                           C.c_int32, C.c_float, C.c_int32, C.c_int, _vp, _vp]),
+    "paged_attention_prefill_fp8": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
+                                              C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                              C.c_int32, C.c_int32, C.c_float, C.c_int32,
+                                              C.c_float, C.c_float, _vp, _vp]),
     "paged_attention_decode_window": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
                                                 C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                                 C.c_int32, C.c_float, C.c_int32, C.c_int32, _vp,
@@ -403,6 +407,26 @@ def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, que
                                         window, _dtype_code(k_cache), _dev(out, "out"),
                                         _stream(stream)),
            "paged_attention_prefill")
+
+
+def paged_attention_prefill_fp8(q, k_cache, v_cache, block_tables, context_lens, query_start, out,
+                                *, num_kv_heads: int, num_blocks: int, max_context_len: int,
+                                max_query_len: int, scale: float, k_scale: float, v_scale: float,
+                                window: int = 0, stream=None) -> None:
+    """paged_attention_prefill over FP8 E4M3 caches (uint8 codes) with tensor
+    scales; q bf16 [T][Hq][D], out fp32."""
+    T, Hq, D = q.shape
+    B = context_lens.shape[0]
+    mb = block_tables.shape[1]
+    _check(_lib.paged_attention_prefill_fp8(_dev(q, "q"), _dev(k_cache, "k_cache"),
+                                            _dev(v_cache, "v_cache"),
+                                            _dev(block_tables, "block_tables"),
+                                            _dev(context_lens, "context_lens"),
+                                            _dev(query_start, "query_start"), B, Hq, num_kv_heads,
+                                            D, num_blocks, mb, max_context_len, max_query_len,
+                                            scale, window, k_scale, v_scale, _dev(out, "out"),
+                                            _stream(stream)),
+           "paged_attention_prefill_fp8")
 
 
 def paged_kv_write_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, num_kv_heads: int,

@@ -1660,6 +1660,7 @@ struct PrefillArgs {
   int num_blocks, max_blocks, max_ctx;
   float scale_log2e;
   int window;  // sliding window in tokens: position p sees p-window+1 .. p (0: 0 .. p)
+  float out_scale;  // 1, or the V scale of an FP8 cache
 };
 
 constexpr int kPfWaves = 8;
@@ -1668,8 +1669,12 @@ constexpr int kPfCols = kPfWaves * kPfColTiles * 16;  // score columns per workg
 constexpr float kPfRescale = 8.0f;                   // lazy max threshold (log2 domain)
 constexpr int kPfStageBlocks = 4;                    // default blocks per pipeline stage
 
-// SB: blocks per pipeline stage (even: P.V takes them in pairs).
-template <int D, bool WIN, int SB>
+// SB: blocks per pipeline stage (even: P.V takes them in pairs).  F8: the
+// cache holds FP8 E4M3 codes; each lane's 16 codes of a 1 KiB run are
+// expanded to its two bf16 pieces on the way into LDS, so everything after
+// the staging is the bf16 path (K scale folded into the score scale, V
+// scale into out_scale).
+template <int D, bool WIN, int SB, bool F8 = false>
 __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillArgs a) {
   static_assert(SB % 2 == 0, "blocks per stage come in pairs");
@@ -1681,6 +1686,12 @@ void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int PIECES = STAGE_BYTES / 16;     // 16-byte loads per stage
   constexpr int PT = PIECES / (64 * kPfWaves);  // per thread
   constexpr int TILE_PIECES = TILE_BYTES / 16;
+  // tiles in global memory: as in LDS, or FP8 at one byte per element
+  constexpr int TILE_G = F8 ? kBlock * D : TILE_BYTES;
+  constexpr int TILE_PIECES_G = TILE_G / 16;
+  constexpr int PT_G = 2 * SB * TILE_PIECES_G / (64 * kPfWaves);  // global pieces per thread
+  static_assert(PT_G >= 1 && (2 * SB * TILE_PIECES_G) % (64 * kPfWaves) == 0,
+                "a stage's global pieces spread evenly over the threads");
   constexpr int NBUF = 2;  // stage s, and stage s + 1 being filled
   __shared__ __align__(16) unsigned char lds[NBUF * STAGE_BYTES];
 
@@ -1796,17 +1807,18 @@ void prefill_bf16_kernel(PrefillArgs a) {
     }
   }
 
-  const char* kc = static_cast<const char*>(a.kc) + int64_t(kvh) * TILE_BYTES;
-  const char* vc = static_cast<const char*>(a.vc) + int64_t(kvh) * TILE_BYTES;
-  const int64_t block_bytes = int64_t(a.num_kv_heads) * TILE_BYTES;
+  const char* kc = static_cast<const char*>(a.kc) + int64_t(kvh) * TILE_G;
+  const char* vc = static_cast<const char*>(a.vc) + int64_t(kvh) * TILE_G;
+  const int64_t block_bytes = int64_t(a.num_kv_heads) * TILE_G;
   bool bad = false;
 
   // Stage loader: thread tid moves pieces 512 u + tid (u < PT) of the stage's
   // four tiles (block 0 K, block 0 V, block 1 K, block 1 V); a wavefront's 64
   // pieces lie in one tile, so the tile (and its block id, read once per
   // stage through the scalar cache) is wave-uniform.  V slots outside
-  // [t_lo, L) are zeroed on the way (they may hold anything).
-  uint4 st[PT];
+  // [t_lo, L) are zeroed on the way (they may hold anything).  An FP8 run
+  // expands to two bf16 runs: st[2u] and st[2u + 1].
+  uint4 st[F8 ? 2 * PT_G : PT];
   auto gload = [&](int s) {
     int ph[SB], by[SB];
 #pragma unroll
@@ -1819,15 +1831,15 @@ void prefill_bf16_kernel(PrefillArgs a) {
         if (ph[k] < 0 || ph[k] >= a.num_blocks)
           bad = true;
         else
-          by[k] = TILE_BYTES;
+          by[k] = TILE_G;
       }
     }
 #pragma unroll
-    for (int u = 0; u < PT; ++u) {
+    for (int u = 0; u < PT_G; ++u) {
       // the wavefront's 64 pieces: a 1 KiB run at a uniform offset of its tile
       const int first = 64 * kPfWaves * u + 64 * wave;
-      const int tile = first / TILE_PIECES;
-      const int off0 = (first % TILE_PIECES) * 16;
+      const int tile = first / TILE_PIECES_G;
+      const int off0 = (first % TILE_PIECES_G) * 16;
       const int rel = SB * s + (tile >> 1);
       int phys = 0, bytes = 0;  // selected, not indexed: ph and by stay in registers
 #pragma unroll
@@ -1839,6 +1851,11 @@ void prefill_bf16_kernel(PrefillArgs a) {
       const char* base = ((tile & 1) ? vc : kc) + (bytes ? int64_t(phys) * block_bytes : 0) + off0;
       const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, bytes ? bytes - off0 : 0);
       uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, 0));
+      uint4 y = make_uint4(0u, 0u, 0u, 0u);  // FP8: the second bf16 piece
+      if constexpr (F8) {
+        y = e4m3x8_to_bf16x8(x.z, x.w);
+        x = e4m3x8_to_bf16x8(x.x, x.y);
+      }
       if (tile & 1) {
         // V piece: lane l of a 1 KiB run holds tokens 4 (l / 16) .. + 3
         const int t0 = (i0 + rel) * kBlock + 4 * grp;
@@ -1850,18 +1867,37 @@ void prefill_bf16_kernel(PrefillArgs a) {
           x.y &= m23;
           x.z &= m01;
           x.w &= m23;
+          if constexpr (F8) {
+            y.x &= m01;
+            y.y &= m23;
+            y.z &= m01;
+            y.w &= m23;
+          }
         }
       }
-      st[u] = x;
+      if constexpr (F8) {
+        st[2 * u] = x;
+        st[2 * u + 1] = y;
+      } else {
+        st[u] = x;
+      }
     }
   };
   auto lwrite = [&](int s) {
     unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
 #pragma unroll
-    for (int u = 0; u < PT; ++u) {
+    for (int u = 0; u < PT_G; ++u) {
       const int first = 64 * kPfWaves * u + 64 * wave;  // same run as in gload
-      *reinterpret_cast<uint4*>(sb + (first / TILE_PIECES) * TILE_BYTES +
-                                (first % TILE_PIECES) * 16 + lane * 16) = st[u];
+      if constexpr (F8) {
+        // FP8 run i of the tile holds bf16 pieces 2i and 2i + 1 of each lane
+        unsigned char* d = sb + (first / TILE_PIECES_G) * TILE_BYTES +
+                           2048 * ((first % TILE_PIECES_G) / 64) + lane * 16;
+        *reinterpret_cast<uint4*>(d) = st[2 * u];
+        *reinterpret_cast<uint4*>(d + 1024) = st[2 * u + 1];
+      } else {
+        *reinterpret_cast<uint4*>(sb + (first / TILE_PIECES) * TILE_BYTES +
+                                  (first % TILE_PIECES) * 16 + lane * 16) = st[u];
+      }
     }
   };
 
@@ -2038,7 +2074,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int cl = grp * 4 + r;  // output row = column of the tile
       const int c = (NQ * wave + t) * 16 + cl;
-      const float inv = bad ? __builtin_nanf("") : 1.0f / lacc[t][r];
+      const float inv = bad ? __builtin_nanf("") : a.out_scale / lacc[t][r];
       if (c < ncol) {
         float* dst = out_row(c) + hcol;
 #pragma unroll
@@ -2401,32 +2437,84 @@ void launch_decode_bf16_cu(unsigned grid, hipStream_t stream, const DecodeArgs& 
     launch_decode_bf16_cu_w<false>(grid, stream, a, head_dim, fp8);
 }
 
-template <int SB>
+template <int SB, bool F8>
 void launch_prefill_bf16_sb(unsigned grid, hipStream_t stream, const PrefillArgs& a,
                             int head_dim) {
   const dim3 block(64 * kPfWaves);
   const bool win = a.window > 0;
   if (head_dim == 64) {
     if (win)
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, true, SB>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, true, SB, F8>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, false, SB>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, false, SB, F8>), grid, block, 0, stream, a);
   } else if (win) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, true, SB>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, true, SB, F8>), grid, block, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, false, SB>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, false, SB, F8>), grid, block, 0, stream, a);
   }
 }
 
-// Blocks per pipeline stage: PKV_PF_STAGE_BLOCKS = 2 or 4 (default kPfStageBlocks).
-void launch_prefill_bf16(unsigned grid, hipStream_t stream, const PrefillArgs& a, int head_dim) {
-  if (env_int("PKV_PF_STAGE_BLOCKS", kPfStageBlocks, 2, 4) == 4)
-    launch_prefill_bf16_sb<4>(grid, stream, a, head_dim);
+// Blocks per pipeline stage: PKV_PF_STAGE_BLOCKS = 2 or 4 (default kPfStageBlocks)
+// for bf16 caches; FP8 caches always take 4 (a 2-block FP8 stage at head_dim
+// 64 has fewer 16-byte pieces than threads).
+void launch_prefill_bf16(unsigned grid, hipStream_t stream, const PrefillArgs& a, int head_dim,
+                         bool fp8) {
+  if (fp8)
+    launch_prefill_bf16_sb<4, true>(grid, stream, a, head_dim);
+  else if (env_int("PKV_PF_STAGE_BLOCKS", kPfStageBlocks, 2, 4) == 4)
+    launch_prefill_bf16_sb<4, false>(grid, stream, a, head_dim);
   else
-    launch_prefill_bf16_sb<2>(grid, stream, a, head_dim);
+    launch_prefill_bf16_sb<2, false>(grid, stream, a, head_dim);
 }
 
 // ============================================================================ C ABI
+namespace {
+// Chunked prefill for a bf16 cache, or an FP8 one with tensor scales.
+pkv_status prefill_impl(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        const int32_t* query_start, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                        int32_t max_blocks_per_seq, int32_t max_context_len,
+                        int32_t max_query_len, float scale, int32_t window, bool fp8,
+                        float k_scale, float v_scale, float* out, hipStream_t stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0 || max_query_len < 0 || window < 0)
+    return PKV_ERR_INVALID;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  const int group = num_q_heads / num_kv_heads;
+  if (group > 16) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+    return PKV_ERR_INVALID;
+  PrefillArgs a;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.qstart = query_start;
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.qtp = kPfCols / group;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.scale_log2e = scale * k_scale * 1.4426950408889634f;
+  a.window = window;
+  a.out_scale = v_scale;
+  const int64_t tiles = (int64_t(max_query_len) + a.qtp - 1) / a.qtp;
+  const int64_t grid = tiles * num_seqs * num_kv_heads;
+  if (grid > 0x7FFFFFFF) return PKV_ERR_UNSUPPORTED;
+  a.tiles = static_cast<int>(tiles);
+  launch_prefill_bf16(static_cast<unsigned>(grid), stream, a, head_dim, fp8);
+  return launch_status();
+}
+}  // namespace
+
 extern "C" {
 
 pkv_status paged_block_table_update(int32_t* block_tables, int64_t table_elems,
@@ -2574,41 +2662,28 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
                                    int32_t max_context_len, int32_t max_query_len, float scale,
                                    int32_t window, pkv_dtype kv_dtype, float* out,
                                    hipStream_t stream) {
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
-      max_blocks_per_seq <= 0 || max_context_len < 0 || max_query_len < 0 || window < 0)
-    return PKV_ERR_INVALID;
-  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
-  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (kv_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-  const int group = num_q_heads / num_kv_heads;
-  if (group > 16) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+  return prefill_impl(q, k_cache, v_cache, block_tables, context_lens, query_start, num_seqs,
+                      num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
+                      max_context_len, max_query_len, scale, window, false, 1.0f, 1.0f, out,
+                      stream);
+}
+
+pkv_status paged_attention_prefill_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       const int32_t* query_start, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len,
+                                       int32_t max_query_len, float scale, int32_t window,
+                                       float k_scale, float v_scale, float* out,
+                                       hipStream_t stream) {
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return PKV_ERR_INVALID;
-  PrefillArgs a;
-  a.q = q;
-  a.kc = k_cache;
-  a.vc = v_cache;
-  a.tables = block_tables;
-  a.lens = context_lens;
-  a.qstart = query_start;
-  a.out = out;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.group = group;
-  a.qtp = kPfCols / group;
-  a.num_blocks = num_blocks;
-  a.max_blocks = max_blocks_per_seq;
-  a.max_ctx = max_context_len;
-  a.scale_log2e = scale * 1.4426950408889634f;
-  a.window = window;
-  const int64_t tiles = (int64_t(max_query_len) + a.qtp - 1) / a.qtp;
-  const int64_t grid = tiles * num_seqs * num_kv_heads;
-  if (grid > 0x7FFFFFFF) return PKV_ERR_UNSUPPORTED;
-  a.tiles = static_cast<int>(tiles);
-  launch_prefill_bf16(static_cast<unsigned>(grid), stream, a, head_dim);
-  return launch_status();
+  return prefill_impl(q, k_cache, v_cache, block_tables, context_lens, query_start, num_seqs,
+                      num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
+                      max_context_len, max_query_len, scale, window, true, k_scale, v_scale, out,
+                      stream);
 }
 
 }  // extern "C"

@@ -255,6 +255,14 @@ class PagedKV:
             qs_d = torch.from_numpy(qs).to(self.device)
             max_q = int(np.max(np.diff(qs))) if qs.size > 1 else 0
         max_ctx = int(self.lens.max()) if self.lens.size else 0
+        if self.dtype == "fp8":
+            capi.paged_attention_prefill_fp8(q, self.k_cache, self.v_cache, self.tables_d,
+                                             self.lens_d, qs_d, out, num_kv_heads=self.num_kv_heads,
+                                             num_blocks=self.num_blocks, max_context_len=max_ctx,
+                                             max_query_len=max_q, scale=scale,
+                                             k_scale=self.k_scale, v_scale=self.v_scale,
+                                             window=self.window, stream=stream.cuda_stream)
+            return out
         capi.paged_attention_prefill(q, self.k_cache, self.v_cache, self.tables_d, self.lens_d, qs_d,
                                      out, num_kv_heads=self.num_kv_heads, num_blocks=self.num_blocks,
                                      max_context_len=max_ctx, max_query_len=max_q, scale=scale,
