@@ -1813,12 +1813,13 @@ void prefill_bf16_kernel(PrefillArgs a) {
   bool bad = false;
 
   // Stage loader: thread tid moves pieces 512 u + tid (u < PT) of the stage's
-  // four tiles (block 0 K, block 0 V, block 1 K, block 1 V); a wavefront's 64
-  // pieces lie in one tile, so the tile (and its block id, read once per
-  // stage through the scalar cache) is wave-uniform.  V slots outside
-  // [t_lo, L) are zeroed on the way (they may hold anything).  An FP8 run
-  // expands to two bf16 runs: st[2u] and st[2u + 1].
-  uint4 st[F8 ? 2 * PT_G : PT];
+  // tiles (block 0 K, block 0 V, block 1 K, ...); a wavefront's 64 pieces lie
+  // in one tile, so the tile (and its block id, read once per stage through
+  // the scalar cache) is wave-uniform.  V slots outside [t_lo, L) are zeroed
+  // when the pieces go into LDS, a trip after their loads (they may hold
+  // anything; masking them at load time would wait for the loads at once).
+  // An FP8 run expands to two bf16 runs as it goes into LDS.
+  uint4 st[PT_G];
   auto gload = [&](int s) {
     int ph[SB], by[SB];
 #pragma unroll
@@ -1840,7 +1841,6 @@ void prefill_bf16_kernel(PrefillArgs a) {
       const int first = 64 * kPfWaves * u + 64 * wave;
       const int tile = first / TILE_PIECES_G;
       const int off0 = (first % TILE_PIECES_G) * 16;
-      const int rel = SB * s + (tile >> 1);
       int phys = 0, bytes = 0;  // selected, not indexed: ph and by stay in registers
 #pragma unroll
       for (int k = 0; k < SB; ++k)
@@ -1850,36 +1850,22 @@ void prefill_bf16_kernel(PrefillArgs a) {
         }
       const char* base = ((tile & 1) ? vc : kc) + (bytes ? int64_t(phys) * block_bytes : 0) + off0;
       const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, bytes ? bytes - off0 : 0);
-      uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, 0));
-      uint4 y = make_uint4(0u, 0u, 0u, 0u);  // FP8: the second bf16 piece
-      if constexpr (F8) {
-        y = e4m3x8_to_bf16x8(x.z, x.w);
-        x = e4m3x8_to_bf16x8(x.x, x.y);
-      }
-      if (tile & 1) {
-        // V piece: lane l of a 1 KiB run holds tokens 4 (l / 16) .. + 3
-        const int t0 = (i0 + rel) * kBlock + 4 * grp;
-        if (t0 < t_lo || t0 + 4 > L) {
-          auto in = [&](int t) { return t < L && t >= t_lo; };
-          const uint32_t m01 = (in(t0) ? 0x0000FFFFu : 0u) | (in(t0 + 1) ? 0xFFFF0000u : 0u);
-          const uint32_t m23 = (in(t0 + 2) ? 0x0000FFFFu : 0u) | (in(t0 + 3) ? 0xFFFF0000u : 0u);
-          x.x &= m01;
-          x.y &= m23;
-          x.z &= m01;
-          x.w &= m23;
-          if constexpr (F8) {
-            y.x &= m01;
-            y.y &= m23;
-            y.z &= m01;
-            y.w &= m23;
-          }
-        }
-      }
-      if constexpr (F8) {
-        st[2 * u] = x;
-        st[2 * u + 1] = y;
-      } else {
-        st[u] = x;
+      st[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, 0));
+    }
+  };
+  // V slots of stage s outside [t_lo, L): lane l of a 1 KiB V run holds
+  // tokens 4 (l / 16) .. + 3 of its block
+  auto vmask = [&](int s, int tile, uint4& x) {
+    if (tile & 1) {
+      const int t0 = (i0 + SB * s + (tile >> 1)) * kBlock + 4 * grp;
+      if (t0 < t_lo || t0 + 4 > L) {
+        auto in = [&](int t) { return t < L && t >= t_lo; };
+        const uint32_t m01 = (in(t0) ? 0x0000FFFFu : 0u) | (in(t0 + 1) ? 0xFFFF0000u : 0u);
+        const uint32_t m23 = (in(t0 + 2) ? 0x0000FFFFu : 0u) | (in(t0 + 3) ? 0xFFFF0000u : 0u);
+        x.x &= m01;
+        x.y &= m23;
+        x.z &= m01;
+        x.w &= m23;
       }
     }
   };
@@ -1888,15 +1874,20 @@ void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
     for (int u = 0; u < PT_G; ++u) {
       const int first = 64 * kPfWaves * u + 64 * wave;  // same run as in gload
+      const int tile = first / TILE_PIECES_G;
       if constexpr (F8) {
         // FP8 run i of the tile holds bf16 pieces 2i and 2i + 1 of each lane
-        unsigned char* d = sb + (first / TILE_PIECES_G) * TILE_BYTES +
-                           2048 * ((first % TILE_PIECES_G) / 64) + lane * 16;
-        *reinterpret_cast<uint4*>(d) = st[2 * u];
-        *reinterpret_cast<uint4*>(d + 1024) = st[2 * u + 1];
+        const uint4 w = st[u];
+        uint4 x = e4m3x8_to_bf16x8(w.x, w.y), y = e4m3x8_to_bf16x8(w.z, w.w);
+        vmask(s, tile, x);
+        vmask(s, tile, y);
+        unsigned char* d = sb + tile * TILE_BYTES + 2048 * ((first % TILE_PIECES_G) / 64) + lane * 16;
+        *reinterpret_cast<uint4*>(d) = x;
+        *reinterpret_cast<uint4*>(d + 1024) = y;
       } else {
-        *reinterpret_cast<uint4*>(sb + (first / TILE_PIECES) * TILE_BYTES +
-                                  (first % TILE_PIECES) * 16 + lane * 16) = st[u];
+        uint4 x = st[u];
+        vmask(s, tile, x);
+        *reinterpret_cast<uint4*>(sb + tile * TILE_BYTES + (first % TILE_PIECES) * 16 + lane * 16) = x;
       }
     }
   };
