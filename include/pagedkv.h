@@ -69,9 +69,10 @@
  * A byte is an OCP FP8 E4M3 code (1 sign, 4 exponent bits with bias 7, 3
  * mantissa bits, subnormals m * 2^-9, no infinity, 0x7F/0xFF = NaN, largest
  * finite 448) standing for its value times the tensor's scale (one scale
- * for K, one for V).  ["KV cache: la memoria de trabajo...", «Cuantización
- * del KV cache»: an 8-bit cache halves its size and the bytes read per
- * step, and FP8 is described as safe almost always; the format and the
+ * for K, one for V).  ["KV cache: la memoria de trabajo...", «Trucos para
+ * que el cuaderno sea más fino»: an 8-bit cache halves its size and the
+ * bytes read per step; "PagedAttention por dentro", «Trampas y mitos
+ * comunes»: FP8 is described as safe almost always.  The format and the
  * scaling are this library's reading.]
  *
  * Token position p of sequence s (0-based) lives in physical block
@@ -519,8 +520,8 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
 
 /* Chunked prefill over an FP8 E4M3 cache: paged_attention_prefill's result
  * for K, V = code value x k_scale, v_scale ["KV cache: la memoria de
- * trabajo...", «Cuantización del KV cache»: the cache is read at half the
- * bytes].  q is bf16, out fp32, as above.  The codes are expanded to bf16
+ * trabajo...", «Trucos para que el cuaderno sea más fino»: the cache is
+ * read at half the bytes].  q is bf16, out fp32, as above.  The codes are expanded to bf16
  * exactly on their way into LDS; k_scale folds into the score scale and
  * v_scale into the output.  Scales must be positive and finite, else
  * PKV_ERR_INVALID; other arguments and errors as paged_attention_prefill. */

@@ -1,9 +1,10 @@
 """OCP FP8 E4M3 ("E4M3FN") codes for the quantised KV cache.
 
-"KV cache: la memoria de trabajo ..." (blog.lo0.es), "Cuantización del KV
-cache" and "Trucos para que el cuaderno sea mas fino": the cache can be
-stored in 8 bits, which halves its size and the bytes each decode step
-reads, and FP8 is described there as safe almost always.  The pages fix
+"KV cache: la memoria de trabajo ..." (blog.lo0.es), "Trucos para que el
+cuaderno sea mas fino": the cache can be stored in 8 bits, which halves its
+size and the bytes each decode step reads; "PagedAttention por dentro"
+(blog.lo0.es), "Trampas y mitos comunes": an FP8 cache is described as safe
+almost always.  The pages fix
 neither the 8-bit format nor how values are scaled.  Readings:
   - the format is OCP 8-bit floating point E4M3: 1 sign bit, 4 exponent
     bits with bias 7, 3 mantissa bits; exponent field 0 holds the

@@ -2,37 +2,48 @@
 // entry points that launch them.
 //
 // Kernels:
-//   table_update   block-table deltas into the device-resident tables
-//   kv_write       scatter of new tokens' K/V through the slot mapping
-//   copy_blocks    whole-block copies for copy-on-write
-//   decode_bf16    PagedAttention decode, bf16 cache, matrix cores
-//   decode_f32     PagedAttention decode, fp32 cache, vector ALU
-//   lse_reduce     log-sum-exp merge of partitions
+//   table_update      block-table (and length) deltas into device-resident tables
+//   kv_write          scatter of new tokens' K/V through the slot mapping
+//   append            table deltas and the scatter in one launch (a decode step)
+//   kv_write_fp8      the scatter with E4M3 quantisation
+//   copy_blocks       whole-block copies inside a cache (copy-on-write)
+//   swap_blocks       whole-block copies between a cache and a pinned-host swap space
+//   decode_bf16_cu    decode attention, default form: the block list split evenly
+//                     over the CUs, partial states folded inside each CU and merged
+//                     across CUs in the same launch; bf16 or FP8 cache, optional
+//                     sliding window
+//   decode_bf16_balanced  the same split per wavefront (fallback form)
+//   decode_bf16 / decode_f32 + lse_reduce  fixed split-K partitions
+//   prefill_bf16      chunked prefill (multi-query, causal) on the matrix cores,
+//                     bf16 or FP8 cache, optional sliding window
+//   stream_read       plain streaming read, the bandwidth reference
 //
 // Sources: "PagedAttention por dentro" (blog.lo0.es), sections "La tabla de
-// paginas (block table)", "Copy-on-write para sampling paralelo" and "El
-// kernel CUDA" (attention walks the context in block-aligned chunks, each
-// located through the table); "Como funciona realmente vLLM"
-// (alexanderzelada.com), "Que es el mecanismo de atencion" and
-// "PagedAttention: ..." (scattered blocks are read in place through the
-// table, never gathered into a contiguous buffer).
+// paginas (block table)", "Copy-on-write para sampling paralelo", "El kernel
+// CUDA" (attention walks the context in block-aligned chunks, each located
+// through the table), "Chunked prefill integrado con paged KV", "Prefix
+// caching cross-session", "Evicción y preemption" and "Sliding window
+// attention"; "Como funciona realmente vLLM" (alexanderzelada.com), "Que es
+// el mecanismo de atencion" and "PagedAttention: ..." (scattered blocks are
+// read in place through the table, never gathered into a contiguous buffer);
+// "KV cache: la memoria de trabajo..." (blog.lo0.es), «Trucos para que el
+// cuaderno sea más fino» (an 8-bit cache).
 //
-// Decode design (bf16).  One wavefront (64 lanes) owns one
-// (sequence, kv head, partition) work item and walks that partition's
-// blocks through the block table.  The cache tile order (pagedkv.h) makes
-// lane l's 16-byte piece j of a tile exactly its matrix-core operand:
+// Matrix-core layout (bf16).  The cache tile order (pagedkv.h) makes lane l's
+// 16-byte piece j of a tile exactly its matrix-core operand:
 //   K piece j = 8 channels 32j + 8(l/16) .. +8 of token l%16
 //       -> A operand of v_mfma_f32_16x16x32_bf16 (rows = tokens, k = channels)
 //   V piece j = 4 tokens 4(l/16) .. +4 at channel 32j + l%16 (low half) and
 //       channel 32j + 16 + l%16 (high half)
 //       -> B operands of v_mfma_f32_16x16x16_bf16 (k = tokens, cols = channels)
-// so each load instruction of the wave reads 1 KiB of contiguous memory and
-// nothing passes through LDS or gets reshuffled.  Scores come out as
-// S^T[token 4(l/16)+i][query head l%16] -- exactly the A-operand layout of
-// the P.V product (rows = heads, k = tokens) -- so up to 16 query heads of a
-// kv head share one pass over the tile.  Softmax weights are split into a
-// bf16 high part and a bf16 residual so that P.V keeps ~16 bits of weight
-// precision; accumulation is fp32 throughout.
+// so each load instruction of a wavefront reads 1 KiB of contiguous memory
+// and nothing is reshuffled.  Scores come out as S^T[token 4(l/16)+i][query
+// head l%16] -- exactly the A-operand layout of the P.V product (rows =
+// heads, k = tokens) -- so up to 16 query heads of a kv head share one pass
+// over the tile.  Softmax weights are split into a bf16 high part and a bf16
+// residual so that P.V keeps ~16 bits of weight precision; accumulation is
+// fp32 throughout.  An FP8 tile holds the same pieces at one byte per
+// element, a lane's pieces paired into 16 bytes.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
