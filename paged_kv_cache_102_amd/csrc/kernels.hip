@@ -1056,6 +1056,7 @@ __global__ void kv_write_fp8_kernel(const T* __restrict__ k_new, const T* __rest
 constexpr int kCuWaves = 8;
 constexpr int kCuLdsBytes = 160 * 1024;
 constexpr int kCuChunksMax = 64;                           // chunks per CU
+constexpr float kCuRescale = 8.0f;                         // lazy-max threshold (log2)
 constexpr int kCuSlots = 2 * (kCuWaves + kCuChunksMax);    // partial segments per CU
 constexpr int kCuHeaderBytes = 64 + kCuSlots * 3 * 4;      // counters + slot metadata
 
@@ -1388,14 +1389,16 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
       sv[r] = (tb + r < c_L && tb + r >= wlo) ? s[r] * a.scale_log2e : -INFINITY;
     float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mloc = group_max(mloc);
-    const float mnew = fmaxf(m, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sv[r] - mnew);
-    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m = mnew;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+    // lazy reference: raised only when a tile's max exceeds it by more than
+    // kCuRescale (log2 domain), so weights stay below 2^kCuRescale and most
+    // tiles skip rescaling the accumulators; the ratios do not depend on the
+    // reference, and the merges carry it with each partial state.  (Every
+    // tile holds a visible token, so a segment's first tile sets it.)
+    const bool raise = mloc > m + kCuRescale;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m - mloc) : 1.0f;
+      m = raise ? mloc : m;
+      lsum *= alpha;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float ar = __shfl(alpha, grp * 4 + r);
@@ -1403,6 +1406,10 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
         for (int n = 0; n < NT; ++n) o[n][r] *= ar;
       }
     }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sv[r] - m);
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
     uint32_t hi01, lo01, hi23, lo23;
     split_bf16x2(p[0], p[1], hi01, lo01);
     split_bf16x2(p[2], p[3], hi23, lo23);
