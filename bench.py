@@ -124,8 +124,8 @@ def prefill_measure(dev, reps: int = 20, cache: str = "bf16"):
     shape with 1024..2048 cached tokens each take a 512-token chunk, causal
     inside the chunk, over a bf16 or an FP8 (E4M3, tensor scales) cache.
     Returns the kernel time and its rate against the bf16 matrix-core peak
-    (4 * D flops per (query row, attended token); the products run in bf16
-    for both caches)."""
+    (4 * D flops per (query row, attended token); Q.K^T runs on bf16 and
+    P.V on f16 operands, 16-bit products priced at the same peak)."""
     import numpy as np
     import torch
     from paged_kv_cache_102_amd.driver import PagedKV, replay_prefill
@@ -167,7 +167,7 @@ def prefill_measure(dev, reps: int = 20, cache: str = "bf16"):
     return {"workload": "8 sequences x 512-token chunks on 1024..2048 cached tokens, 32 q / 8 kv heads, "
                         "head_dim 128, " + ("FP8 E4M3 cache" if f8 else "bf16"),
             "kernel": f"prefill_bf16_kernel<128,false,4{',F8' if f8 else ''}> (8 wavefronts, 256 score "
-                      "columns, 4-block K/V stages in LDS" + (", codes expanded to bf16 on the way in)"
+                      "columns, 4-block K/V stages in LDS, P.V on f16" + (", codes expanded on the way in)"
                                                             if f8 else ")"),
             "ms": round(ms, 4),
             "tflops": round(tflops, 2), "bound": "mfma", "peak_tflops": BF16_MFMA_PEAK_TFLOPS,

@@ -505,7 +505,11 @@ pkv_status paged_attention_decode_fp8(const void* q, const void* k_cache, const 
  *   out: device fp32 [T][num_q_heads][head_dim], written for every chunk row
  *   max_query_len: host-side upper bound of n_s (sizes the grid)
  * bf16 caches (kv_dtype PKV_BF16; FP8: paged_attention_prefill_fp8);
- * head_dim 64 or 128; at most 16 query heads per kv head.
+ * head_dim 64 or 128; at most 16 query heads per kv head.  Precision: fp32
+ * accumulation; the softmax weights and V enter P.V as f16 (11 significant
+ * bits), and a workgroup whose stage holds a V element beyond f16's range
+ * (|v| >= 65536, inf, NaN) reruns with bf16 operands, so every value of
+ * the cache is handled.
  * Errors: as paged_attention_decode (PKV_ERR_INVALID / PKV_ERR_UNSUPPORTED);
  * on the device a sequence with a bad length, n_s > L, or a table entry
  * outside [0, num_blocks) gets NaN rows instead of out-of-range reads. */
@@ -521,8 +525,8 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
 /* Chunked prefill over an FP8 E4M3 cache: paged_attention_prefill's result
  * for K, V = code value x k_scale, v_scale ["KV cache: la memoria de
  * trabajo...", «Trucos para que el cuaderno sea más fino»: the cache is
- * read at half the bytes].  q is bf16, out fp32, as above.  The codes are expanded to bf16
- * exactly on their way into LDS; k_scale folds into the score scale and
+ * read at half the bytes].  q is bf16, out fp32, as above.  The codes are expanded
+ * exactly on their way into LDS (K to bf16, V to f16); k_scale folds into the score scale and
  * v_scale into the output.  Scales must be positive and finite, else
  * PKV_ERR_INVALID; other arguments and errors as paged_attention_prefill. */
 pkv_status paged_attention_prefill_fp8(const void* q, const void* k_cache, const void* v_cache,

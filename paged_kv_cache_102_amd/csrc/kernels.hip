@@ -40,9 +40,9 @@
 // and nothing is reshuffled.  Scores come out as S^T[token 4(l/16)+i][query
 // head l%16] -- exactly the A-operand layout of the P.V product (rows =
 // heads, k = tokens) -- so up to 16 query heads of a kv head share one pass
-// over the tile.  Softmax weights are split into a bf16 high part and a bf16
-// residual so that P.V keeps ~16 bits of weight precision; accumulation is
-// fp32 throughout.  An FP8 tile holds the same pieces at one byte per
+// over the tile.  In decode, softmax weights are split into a bf16 high part
+// and a bf16 residual so that P.V keeps ~16 bits of weight precision (the
+// prefill takes them, and V, as f16); accumulation is fp32 throughout.  An FP8 tile holds the same pieces at one byte per
 // element, a lane's pieces paired into 16 bytes.
 #include <hip/hip_runtime.h>
 
@@ -64,6 +64,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ in-tile order
 __host__ __device__ inline int k_elem(int t, int d) { return (d >> 3) * 128 + t * 8 + (d & 7); }
@@ -100,6 +102,18 @@ __device__ inline void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo
   hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
   const f32x2 rest = {a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u)};
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
+}
+
+// Two bf16 -> two f16, exact for magnitudes below 65520 (8 significant bits
+// fit in 11; under 2^-14 f16 is subnormal, within 2^-25 of the value).
+__device__ inline uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const f32x2 f = {__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+// Bit 15 / 31 set where a bf16 half has magnitude >= 65536 (0x4780), inf or
+// NaN: the halves that have no f16 equal.  The add cannot carry across halves.
+__device__ inline uint32_t bf16x2_beyond_f16(uint32_t w) {
+  return ((w & 0x7FFF7FFFu) + 0x38803880u) & 0x80008000u;
 }
 
 // Small index inputs of the cache-update kernels (slots, table deltas, block
@@ -965,6 +979,19 @@ __device__ inline uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   r.w = e4m3x2_to_bf16x2<true>(hi);
   return r;
 }
+// The same 8 codes as f16 (v_cvt_scalef32_pk_f16_fp8, scale 1)
+template <bool HIGH>
+__device__ inline uint32_t e4m3x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HIGH));
+}
+__device__ inline uint4 e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
+  uint4 r;
+  r.x = e4m3x2_to_f16x2<false>(lo);
+  r.y = e4m3x2_to_f16x2<true>(lo);
+  r.z = e4m3x2_to_f16x2<false>(hi);
+  r.w = e4m3x2_to_f16x2<true>(hi);
+  return r;
+}
 // Byte offset in an FP8 tile of lane `lane`'s 8-byte piece `j` (the codes of
 // its bf16 operand piece j).  Pieces 2i and 2i + 1 of all lanes fill bytes
 // [1024 i, 1024 i + 1024) as 64 lanes x 16 bytes, so one 16-byte load per
@@ -1649,18 +1676,20 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
 // One workgroup of 8 wavefronts per (sequence, kv head, tile of query
 // positions), two per SIMD.  The tile's score columns are (position,
 // head-in-group) pairs, 256 of them (32 per wavefront, as two 16-column MFMA
-// tiles), so 256 / g positions per tile.  The K and V tiles of two consecutive blocks
-// (one stage) are loaded once per workgroup into LDS (double-buffered, the
-// next stage's global loads in flight during this stage's compute) and every
-// wavefront reads them from there:
+// tiles), so 256 / g positions per tile.  The K and V tiles of SB consecutive
+// blocks (one stage) are loaded once per workgroup into LDS (double-buffered,
+// the next stage's global loads in flight during this stage's compute) and
+// every wavefront reads them from there:
 //   S^T = K . Q^T   v_mfma_f32_16x16x32_bf16, A = K piece j (16 tokens x 32
 //                   channels, the cache's lane order), B = Q^T chunk j;
-//   O  += P . V     v_mfma_f32_16x16x32_bf16 over the stage's 32 tokens: a
-//                   lane's k-index i < 4 is token 4(l/16)+i of the first
-//                   block, i >= 4 the same token of the second block -- the
-//                   layout S^T comes out in, and the halves of the V tile's
-//                   lane pieces of the two blocks;
-// with P carried as a bf16 high part plus a bf16 residual.  The running max
+//   O  += P . V     v_mfma_f32_16x16x32_f16 over each pair of blocks (32
+//                   tokens): a lane's k-index i < 4 is token 4(l/16)+i of the
+//                   first block, i >= 4 the same token of the second block --
+//                   the layout S^T comes out in, and the halves of the V
+//                   tile's lane pieces of the two blocks;
+// with P and V as f16 (V converted on its way into LDS; a bf16 V element
+// beyond f16's range makes the workgroup run again with P as a bf16 high
+// part plus residual and V as bf16).  The running max
 // is raised only when a block's max exceeds it by more than 2^8 (the
 // normaliser uses the same reference, so the result is unchanged, and the
 // accumulator is rescaled rarely).
@@ -1686,6 +1715,10 @@ constexpr int kPfColTiles = 2;                       // 16-column tiles per wave
 constexpr int kPfCols = kPfWaves * kPfColTiles * 16;  // score columns per workgroup
 constexpr float kPfRescale = 8.0f;                   // lazy max threshold (log2 domain)
 constexpr int kPfStageBlocks = 4;                    // default blocks per pipeline stage
+template <bool B>
+struct PfF16 {  // P.V operand type of a prefill pass: f16 (true) or bf16 high + residual
+  static constexpr bool value = B;
+};
 
 // SB: blocks per pipeline stage (even: P.V takes them in pairs).  F8: the
 // cache holds FP8 E4M3 codes; each lane's 16 codes of a 1 KiB run are
@@ -1887,16 +1920,29 @@ void prefill_bf16_kernel(PrefillArgs a) {
       }
     }
   };
-  auto lwrite = [&](int s) {
+  // V goes into LDS as f16 when P.V runs on f16 operands (H); a bf16 V
+  // element with no f16 equal is noted in `wide` (the workgroup then runs
+  // again with bf16 operands)
+  uint32_t wide = 0;
+  auto lwrite = [&](int s, auto h) {
+    constexpr bool H = decltype(h)::value;
     unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
 #pragma unroll
     for (int u = 0; u < PT_G; ++u) {
       const int first = 64 * kPfWaves * u + 64 * wave;  // same run as in gload
       const int tile = first / TILE_PIECES_G;
       if constexpr (F8) {
-        // FP8 run i of the tile holds bf16 pieces 2i and 2i + 1 of each lane
+        // FP8 run i of the tile holds operand pieces 2i and 2i + 1 of each
+        // lane (E4M3 values are exact in both bf16 and f16)
         const uint4 w = st[u];
-        uint4 x = e4m3x8_to_bf16x8(w.x, w.y), y = e4m3x8_to_bf16x8(w.z, w.w);
+        uint4 x, y;
+        if (H && (tile & 1)) {
+          x = e4m3x8_to_f16x8(w.x, w.y);
+          y = e4m3x8_to_f16x8(w.z, w.w);
+        } else {
+          x = e4m3x8_to_bf16x8(w.x, w.y);
+          y = e4m3x8_to_bf16x8(w.z, w.w);
+        }
         vmask(s, tile, x);
         vmask(s, tile, y);
         unsigned char* d = sb + tile * TILE_BYTES + 2048 * ((first % TILE_PIECES_G) / 64) + lane * 16;
@@ -1904,17 +1950,19 @@ void prefill_bf16_kernel(PrefillArgs a) {
         *reinterpret_cast<uint4*>(d + 1024) = y;
       } else {
         uint4 x = st[u];
-        vmask(s, tile, x);
+        vmask(s, tile, x);  // first: slots outside the context may hold anything
+        if (H && (tile & 1)) {
+          wide |= bf16x2_beyond_f16(x.x) | bf16x2_beyond_f16(x.y) | bf16x2_beyond_f16(x.z) |
+                  bf16x2_beyond_f16(x.w);
+          x = make_uint4(bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
+                         bf16x2_to_f16x2(x.w));
+        }
         *reinterpret_cast<uint4*>(sb + tile * TILE_BYTES + (first % TILE_PIECES) * 16 + lane * 16) = x;
       }
     }
   };
 
   f32x4 o[NQ][NT];
-#pragma unroll
-  for (int t = 0; t < NQ; ++t)
-#pragma unroll
-    for (int k = 0; k < NT; ++k) o[t][k] = f32x4{0.f, 0.f, 0.f, 0.f};
   // running max per column (log2 domain, scaled; a finite floor, so that a
   // column with nothing visible yet gets weights exp2(-inf - floor) = 0),
   // and the normalisers: row sums of the same bf16 weight parts that P.V
@@ -1922,11 +1970,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
   // output layout, so numerator and denominator share every rounding
   float m[NQ];
   f32x4 lacc[NQ];
-#pragma unroll
-  for (int t = 0; t < NQ; ++t) {
-    m[t] = -1e30f;
-    lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  const f16x8 ones16 = __builtin_bit_cast(f16x8, make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
   // weights exp2(cs * s - m) with cs >= 0: a negative scale negates Q
   // instead (exact in bf16), so the scaled max is the raw max times cs
@@ -1945,12 +1989,14 @@ void prefill_bf16_kernel(PrefillArgs a) {
       }
   }
 
-  // weights of the stage being processed (bf16 high parts and residuals)
+  // weights of the stage being processed: f16 pairs (H), else bf16 high
+  // parts and residuals
   uint32_t phi[NQ][2 * SB], plo[NQ][2 * SB];
   // O += P . V over each pair of blocks of stage s (k < 4: the pair's first
   // block, k >= 4: its second); each V piece is read once and used by all
   // column tiles
-  auto pv = [&](int s) {
+  auto pv = [&](int s, auto h) {
+    constexpr bool H = decltype(h)::value;
     const unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
 #pragma unroll
     for (int pp = 0; pp < SB / 2; ++pp) {
@@ -1958,6 +2004,18 @@ void prefill_bf16_kernel(PrefillArgs a) {
       for (int j = 0; j < NJ; ++j) {
         const uint4 v0 = *reinterpret_cast<const uint4*>(sb + (4 * pp + 1) * TILE_BYTES + 1024 * j + lane * 16);
         const uint4 v1 = *reinterpret_cast<const uint4*>(sb + (4 * pp + 3) * TILE_BYTES + 1024 * j + lane * 16);
+        if constexpr (H) {
+          const f16x8 vlo = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+          const f16x8 vhi = __builtin_bit_cast(f16x8, make_uint4(v0.z, v0.w, v1.z, v1.w));
+#pragma unroll
+          for (int t = 0; t < NQ; ++t) {
+            const f16x8 ph = __builtin_bit_cast(f16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
+                                                                  phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
+            o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vlo, o[t][2 * j], 0, 0, 0);
+            o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vhi, o[t][2 * j + 1], 0, 0, 0);
+          }
+          continue;
+        }
         const bf16x8 vlo = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
         const bf16x8 vhi = __builtin_bit_cast(bf16x8, make_uint4(v0.z, v0.w, v1.z, v1.w));
 #pragma unroll
@@ -1974,6 +2032,12 @@ void prefill_bf16_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int t = 0; t < NQ; ++t) {
+        if constexpr (H) {
+          const f16x8 ph = __builtin_bit_cast(f16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
+                                                                phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
+          lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, ones16, lacc[t], 0, 0, 0);
+          continue;
+        }
         const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
                                                                 phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
         const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(plo[t][4 * pp], plo[t][4 * pp + 1],
@@ -1985,7 +2049,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
   };
 
   // scores of stage s, softmax update, weights into phi / plo
-  auto score = [&](int s) {
+  auto score = [&](int s, auto h) {
+    constexpr bool H = decltype(h)::value;
     const unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
     const int tb0 = (i0 + SB * s) * kBlock;  // first position of the stage
     // scores of all blocks of the stage for every column tile
@@ -2055,7 +2120,10 @@ void prefill_bf16_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 2 * SB; ++e) {
-        split_bf16x2(p[2 * e], p[2 * e + 1], phi[t][e], plo[t][e]);
+        if constexpr (H)
+          phi[t][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p[2 * e], p[2 * e + 1]}), f16x2));
+        else
+          split_bf16x2(p[2 * e], p[2 * e + 1], phi[t][e], plo[t][e]);
       }
     }
   };
@@ -2064,17 +2132,42 @@ void prefill_bf16_kernel(PrefillArgs a) {
   // barrier makes stage s visible and frees buffer (s + 1) % 2 (every
   // wavefront has finished stage s - 1), which then takes stage s + 1 from
   // registers while stage s + 2's global loads go out.
-  gload(0);
-  lwrite(0);
-  gload(1);
-  for (int s = 0; s < nst; ++s) {
-    __syncthreads();
-    if (s + 1 < nst) {
-      lwrite(s + 1);
-      gload(s + 2);
+  auto run = [&](auto h) {
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) {
+#pragma unroll
+      for (int k = 0; k < NT; ++k) o[t][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m[t] = -1e30f;
+      lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    score(s);
-    pv(s);
+    gload(0);
+    lwrite(0, h);
+    gload(1);
+    for (int s = 0; s < nst; ++s) {
+      __syncthreads();
+      if (s + 1 < nst) {
+        lwrite(s + 1, h);
+        gload(s + 2);
+      }
+      score(s, h);
+      pv(s, h);
+    }
+  };
+  // P.V on f16 operands: the weights lie in [0, 2^8] and round to 11
+  // significant bits (bf16 would keep 8, and needs a residual product to
+  // stay inside the tolerance).  A bf16 cache can hold V elements that f16
+  // cannot; when a stage held one, the workgroup runs again with bf16
+  // operands (the weights as high part plus residual).
+  run(PfF16<true>{});
+  if constexpr (!F8) {
+    __shared__ int s_wide[kPfWaves];
+    const bool mine = __builtin_amdgcn_ballot_w64(wide != 0) != 0;
+    if (lane == 0) s_wide[wave] = mine;
+    __syncthreads();  // also: every wavefront is done with the last stage's LDS
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < kPfWaves; ++w) any |= s_wide[w];
+    if (any) run(PfF16<false>{});
   }
 
 #pragma unroll

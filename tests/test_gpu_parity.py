@@ -301,6 +301,46 @@ def test_prefill_chunks_vs_oracle(Hq, Hkv, D, seed):
         assert np.max(np.abs(dout[b] - got[qstart[b]])) <= 2e-3
 
 
+def test_prefill_v_beyond_f16_range():
+    """P.V runs on f16 operands; a bf16 V element that f16 cannot hold
+    (65536, -2^20) sends its workgroup through the bf16 form, which still
+    matches the oracle (to 2e-3 relative on the rows that see it); the other
+    sequences keep the f16 form and the absolute tolerance."""
+    from oracle import attention as oatt
+    from oracle.slots import plan_append
+    from tests.gpu_parity import to_device
+    Hq, Hkv, D, B = 8, 2, 128, 4
+    w = synth.small_random(131, num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           dtype="bf16", max_len=200, append=48)
+    p = _pair(w)
+    rng = np.random.default_rng(131)
+    counts = np.array([40, 48, 1, 17], np.int64)
+    T = int(counts.sum())
+    k_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    v_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    q = synth.round_bf16_bits(rng.standard_normal((T, Hq, D)).astype(np.float32))
+    big = synth.round_bf16_bits(np.array([65536.0, -2.0 ** 20], np.float32))
+    v_new[40 + 3, 1, 5] = big[0]    # sequence 1, kv head 1
+    v_new[40 + 30, 1, 77] = big[1]
+    slots, _, cows = plan_append(p.ora.pool, p.ora.tables, p.ora.lens, counts)
+    p.ora.cache.copy_blocks(cows)
+    p.ora.cache.write(k_new, v_new, slots)
+    p.kv.append(to_device(k_new), to_device(v_new), counts.astype(np.int32))
+    qstart = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    print(f"[prefill wide V] counts={counts.tolist()}", flush=True)
+    out = p.kv.prefill_attention(to_device(q), qstart, w.spec.scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    exp = oatt.prefill(q, p.ora.cache, p.ora.tables, p.ora.lens, qstart, Hq, Hkv, w.spec.scale)
+    assert np.isfinite(got).all()
+    assert np.max(np.abs(exp[40:88, 4:8])) > 1e3   # the wide values reach the output
+    rel = np.abs(got - exp) / np.maximum(1.0, np.abs(exp))
+    assert float(np.max(rel)) <= 2e-3
+    others = np.r_[0:40, 88:T]
+    assert float(np.max(np.abs(got[others] - exp[others]))) <= 2e-3
+    assert float(np.max(np.abs(got[40:88, 0:4] - exp[40:88, 0:4]))) <= 2e-3
+
+
 def test_prefill_bad_rows_are_nan():
     """A chunk longer than its context, or a table entry outside the pool,
     gives NaN rows for that sequence only."""
