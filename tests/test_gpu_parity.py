@@ -301,6 +301,42 @@ def test_prefill_chunks_vs_oracle(Hq, Hkv, D, seed):
         assert np.max(np.abs(dout[b] - got[qstart[b]])) <= 2e-3
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+def test_scales_vs_oracle(scale):
+    """The softmax scale is any real: a negative one (the prefill negates Q
+    instead), zero (every visible position weighs the same) and a large one,
+    through decode (every split form) and prefill, against the oracle."""
+    from oracle import attention as oatt
+    from oracle.slots import plan_append
+    from tests.gpu_parity import to_device
+    Hq, Hkv, D, B = 8, 2, 128, 6
+    w = synth.small_random(141, num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           dtype="bf16", max_len=400, append=40, fixed=[1, 16, 17])
+    p = _pair(w)
+    print(f"[scale] {scale} decode", flush=True)
+    exp = oatt.decode(w.q, p.ora.cache, p.ora.tables, p.ora.lens, Hq, Hkv, scale)
+    for ps in (0, 32, 512):
+        got = p.kv.decode(p.q, scale, partition_size=ps).cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all()
+        assert float(np.max(np.abs(got - exp))) <= 2e-3, ps
+    rng = np.random.default_rng(141)
+    counts = np.array([40, 1, 0, 33, 16, 17], np.int64)
+    T = int(counts.sum())
+    k_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    v_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    q = synth.round_bf16_bits(rng.standard_normal((T, Hq, D)).astype(np.float32))
+    slots, _, cows = plan_append(p.ora.pool, p.ora.tables, p.ora.lens, counts)
+    p.ora.cache.copy_blocks(cows)
+    p.ora.cache.write(k_new, v_new, slots)
+    p.kv.append(to_device(k_new), to_device(v_new), counts.astype(np.int32))
+    qstart = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    print(f"[scale] {scale} prefill counts={counts.tolist()}", flush=True)
+    got = p.kv.prefill_attention(to_device(q), qstart, scale).cpu().numpy().astype(np.float64)
+    exp = oatt.prefill(q, p.ora.cache, p.ora.tables, p.ora.lens, qstart, Hq, Hkv, scale)
+    assert np.isfinite(got).all()
+    assert float(np.max(np.abs(got - exp))) <= 2e-3
+
+
 def test_prefill_v_beyond_f16_range():
     """P.V runs on f16 operands; a bf16 V element that f16 cannot hold
     (65536, -2^20) sends its workgroup through the bf16 form, which still
