@@ -126,11 +126,14 @@ class Pool:
 
     def __init__(self, handle):
         self.handle = handle
+        # held here: at interpreter exit the module's globals may be gone
+        # before the last pool is collected
+        self._destroy = _lib.pkv_pool_destroy
 
     def __del__(self):
         h, self.handle = getattr(self, "handle", None), None
         if h:
-            _lib.pkv_pool_destroy(h)
+            self._destroy(h)
 
 
 def pkv_pool_create(num_blocks: int, block_size: int = BLOCK_SIZE, init_order=None) -> Pool:
