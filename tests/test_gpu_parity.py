@@ -1056,6 +1056,48 @@ def test_fp8_prefill_vs_oracle(Hq, Hkv, D, seed, W):
         assert np.max(np.abs(dout[b] - got[qstart[b]])) <= 2e-3
 
 
+def test_fp8_prefill_every_code_exact():
+    """Window 1: every chunk row attends to its own token alone, so its output
+    is that token's V value times v_scale.  The new tokens' V rows hold all
+    254 finite E4M3 codes (bytes checked against the oracle's quantiser),
+    and the prefill's code expansion (V to f16) must give the oracle's
+    value times the scale bit for bit."""
+    from oracle import attention as oatt
+    from oracle import fp8 as ofp8
+    from oracle.cache import widen
+    from oracle.slots import plan_append
+    from tests.gpu_parity import to_device
+    Hq, Hkv, D, B = 4, 2, 128, 2
+    w = synth.small_random(311, num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           dtype="bf16", max_len=40, min_len=5, append=2)
+    ks, vs = 4.0 / 448, 0.25     # a power-of-two V scale: code value x scale is exact in bf16
+    ora, kv = _fp8_pair(w, ks, vs)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)] + [0, 0x80], np.uint8)
+    rng = np.random.default_rng(311)
+    counts = np.array([2, 2], np.int64)
+    T = int(counts.sum())
+    vals = np.empty((T, Hkv, D), np.float32)
+    for b in range(B):
+        for h in range(Hkv):
+            vals[2 * b:2 * b + 2, h] = (ofp8.decode(rng.permutation(codes)) * vs).reshape(2, D)
+    v_new = synth.round_bf16_bits(vals)
+    k_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    q = synth.round_bf16_bits(rng.standard_normal((T, Hq, D)).astype(np.float32))
+    slots, _, cows = plan_append(ora.pool, ora.tables, ora.lens, counts)
+    ora.cache.copy_blocks(cows)
+    v8 = ofp8.quantize(widen(v_new, "bf16").astype(np.float32), vs)
+    assert sorted(set(v8.ravel().tolist())) == sorted(set(codes.tolist()))
+    ora.cache.write(ofp8.quantize(widen(k_new, "bf16").astype(np.float32), ks), v8, slots)
+    kv.append(to_device(k_new), to_device(v_new), counts.astype(np.int32))
+    _fp8_check_cache(ora, kv)
+    kv.window = 1
+    qstart = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    got = kv.prefill_attention(to_device(q), qstart, w.spec.scale).cpu().numpy()
+    exp = oatt.prefill(q, ora.cache, ora.tables, ora.lens, qstart, Hq, Hkv, w.spec.scale, window=1)
+    assert got.dtype == np.float32
+    assert np.array_equal(got, exp.astype(np.float32))
+
+
 def test_fp8_prefill_argument_errors():
     from paged_kv_cache_102_amd import _capi as capi
     w = synth.small_random(9, num_seqs=2, num_q_heads=4, num_kv_heads=2, head_dim=64,
