@@ -377,6 +377,48 @@ def test_prefill_v_beyond_f16_range():
     assert float(np.max(np.abs(got[40:88, 0:4] - exp[40:88, 0:4]))) <= 2e-3
 
 
+def test_prefill_v_conversion_exact():
+    """Window 1 over a bf16 cache: each chunk row's output is its own token's
+    V as P.V sees it.  Values run from 2^-20 to 2^15.9; on the f16 form the
+    output is exact from 2^-14 up and within 2^-25 below (f16 subnormals).
+    Sequence 1's kv head 0 also holds values f16 cannot hold, so its
+    workgroup runs the bf16 form: every value within 2 ulp."""
+    from oracle import attention as oatt
+    from oracle.slots import plan_append
+    from tests.gpu_parity import to_device
+    Hq, Hkv, D, B = 4, 2, 128, 2
+    w = synth.small_random(151, num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           dtype="bf16", max_len=40, min_len=5, append=3)
+    p = _pair(w)
+    rng = np.random.default_rng(151)
+    counts = np.array([3, 3], np.int64)
+    T = int(counts.sum())
+    mag = np.exp2(rng.uniform(-20.0, 15.9, size=(T, Hkv, D)))
+    vals = (np.where(rng.random((T, Hkv, D)) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
+    vals[3, 0, :4] = [65536.0, -1.0e5, 3.0e6, -6.6e4]
+    v_new = synth.round_bf16_bits(vals)
+    k_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    q = synth.round_bf16_bits(rng.standard_normal((T, Hq, D)).astype(np.float32))
+    slots, _, cows = plan_append(p.ora.pool, p.ora.tables, p.ora.lens, counts)
+    p.ora.cache.copy_blocks(cows)
+    p.ora.cache.write(k_new, v_new, slots)
+    p.kv.append(to_device(k_new), to_device(v_new), counts.astype(np.int32))
+    p.kv.window = 1
+    qstart = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    got = p.kv.prefill_attention(to_device(q), qstart, w.spec.scale).cpu().numpy().astype(np.float64)
+    exp = oatt.prefill(q, p.ora.cache, p.ora.tables, p.ora.lens, qstart, Hq, Hkv, w.spec.scale,
+                       window=1)
+    f16_rows = [(slice(0, 3), slice(0, Hq)), (slice(3, 6), slice(2, 4))]
+    for rows, heads in f16_rows:
+        g, e = got[rows, heads], exp[rows, heads]
+        normal = np.abs(e) >= 2.0 ** -14
+        assert np.array_equal(g[normal], e[normal])
+        assert float(np.max(np.abs(g[~normal] - e[~normal]))) <= 2.0 ** -25
+    g1, e1 = got[3:6, 0:2], exp[3:6, 0:2]   # query heads of kv head 0 (group 2)
+    assert np.max(np.abs(e1)) >= 2.9e6   # 3e6 in bf16
+    assert np.all(np.abs(g1 - e1) <= 2.0 ** -22 * np.abs(e1))
+
+
 def test_prefill_bad_rows_are_nan():
     """A chunk longer than its context, or a table entry outside the pool,
     gives NaN rows for that sequence only."""
