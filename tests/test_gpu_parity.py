@@ -379,7 +379,8 @@ def test_prefill_v_beyond_f16_range():
 
 def test_prefill_v_conversion_exact():
     """Window 1 over a bf16 cache: each chunk row's output is its own token's
-    V as P.V sees it.  Values run from 2^-20 to 2^15.9; on the f16 form the
+    V as P.V sees it.  Values run from 2^-20 to 2^15.9 (and +-65280, the
+    largest bf16 magnitude f16 holds); on the f16 form the
     output is exact from 2^-14 up and within 2^-25 below (f16 subnormals).
     Sequence 1's kv head 0 also holds values f16 cannot hold, so its
     workgroup runs the bf16 form: every value within 2 ulp."""
@@ -395,6 +396,7 @@ def test_prefill_v_conversion_exact():
     T = int(counts.sum())
     mag = np.exp2(rng.uniform(-20.0, 15.9, size=(T, Hkv, D)))
     vals = (np.where(rng.random((T, Hkv, D)) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
+    vals[0, 1, :2] = [65280.0, -65280.0]    # the largest bf16 magnitude f16 holds
     vals[3, 0, :4] = [65536.0, -1.0e5, 3.0e6, -6.6e4]
     v_new = synth.round_bf16_bits(vals)
     k_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
