@@ -40,9 +40,10 @@
 // and nothing is reshuffled.  Scores come out as S^T[token 4(l/16)+i][query
 // head l%16] -- exactly the A-operand layout of the P.V product (rows =
 // heads, k = tokens) -- so up to 16 query heads of a kv head share one pass
-// over the tile.  In decode, softmax weights are split into a bf16 high part
-// and a bf16 residual so that P.V keeps ~16 bits of weight precision (the
-// prefill takes them, and V, as f16); accumulation is fp32 throughout.  An FP8 tile holds the same pieces at one byte per
+// over the tile.  In bf16 decode, softmax weights are split into a bf16 high
+// part and a bf16 residual so that P.V keeps ~16 bits of weight precision;
+// where V fits f16 (FP8 codes; the prefill's bf16 V below 65536) the weights
+// and V enter P.V as f16 instead.  Accumulation is fp32 throughout.  An FP8 tile holds the same pieces at one byte per
 // element, a lane's pieces paired into 16 bytes.
 #include <hip/hip_runtime.h>
 
@@ -1395,7 +1396,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
       if constexpr (F8) {
         const uint4 kw = kr[st][j / 2], vw = vr[st][j / 2];
         kx[j] = (j & 1) ? e4m3x8_to_bf16x8(kw.z, kw.w) : e4m3x8_to_bf16x8(kw.x, kw.y);
-        vx[j] = (j & 1) ? e4m3x8_to_bf16x8(vw.z, vw.w) : e4m3x8_to_bf16x8(vw.x, vw.y);
+        vx[j] = (j & 1) ? e4m3x8_to_f16x8(vw.z, vw.w) : e4m3x8_to_f16x8(vw.x, vw.y);
       } else {
         kx[j] = kr[st][j];
         vx[j] = vr[st][j];
@@ -1436,10 +1437,20 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sv[r] - m);
+    if constexpr (F8) {
+      // weights rounded to f16 once: P.V and the normaliser use the same values
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = static_cast<float>(static_cast<_Float16>(p[r]));
+    }
     lsum += (p[0] + p[1]) + (p[2] + p[3]);
-    uint32_t hi01, lo01, hi23, lo23;
-    split_bf16x2(p[0], p[1], hi01, lo01);
-    split_bf16x2(p[2], p[3], hi23, lo23);
+    uint32_t hi01, lo01 = 0, hi23, lo23 = 0;
+    if constexpr (F8) {
+      hi01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p[0], p[1]}), f16x2));
+      hi23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p[2], p[3]}), f16x2));
+    } else {
+      split_bf16x2(p[0], p[1], hi01, lo01);
+      split_bf16x2(p[2], p[3], hi23, lo23);
+    }
     const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi01, hi23));
     const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo01, lo23));
     if ((c_first + c_blk) * kBlock + kBlock > c_L || (c_first + c_blk) * kBlock < wlo) {
@@ -1459,6 +1470,13 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     for (int j = 0; j < NJ; ++j) {
       const s16x4 v0 = __builtin_bit_cast(s16x4, make_uint2(vx[j].x, vx[j].y));
       const s16x4 v1 = __builtin_bit_cast(s16x4, make_uint2(vx[j].z, vx[j].w));
+      if constexpr (F8) {
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        const f16x4 ph = __builtin_bit_cast(f16x4, phi);
+        o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, __builtin_bit_cast(f16x4, v0), o[2 * j], 0, 0, 0);
+        o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, __builtin_bit_cast(f16x4, v1), o[2 * j + 1], 0, 0, 0);
+        continue;
+      }
       o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, v0, o[2 * j], 0, 0, 0);
       o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, v0, o[2 * j], 0, 0, 0);
       o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, v1, o[2 * j + 1], 0, 0, 0);
