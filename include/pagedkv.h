@@ -473,8 +473,8 @@ pkv_status paged_kv_write_fp8(const void* k_new, const void* v_new, pkv_dtype sr
  * code value x k_scale, v_scale (q is bf16 [B][Hq][D], out fp32).  The codes
  * are expanded to bf16 exactly in registers; k_scale folds into the score
  * scale and v_scale into the output.  Balanced split only (partition_size
- * 0 implied): up to 256 sequences and a tile list below 2^31, else
- * PKV_ERR_UNSUPPORTED.  Workspace as paged_attention_workspace_size(...,
+ * 0 implied): up to 16384 sequences and num_seqs * max_blocks_per_seq *
+ * num_kv_heads below 2^31, else PKV_ERR_UNSUPPORTED.  Workspace as paged_attention_workspace_size(...,
  * partition_size 0).  Errors otherwise as paged_attention_decode. */
 pkv_status paged_attention_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* block_tables, const int32_t* context_lens,
@@ -503,7 +503,8 @@ pkv_status paged_attention_decode_fp8(const void* q, const void* k_cache, const 
  *   q: device [T][num_q_heads][head_dim] in the cache dtype, T = query_start[num_seqs]
  *   query_start: device int32 [num_seqs + 1], non-decreasing, query_start[0] = 0
  *   out: device fp32 [T][num_q_heads][head_dim], written for every chunk row
- *   max_query_len: host-side upper bound of n_s (sizes the grid)
+ *   max_query_len: host-side upper bound of n_s (sizes the grid); rows of a
+ *     chunk beyond it get NaN
  * bf16 caches (kv_dtype PKV_BF16; FP8: paged_attention_prefill_fp8);
  * head_dim 64 or 128; at most 16 query heads per kv head.  Precision: fp32
  * accumulation; the softmax weights and V enter P.V as f16 (11 significant
@@ -572,6 +573,12 @@ pkv_status paged_attention_decode_window(const void* q, const void* k_cache, con
  * not timed).  every < 1 -> PKV_ERR_INVALID.  Not thread-safe. */
 pkv_status pkv_profile_begin(int32_t every);
 pkv_status pkv_profile_end(int32_t* num_launches, double* total_ms);
+/* While profiling is on: synchronizes on the launches timed so far and
+ * writes the duration of each (milliseconds, in call order) to out_ms
+ * [min(capacity, count)], the count to *num_launches; the session stays
+ * open.  A fixed-partition call's span covers its reduce kernel too.
+ * out_ms: host.  Bad arguments -> PKV_ERR_INVALID. */
+pkv_status pkv_profile_durations(float* out_ms, int32_t capacity, int32_t* num_launches);
 
 /* Streaming-read reference: reads `bytes` (rounded down to 16) of device
  * memory `buf` once with 16-byte loads, on `stream`, so the caller can time

@@ -89,6 +89,7 @@ _SIGS = {
                                      C.c_int32, C.c_int32, C.c_float, C.c_float, _vp]),
     "pkv_profile_begin": (C.c_int, [C.c_int32]),
     "pkv_profile_end": (C.c_int, [_i32p, C.POINTER(C.c_double)]),
+    "pkv_profile_durations": (C.c_int, [C.POINTER(C.c_float), C.c_int32, _i32p]),
     "pkv_stream_read": (C.c_int, [_vp, C.c_size_t, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -492,6 +493,14 @@ def pkv_profile_end():
     n, ms = C.c_int32(), C.c_double()
     _check(_lib.pkv_profile_end(C.byref(n), C.byref(ms)), "pkv_profile_end")
     return n.value, ms.value
+
+
+def pkv_profile_durations(capacity: int = 8192):
+    """Durations (ms) of the launches timed so far in this session."""
+    buf = (C.c_float * max(capacity, 1))()
+    n = C.c_int32()
+    _check(_lib.pkv_profile_durations(buf, capacity, C.byref(n)), "pkv_profile_durations")
+    return [buf[i] for i in range(min(n.value, capacity))]
 
 
 def pkv_stream_read(buf, sink, stream=None) -> None:

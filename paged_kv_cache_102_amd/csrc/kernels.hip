@@ -282,9 +282,11 @@ struct DecodeArgs {
   unsigned long long* bw_count;  // [num_seqs * num_kv_heads]: epoch << 32 | arrivals
   unsigned epoch;                // distinct for every balanced launch
   int grid_waves;
-  // per-CU form: overflow partial-state slots, fixed share of each
-  // wavefront (per mille of the CU's range), minimum chunk size in tiles
+  // per-CU form: overflow partial-state slots (over_slots per CU), fixed
+  // share of each wavefront (per mille of the CU's range), minimum chunk
+  // size in tiles
   float* cu_over;
+  int over_slots;
   int static_permille, chunk_min;
   float out_scale;  // FP8 cache: the V tensor scale (1 otherwise)
   int window;       // sliding window in tokens (0: the whole context)
@@ -1087,15 +1089,26 @@ constexpr int kCuChunksMax = 64;                           // chunks per CU
 constexpr float kCuRescale = 8.0f;                         // lazy-max threshold (log2)
 constexpr int kCuSlots = 2 * (kCuWaves + kCuChunksMax);    // partial segments per CU
 constexpr int kCuHeaderBytes = 64 + kCuSlots * 3 * 4;      // counters + slot metadata
+// With the whole range in fixed shares (and chunks of at least 4 tiles) a CU
+// runs at most 8 shares plus 2 chunks of the under-8-tile remainder, each
+// leaving at most 2 partial segments.
+constexpr int kCuStaticSlots = 2 * (kCuWaves + 2);
+// Sequences the per-CU form takes: their block-count prefix sits in LDS.
+constexpr int kCuMaxSeqs = 16384;
 
 // Partial-state slots: m and l [slot][group], then o [slot][group][D].
 __host__ __device__ inline int cu_state_floats(int group, int head_dim) {
   return group * (head_dim + 2);
 }
-// Slots that fit in LDS next to the header (the rest overflow).
-__host__ __device__ inline int cu_lds_slots(int group, int head_dim) {
-  const int n = (kCuLdsBytes - kCuHeaderBytes) / (cu_state_floats(group, head_dim) * 4);
-  return n > kCuSlots ? kCuSlots : n;
+// LDS bytes of the block-count prefix of num_seqs sequences ([num_seqs + 1] ints).
+__host__ __device__ inline int cu_prefix_bytes(int num_seqs) {
+  return ((num_seqs + 1) * 4 + 15) & ~15;
+}
+// Slots that fit in LDS next to the header and the prefix (the rest overflow).
+__host__ __device__ inline int cu_lds_slots(int group, int head_dim, int num_seqs) {
+  const int n = (kCuLdsBytes - kCuHeaderBytes - cu_prefix_bytes(num_seqs)) /
+                (cu_state_floats(group, head_dim) * 4);
+  return n > kCuSlots ? kCuSlots : (n < 0 ? 0 : n);
 }
 
 // F8: the cache holds FP8 E4M3 codes (tiles of 16 D bytes, converted to
@@ -1113,12 +1126,15 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
 
   __shared__ __align__(16) unsigned char smem[kCuLdsBytes];
   const int g = a.group;
-  const int cap = cu_lds_slots(g, D);  // slots held in LDS
+  const int B = a.num_seqs;
+  const int cap = cu_lds_slots(g, D, B);  // slots held in LDS
   int* hdr = reinterpret_cast<int*>(smem);
   int* s_item = hdr + 16;
   int* s_s0 = s_item + kCuSlots;
   int* s_nb = s_s0 + kCuSlots;
-  float* s_m = reinterpret_cast<float*>(smem + kCuHeaderBytes);
+  // s_cum[b] = tiles of the sequences before b in the list, b = 0..B
+  int* s_cum = reinterpret_cast<int*>(smem + kCuHeaderBytes);
+  float* s_m = reinterpret_cast<float*>(smem + kCuHeaderBytes + cu_prefix_bytes(B));
   float* s_l = s_m + cap * g;
   float* s_o = s_l + cap * g;
   // overflow slots of this CU in the workspace, [m g][l g][o g*D] per slot.
@@ -1126,51 +1142,64 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   // compiles to an LDS or a global instruction (a pointer that could be
   // either would become a flat access, which the compiler waits on with the
   // vector-memory counter).
-  float* const o_base = a.cu_over + int64_t(blockIdx.x) * (kCuSlots - cap) * cu_state_floats(g, D);
+  float* const o_base = a.cu_over + int64_t(blockIdx.x) * a.over_slots * cu_state_floats(g, D);
 
   const int lane = threadIdx.x & 63;
   // wave-uniform (scalar register): everything derived from it stays uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hcol = lane & 15;
   const int grp = lane >> 4;
-  const int B = a.num_seqs;
   const int Hkv = a.num_kv_heads;
   const int wg = blockIdx.x;
   const int NWG = gridDim.x;
 
-  // lengths and block counts of up to 256 sequences, 4 per lane; the loads
-  // go through a buffer resource sized to the B lengths (reads past them
-  // return 0), so all four are issued together
-  int lenv[4], cnt[4];
+  // Tile counts of the B sequences and their prefix, in LDS.  Thread i takes
+  // sequences [i k, i k + k); the length loads go through a buffer resource
+  // sized to the B lengths (reads past them return 0, i.e. no tiles).
   {
+    const int tid = threadIdx.x;
+    const int k = (B + 64 * NW - 1) / (64 * NW);
     const __amdgpu_buffer_rsrc_t rl = tile_rsrc(a.lens, B * 4);
+    int part = 0;
+    for (int j = 0; j < k; ++j)
+      part += nblocks_of<WIN>(a, __builtin_amdgcn_raw_buffer_load_b32(rl, (tid * k + j) * 4, 0, 0));
+    int incl = part;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      lenv[k] = __builtin_amdgcn_raw_buffer_load_b32(rl, (lane * 4 + k) * 4, 0, 0);
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(incl, d);
+      if (lane >= d) incl += up;
+    }
+    if (lane == 63) hdr[4 + wave] = incl;  // wave totals
+    __syncthreads();
+    int run = incl - part;
+    int total = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) cnt[k] = nblocks_of<WIN>(a, lenv[k]);
+    for (int w = 0; w < NW; ++w) {
+      const int t = hdr[4 + w];
+      run += w < wave ? t : 0;
+      total += t;
+    }
+    for (int j = 0; j < k; ++j) {
+      const int b = tid * k + j;
+      if (b < B) {
+        s_cum[b] = run;
+        run += nblocks_of<WIN>(a, __builtin_amdgcn_raw_buffer_load_b32(rl, b * 4, 0, 0));
+      }
+    }
+    if (tid == 0) s_cum[B] = total;
   }
-  auto pick = [](const int (&v)[4], int k) {
-    return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
-  };
   // rows of sequences with no work: zeros for an empty context, NaN for a
   // bad length, spread over all wavefronts of the grid
   for (int b = wg * NW + wave; b < B; b += NWG * NW) {
-    const int L = __builtin_amdgcn_readlane(pick(lenv, b & 3), b >> 2);
+    const int L = load_uniform(a.lens, b);
     if (!len_ok(L, a) || L == 0) {
       const float fill = (L == 0) ? 0.f : __builtin_nanf("");
       for (int e = lane; e < a.num_q_heads * D; e += 64)
         a.out[int64_t(b) * a.num_q_heads * D + e] = fill;
     }
   }
-  const int mine = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-  int incl = mine;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int up = __shfl_up(incl, d);
-    if (lane >= d) incl += up;
-  }
-  const int total = __builtin_amdgcn_readlane(incl, 63);
+  __syncthreads();
+  const int total = __builtin_amdgcn_readfirstlane(s_cum[B]);
   const int G = total * Hkv;  // < 2^31 (checked on the host)
 
   // this CU's range, the fixed share of each wavefront and the chunk size
@@ -1187,25 +1216,28 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // tile index -> (kv head, sequence, block, length, block count), from registers
+  // tile index -> (kv head, sequence, block, length, block count): the
+  // sequence is the last b with s_cum[b] <= the tile's rank in its kv head's
+  // list (s_cum is non-decreasing, s_cum[0] = 0 and s_cum[B] = total), found
+  // by a 64-way search, one LDS read and one ballot per level
   auto locate = [&](int t, int& kvh, int& b, int& blk, int& L, int& nb) {
     kvh = t / total;
     const int rem = t - kvh * total;
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > rem);
-    const int pos = static_cast<int>(__builtin_ctzll(hit));
-    int r = rem - (__builtin_amdgcn_readlane(incl, pos) - __builtin_amdgcn_readlane(mine, pos));
-    int k = 0;
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int nq = __builtin_amdgcn_readlane(cnt[q], pos);
-      if (k == q && r >= nq) {
-        r -= nq;
-        k = q + 1;
-      }
+    int lo = 0, span = B;  // the answer lies in [lo, lo + span)
+    while (span > 64) {
+      const int stride = (span + 63) >> 6;
+      const int off = lane * stride;
+      const int v = off < span ? s_cum[lo + off] : 0x7FFFFFFF;
+      const uint64_t le = __builtin_amdgcn_ballot_w64(v <= rem);
+      const int p = 63 - static_cast<int>(__builtin_clzll(le));
+      lo += p * stride;
+      span = min(stride, span - p * stride);
     }
-    b = __builtin_amdgcn_readfirstlane(pos * 4 + k);
-    blk = __builtin_amdgcn_readfirstlane(r);
-    L = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(pick(lenv, k), pos));
+    const int v = lane < span ? s_cum[lo + lane] : 0x7FFFFFFF;
+    const uint64_t le = __builtin_amdgcn_ballot_w64(v <= rem);
+    b = __builtin_amdgcn_readfirstlane(lo + 63 - static_cast<int>(__builtin_clzll(le)));
+    blk = __builtin_amdgcn_readfirstlane(rem - s_cum[b]);
+    L = load_uniform(a.lens, b);
     nb = nblocks_of<WIN>(a, L);
   };
   auto advance = [&](int& kvh, int& b, int& blk, int& L, int& nb) {
@@ -1625,18 +1657,26 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     if (lane == 0) {
       unsigned long long* cp = a.bw_count + item;
       unsigned long long old = __hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      unsigned long long nv = 0;
+      arrived = 0xFFFFFFFFu;  // stays so if the count could not be raised
       for (int tries = 0; tries < (1 << 20); ++tries) {
-        nv = (unsigned(old >> 32) == a.epoch)
-                 ? old + 1
-                 : ((static_cast<unsigned long long>(a.epoch) << 32) | 1ull);
+        const unsigned long long nv =
+            (unsigned(old >> 32) == a.epoch)
+                ? old + 1
+                : ((static_cast<unsigned long long>(a.epoch) << 32) | 1ull);
         if (__hip_atomic_compare_exchange_weak(cp, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT))
+                                               __HIP_MEMORY_SCOPE_AGENT)) {
+          arrived = static_cast<unsigned>(nv);
           break;
+        }
       }
-      arrived = static_cast<unsigned>(nv);
     }
     arrived = __builtin_amdgcn_readlane(arrived, 0);
+    if (arrived == 0xFFFFFFFFu) {
+      // this CU's arrival was never counted, so no CU will merge the item:
+      // its rows become NaN rather than stay unwritten
+      for (int e = lane; e < g * D; e += 64) a.out[head0 * D + e] = __builtin_nanf("");
+      continue;
+    }
     if (arrived != need) continue;
     __asm__ volatile("" ::: "memory");
     // merge every CU's share (this one's included, read back like the
@@ -1752,8 +1792,6 @@ void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int NQ = kPfColTiles;
   constexpr int TILE_BYTES = kBlock * D * 2;
   constexpr int STAGE_BYTES = 2 * SB * TILE_BYTES;  // blocks 0 .. SB-1 x (K, V)
-  constexpr int PIECES = STAGE_BYTES / 16;     // 16-byte loads per stage
-  constexpr int PT = PIECES / (64 * kPfWaves);  // per thread
   constexpr int TILE_PIECES = TILE_BYTES / 16;
   // tiles in global memory: as in LDS, or FP8 at one byte per element
   constexpr int TILE_G = F8 ? kBlock * D : TILE_BYTES;
@@ -1827,6 +1865,15 @@ void prefill_bf16_kernel(PrefillArgs a) {
   const int qs = load_uniform(a.qstart, b);
   const int n = load_uniform(a.qstart, b + 1) - qs;
   const int q0 = qt * QTP;
+  if (qt == a.tiles - 1 && n > a.tiles * QTP) {
+    // chunk rows beyond the grid's tiles (max_query_len below this chunk):
+    // NaN, so that no row of the output is left unwritten
+    const int r0 = a.tiles * QTP;
+    for (int c = wave; c < (n - r0) * g; c += kPfWaves) {
+      float* dst = a.out + ((int64_t(qs) + r0 + c / g) * a.num_q_heads + int64_t(kvh) * g + c % g) * D;
+      for (int e = lane; e < D; e += 64) dst[e] = __builtin_nanf("");
+    }
+  }
   if (q0 >= n || n <= 0) return;
   const int L = load_uniform(a.lens, b);
   const int nq = min(QTP, n - q0);  // positions in this tile
@@ -2452,15 +2499,25 @@ int device_cus() {
 size_t balanced_states_bytes(int waves, int group, int head_dim) {
   return (size_t(waves) * 2 * group * (head_dim + 2) * sizeof(float) + 255) & ~size_t(255);
 }
-size_t cu_overflow_bytes(int cus, int group, int head_dim) {
-  const int over = kCuSlots - cu_lds_slots(group, head_dim);
-  return (size_t(cus) * over * cu_state_floats(group, head_dim) * sizeof(float) + 255) &
+size_t cu_overflow_bytes(int cus, int over_slots, int group, int head_dim) {
+  return (size_t(cus) * over_slots * cu_state_floats(group, head_dim) * sizeof(float) + 255) &
          ~size_t(255);
 }
-size_t balanced_workspace_bytes(int waves, int group, int head_dim, int64_t seq_heads) {
-  return balanced_states_bytes(waves, group, head_dim) +
-         cu_overflow_bytes(device_cus(), group, head_dim) + size_t(seq_heads) * 8;
+// Overflow slots per CU of the per-CU form: every slot beyond LDS (any mix
+// of shares and chunks), or only those the fixed shares can need.
+int cu_over_slots(int group, int head_dim, int num_seqs, bool static_only) {
+  const int cap = cu_lds_slots(group, head_dim, num_seqs < kCuMaxSeqs ? num_seqs : kCuMaxSeqs);
+  const int over = (static_only ? kCuStaticSlots : kCuSlots) - cap;
+  return over > 0 ? over : 0;
 }
+size_t balanced_workspace_bytes(int waves, int group, int head_dim, int num_seqs,
+                                int num_kv_heads) {
+  return balanced_states_bytes(waves, group, head_dim) +
+         cu_overflow_bytes(device_cus(), cu_over_slots(group, head_dim, num_seqs, false), group,
+                           head_dim) +
+         size_t(num_seqs) * num_kv_heads * 8;
+}
+
 
 // Per-CU form parameters: each wavefront's fixed share of its CU's range
 // (per mille) and the smallest chunk.  The default gives the whole range to
@@ -2778,7 +2835,7 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
   // or 512-token partitions for fp32 -- room for either
   const int group = num_q_heads / num_kv_heads;
   const size_t bal = balanced_workspace_bytes(balanced_waves(), group < 16 ? group : 16, head_dim,
-                                              int64_t(num_seqs) * num_kv_heads);
+                                              num_seqs, num_kv_heads);
   return fixed > bal ? fixed : bal;
 }
 
@@ -2849,16 +2906,14 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   // one workgroup per (partition, sequence, head) must fit a 1D grid
   if (max_parts * num_seqs * num_q_heads > 0x7FFFFFFF) return PKV_ERR_UNSUPPORTED;
   const bool balanced = (kv_dtype == PKV_BF16 || fp8) && partition_size == 0;
-  const int waves = balanced ? balanced_waves() : 0;
-  if (balanced && waves <= 0) return PKV_ERR_HIP;
-  const size_t need =
-      balanced ? balanced_workspace_bytes(waves, group, head_dim, int64_t(num_seqs) * num_kv_heads)
-               : paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                max_context_len,
-                                                partition_size == 0 ? kDefaultPartition
-                                                                    : partition_size);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_INVALID;
-
+  const int cus = balanced ? device_cus() : 0;
+  // per-CU form: sequences whose tile-count prefix fits LDS, a tile list
+  // indexed in 32 bits, and global partial-state slots (2 per CU) within
+  // those of the per-wave grid
+  const bool cu_shape = num_seqs <= kCuMaxSeqs &&
+                        int64_t(num_seqs) * max_blocks_per_seq * num_kv_heads <
+                            (int64_t(1) << 31) &&
+                        cus > 0;
   DecodeArgs a;
   a.q = q;
   a.kc = k_cache;
@@ -2866,11 +2921,6 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.tables = block_tables;
   a.lens = context_lens;
   a.out = out;
-  const int64_t heads = int64_t(num_seqs) * num_q_heads;
-  float* ws = static_cast<float*>(workspace);
-  a.ws_o = ws;
-  a.ws_m = ws ? ws + heads * max_parts * head_dim : nullptr;
-  a.ws_l = ws ? a.ws_m + heads * max_parts : nullptr;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -2883,28 +2933,42 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.scale_log2e = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
   a.out_scale = fp8 ? v_scale : 1.0f;
   a.window = window;
-  a.grid_waves = waves;
-  a.bw_o = balanced ? ws : nullptr;
-  a.bw_m = balanced ? ws + size_t(waves) * 2 * group * head_dim : nullptr;
-  a.bw_l = balanced ? a.bw_m + size_t(waves) * 2 * group : nullptr;
-  const int cus = balanced ? device_cus() : 0;
-  a.cu_over = balanced ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                  balanced_states_bytes(waves, group, head_dim))
-                       : nullptr;
-  a.bw_count = balanced ? reinterpret_cast<unsigned long long*>(
-                              static_cast<char*>(workspace) +
-                              balanced_states_bytes(waves, group, head_dim) +
-                              cu_overflow_bytes(cus, group, head_dim))
-                        : nullptr;
+  bool cu_form;
+  int waves = 0;
+  {
+    waves = balanced ? balanced_waves() : 0;
+    if (balanced && waves <= 0) return PKV_ERR_HIP;
+    const size_t need =
+        balanced ? balanced_workspace_bytes(waves, group, head_dim, num_seqs, num_kv_heads)
+                 : paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                  max_context_len,
+                                                  partition_size == 0 ? kDefaultPartition
+                                                                      : partition_size);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_INVALID;
+    const int64_t heads = int64_t(num_seqs) * num_q_heads;
+    float* ws = static_cast<float*>(workspace);
+    a.ws_o = ws;
+    a.ws_m = ws ? ws + heads * max_parts * head_dim : nullptr;
+    a.ws_l = ws ? a.ws_m + heads * max_parts : nullptr;
+    a.grid_waves = waves;
+    a.bw_o = balanced ? ws : nullptr;
+    a.bw_m = balanced ? ws + size_t(waves) * 2 * group * head_dim : nullptr;
+    a.bw_l = balanced ? a.bw_m + size_t(waves) * 2 * group : nullptr;
+    const int over = cu_over_slots(group, head_dim, num_seqs, false);
+    a.over_slots = over;
+    a.cu_over = balanced ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                    balanced_states_bytes(waves, group, head_dim))
+                         : nullptr;
+    a.bw_count = balanced ? reinterpret_cast<unsigned long long*>(
+                                static_cast<char*>(workspace) +
+                                balanced_states_bytes(waves, group, head_dim) +
+                                cu_overflow_bytes(cus, over, group, head_dim))
+                          : nullptr;
+    a.static_permille = env_int("PKV_CU_STATIC_PERMILLE", 1000, 0, 1000);
+    a.chunk_min = env_int("PKV_CU_CHUNK_MIN", 4, 1, 1 << 20);
+    cu_form = balanced && cu_split_enabled() && cu_shape && cus <= waves;
+  }
   a.epoch = balanced ? next_epoch() : 0;
-  a.static_permille = env_int("PKV_CU_STATIC_PERMILLE", 1000, 0, 1000);
-  a.chunk_min = env_int("PKV_CU_CHUNK_MIN", 4, 1, 1 << 20);
-  // per-CU form: up to 256 sequences (lengths held in registers), a tile
-  // list indexed in 32 bits, and global partial-state slots (2 per CU) within
-  // those of the per-wave grid
-  const bool cu_form = balanced && cu_split_enabled() && num_seqs <= 256 &&
-                       int64_t(num_seqs) * max_blocks_per_seq * num_kv_heads < (int64_t(1) << 31) &&
-                       cus > 0 && cus <= waves;
   if (fp8 && !cu_form) return PKV_ERR_UNSUPPORTED;
 
   const bool prof = g_prof.on && g_prof.calls++ % g_prof.every == 0 &&
@@ -2931,18 +2995,21 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
     else
       hipLaunchKernelGGL(decode_f32_kernel<64>, grid, dim3(64), 0, stream, a);
   }
+  pkv_status st = launch_status();
+  if (st == PKV_OK && max_parts > 1) {
+    const unsigned rgrid = static_cast<unsigned>(int64_t(num_seqs) * num_kv_heads);
+    if (head_dim == 128)
+      hipLaunchKernelGGL(lse_reduce_kernel<128>, dim3(rgrid), dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL(lse_reduce_kernel<64>, dim3(rgrid), dim3(64), 0, stream, a);
+    st = launch_status();
+  }
+  // the timed span of a fixed-partition call covers its reduce as well
   if (prof) {
     (void)hipEventRecord(g_prof.pool[g_prof.used + 1], stream);
     g_prof.used += 2;
   }
-  pkv_status st = launch_status();
-  if (st != PKV_OK || max_parts <= 1) return st;
-  const unsigned rgrid = static_cast<unsigned>(int64_t(num_seqs) * num_kv_heads);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(lse_reduce_kernel<128>, dim3(rgrid), dim3(64), 0, stream, a);
-  else
-    hipLaunchKernelGGL(lse_reduce_kernel<64>, dim3(rgrid), dim3(64), 0, stream, a);
-  return launch_status();
+  return st;
 }
 }  // namespace
 
@@ -3055,6 +3122,20 @@ pkv_status pkv_profile_begin(int32_t every) {
   g_prof.calls = 0;
   g_prof.every = every;
   g_prof.on = true;
+  return PKV_OK;
+}
+
+pkv_status pkv_profile_durations(float* out_ms, int32_t capacity, int32_t* num_launches) {
+  if (!num_launches || capacity < 0 || (capacity > 0 && !out_ms)) return PKV_ERR_INVALID;
+  int32_t k = 0;
+  for (size_t i = 0; i + 1 < g_prof.used; i += 2, ++k) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_prof.pool[i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_prof.pool[i], g_prof.pool[i + 1]) != hipSuccess)
+      return PKV_ERR_HIP;
+    if (k < capacity) out_ms[k] = ms;
+  }
+  *num_launches = k;
   return PKV_OK;
 }
 

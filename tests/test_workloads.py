@@ -45,3 +45,26 @@ def test_values_deterministic():
     a = synth.generate("tiny-fp32")
     b = synth.generate("tiny-fp32")
     assert np.array_equal(a.k_rows, b.k_rows) and np.array_equal(a.pool_order, b.pool_order)
+
+
+def test_subset_keeps_each_sequence():
+    """A bounded sample (synth.subset) holds exactly the chosen sequences:
+    the same lengths and rows, so the oracle gives the same outputs for
+    them as on the whole workload (with and without a shared prefix)."""
+    from oracle import attention, replay
+    for w, pick in ((synth.small_random(21, num_seqs=9, num_q_heads=4, num_kv_heads=2,
+                                        head_dim=64, dtype="bf16", max_len=90), [1, 4, 8]),
+                    (synth.generate("shared-prefix-bf16"), [0, 77, 127])):
+        s = w.spec
+        sub = synth.subset(w, pick, seed=3)
+        assert list(sub.lens) == [int(w.lens[b]) for b in pick]
+        assert sorted(sub.pool_order) == list(range(sub.num_blocks))
+        full, part = replay.prefill(w), replay.prefill(sub)
+        exp = attention.decode(w.q, full.cache, full.tables, full.lens, s.num_q_heads,
+                               s.num_kv_heads, s.scale, seqs=pick)
+        got = attention.decode(sub.q, part.cache, part.tables, part.lens, s.num_q_heads,
+                               s.num_kv_heads, s.scale)
+        assert np.array_equal(got, exp[pick])
+        replay.append_step(full, w)
+        replay.append_step(part, sub)
+        assert list(part.lens) == [int(full.lens[b]) for b in pick]

@@ -16,6 +16,7 @@ Five workloads follow the shapes of the decode step described on the pages
   shared-prefix-cow  the same, but the shared prefix is 2040 tokens so its
                    last block is only half full; the append step then adds
                    s_b + 1 tokens per sequence, which forces copy-on-write
+  gqa-8b-bf16-b512 the gqa-8b shape and length law with 512 sequences
 
 Draw order (fixed): one numpy PCG64 generator seeded 1000 + workload number
 draws the lengths, the own-suffix lengths, the pool permutation and Q, in
@@ -91,6 +92,10 @@ SPECS = {
     "shared-prefix-cow-bf16": WorkloadSpec("shared-prefix-cow-bf16", 5, 128, 32, 8, 128, "bf16",
                                            "shared", prefix_len=2040, suffix_range=(0, 512),
                                            cow_append=True),
+    # the gqa-8b shape with twice the batch (a larger serving step)
+    "gqa-8b-bf16-b512": WorkloadSpec("gqa-8b-bf16-b512", 13, 512, 32, 8, 128, "bf16",
+                                     "lognormal", lognormal=(1000.0, 1.0, 16, 8192),
+                                     pinned=((0, 273),)),
 }
 
 
@@ -297,3 +302,43 @@ def small_random(seed: int, *, num_seqs: int, num_q_heads: int, num_kv_heads: in
                     suffix_lens=np.zeros(num_seqs, np.int32), append_counts=append_c.astype(np.int32),
                     num_blocks=nb, max_blocks_per_seq=max_blocks, pool_order=order,
                     q=q, k_rows=k_rows, v_rows=v_rows, k_app=k_app, v_app=v_app)
+
+
+def subset(w: Workload, seqs, seed: int = 0) -> Workload:
+    """The sequences ``seqs`` of workload ``w`` as a workload of their own
+    (a bounded sample with the same lengths, prefix sharing and values): the
+    rows of each chosen sequence in the same append order, a pool of 1.25x
+    their need (shared prefix blocks counted once), drawn in a seeded order.
+    Used to time a fixed share of a large workload on the CPU."""
+    s = w.spec
+    idx = np.asarray(sorted(int(b) for b in seqs), dtype=np.int64)
+    sub = WorkloadSpec(f"{s.key}[{len(idx)} of {s.num_seqs}]", s.number, len(idx), s.num_q_heads,
+                       s.num_kv_heads, s.head_dim, s.dtype, s.lengths, s.fixed_lens,
+                       s.uniform_range, s.lognormal, (), s.prefix_len, s.suffix_range,
+                       s.cow_append, 0, s.partition_tokens)
+    own = w.own_lens.astype(np.int64)
+    starts = s.prefix_len + np.concatenate([[0], np.cumsum(own)[:-1]])
+    rows = [np.arange(s.prefix_len)] if s.prefix_len else []
+    rows += [np.arange(starts[b], starts[b] + own[b]) for b in idx]
+    rows = np.concatenate(rows).astype(np.int64) if rows else np.zeros(0, np.int64)
+    app = w.append_counts.astype(np.int64)
+    app_starts = np.concatenate([[0], np.cumsum(app)[:-1]])
+    app_rows = np.concatenate([np.arange(app_starts[b], app_starts[b] + app[b]) for b in idx])
+    lens = w.lens[idx].astype(np.int64)
+    grow = app[idx] + w.extra_tokens
+    if s.prefix_len:
+        full_prefix = s.prefix_len // BLOCK_SIZE
+        need = _ceil_div(s.prefix_len, BLOCK_SIZE) + int(
+            np.sum(_ceil_div(lens + grow, BLOCK_SIZE) - full_prefix))
+    else:
+        need = int(np.sum(_ceil_div(lens + grow, BLOCK_SIZE)))
+    nb = max(1, int(math.ceil(1.25 * need)))
+    order = np.random.Generator(np.random.PCG64(seed)).permutation(nb).astype(np.int32)
+    pick = lambda a, r: None if a is None else a[r]
+    return Workload(spec=sub, lens=w.lens[idx].copy(), own_lens=w.own_lens[idx].copy(),
+                    suffix_lens=w.suffix_lens[idx].copy(),
+                    append_counts=w.append_counts[idx].copy(), num_blocks=nb,
+                    max_blocks_per_seq=int(np.max(_ceil_div(lens + grow, BLOCK_SIZE))),
+                    pool_order=order, q=pick(w.q, idx), k_rows=pick(w.k_rows, rows),
+                    v_rows=pick(w.v_rows, rows), k_app=pick(w.k_app, app_rows),
+                    v_app=pick(w.v_app, app_rows), extra_tokens=w.extra_tokens)
