@@ -560,6 +560,37 @@ pkv_status paged_attention_decode_window(const void* q, const void* k_cache, con
                                          pkv_dtype kv_dtype, float k_scale, float v_scale,
                                          float* out, hipStream_t stream);
 
+/* Decode that allocates nothing, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The result of
+ * paged_attention_decode_window with partition_size 0 (bf16 or FP8 cache;
+ * per-CU balanced split, every CU's range in fixed wavefront shares), with
+ * its partial states and arrival counters in a static device array of
+ * 16 MiB that the library holds on each GPU it runs on until the process
+ * ends (resolved on the first call on each device, with that device
+ * current).  Needs 4 * C * (2 + s) * g * (D + 2) + 8 * num_seqs *
+ * num_kv_heads bytes (each of the two parts rounded up to 256), with
+ * C = compute units, g = num_q_heads / num_kv_heads, D = head_dim and s
+ * the partial states per CU (at most 20) that do not fit in LDS beside the
+ * 4 (num_seqs + 1)-byte tile-count prefix (s = 0 for g = 4 or 8 at D = 128
+ * with up to 4096 sequences; about 1 MiB for g = 4, D = 128 on 256 CUs,
+ * plus the counters); sizes beyond 16 MiB, num_seqs > 16384 or an fp32
+ * cache -> PKV_ERR_UNSUPPORTED.
+ * The counters carry a launch tag, so the array never needs clearing.
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller.  Arguments and other errors as paged_attention_decode_window;
+ * k_scale, v_scale are ignored for bf16.  Calls no allocating routine. */
+pkv_status paged_attention_decode_noalloc(const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t num_blocks,
+                                          int32_t max_blocks_per_seq, int32_t max_context_len,
+                                          float scale, int32_t window, pkv_dtype kv_dtype,
+                                          float k_scale, float v_scale, float* out,
+                                          hipStream_t stream);
+
 /* ===== Measurement ==========================================================
  * While profiling is on, decode calls number 0, every, 2 every, ... since
  * pkv_profile_begin (each paged_attention_decode* call that gets past its

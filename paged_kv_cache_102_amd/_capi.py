@@ -79,6 +79,10 @@ _SIGS = {
                                                 C.c_int32, C.c_float, C.c_int32, C.c_int32, _vp,
                                                 C.c_size_t, C.c_int, C.c_float, C.c_float, _vp,
                                                 _vp]),
+    "paged_attention_decode_noalloc": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
+                                                 C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                                 C.c_int32, C.c_float, C.c_int32, C.c_int,
+                                                 C.c_float, C.c_float, _vp, _vp]),
     "paged_kv_swap_blocks": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32, C.c_int32,
                                        C.c_int32, C.c_int32, C.c_int, _vp]),
     "paged_attention_decode_fp8": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
@@ -482,6 +486,24 @@ def paged_attention_decode_window(q, k_cache, v_cache, block_tables, context_len
                                               _dtype_code(k_cache), k_scale, v_scale,
                                               _dev(out, "out"), _stream(stream)),
            "paged_attention_decode_window")
+
+
+def paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, out, *,
+                                   num_kv_heads: int, num_blocks: int, max_context_len: int,
+                                   scale: float, window: int = 0, k_scale: float = 1.0,
+                                   v_scale: float = 1.0, stream=None) -> None:
+    """Decode without a workspace: partial states in the library's static
+    per-GPU scratch (calls on one GPU must not overlap)."""
+    B, Hq, D = q.shape
+    mb = block_tables.shape[1]
+    _check(_lib.paged_attention_decode_noalloc(_dev(q, "q"), _dev(k_cache, "k_cache"),
+                                               _dev(v_cache, "v_cache"),
+                                               _dev(block_tables, "block_tables"),
+                                               _dev(context_lens, "context_lens"), B, Hq,
+                                               num_kv_heads, D, num_blocks, mb, max_context_len,
+                                               scale, window, _dtype_code(k_cache), k_scale,
+                                               v_scale, _dev(out, "out"), _stream(stream)),
+           "paged_attention_decode_noalloc")
 
 
 def pkv_profile_begin(every: int = 1) -> None:

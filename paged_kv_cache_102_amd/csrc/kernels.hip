@@ -51,9 +51,13 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "pagedkv.h"
+
+// The allocation-free decode's scratch (see scratch_device below).
+static __device__ __align__(256) unsigned char scratch[size_t(16) << 20];
 
 namespace {
 
@@ -1093,6 +1097,7 @@ constexpr int kCuHeaderBytes = 64 + kCuSlots * 3 * 4;      // counters + slot me
 // runs at most 8 shares plus 2 chunks of the under-8-tile remainder, each
 // leaving at most 2 partial segments.
 constexpr int kCuStaticSlots = 2 * (kCuWaves + 2);
+constexpr int kCuStaticChunkMin = 4;
 // Sequences the per-CU form takes: their block-count prefix sits in LDS.
 constexpr int kCuMaxSeqs = 16384;
 
@@ -2518,6 +2523,14 @@ size_t balanced_workspace_bytes(int waves, int group, int head_dim, int num_seqs
          size_t(num_seqs) * num_kv_heads * 8;
 }
 
+// Scratch of the allocation-free decode entry point: one array per GPU,
+// resident until the process ends.  Host code never passes `scratch`
+// itself to a kernel (in host code the name is a host-side stand-in);
+// scratch_device() resolves this GPU's copy once, with the device current.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchMaxDevices] = {};
 
 // Per-CU form parameters: each wavefront's fixed share of its CU's range
 // (per mille) and the smallest chunk.  The default gives the whole range to
@@ -2874,15 +2887,31 @@ pkv_status paged_attention_prefill_fp8(const void* q, const void* k_cache, const
 }  // extern "C"
 
 namespace {
+// This GPU's copy of `scratch`, resolved once per device with the device
+// current (nullptr if that fails).
+void* scratch_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // Decode for every cache dtype; fp8 (E4M3 codes with tensor scales) runs
-// only in the per-CU balanced form.
+// only in the per-CU balanced form.  fixed_scratch: the allocation-free
+// form -- per-CU split with fixed shares only, its partial states and
+// arrival counters in this GPU's `scratch` (workspace arguments ignored).
 pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                        float scale, int32_t window, int32_t partition_size, void* workspace,
                        size_t workspace_bytes, pkv_dtype kv_dtype, float k_scale, float v_scale,
-                       float* out, hipStream_t stream) {
+                       float* out, hipStream_t stream, bool fixed_scratch = false) {
   const bool fp8 = kv_dtype == PKV_FP8_E4M3;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || partition_size < 0 ||
@@ -2896,6 +2925,7 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
               !std::isfinite(v_scale)))
     return PKV_ERR_INVALID;
   if (fp8 && partition_size != 0) return PKV_ERR_UNSUPPORTED;
+  if (fixed_scratch && (kv_dtype == PKV_F32 || partition_size != 0)) return PKV_ERR_UNSUPPORTED;
   const int group = num_q_heads / num_kv_heads;
   if ((kv_dtype == PKV_BF16 || fp8) && group > 16) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PKV_OK;
@@ -2935,7 +2965,29 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.window = window;
   bool cu_form;
   int waves = 0;
-  {
+  if (fixed_scratch) {
+    if (!cu_shape) return PKV_ERR_UNSUPPORTED;
+    // [2 cus][g][D] o, [2 cus][g] m, [2 cus][g] l | overflow | counters
+    const size_t states = balanced_states_bytes(cus, group, head_dim);
+    const int over = cu_over_slots(group, head_dim, num_seqs, true);
+    const size_t overflow = cu_overflow_bytes(cus, over, group, head_dim);
+    const size_t need = states + overflow + size_t(num_seqs) * num_kv_heads * 8;
+    if (need > kScratchBytes) return PKV_ERR_UNSUPPORTED;
+    char* base = static_cast<char*>(scratch_device());
+    if (!base) return PKV_ERR_HIP;
+    float* ws = reinterpret_cast<float*>(base);
+    a.ws_o = a.ws_m = a.ws_l = nullptr;
+    a.bw_o = ws;
+    a.bw_m = ws + size_t(cus) * 2 * group * head_dim;
+    a.bw_l = a.bw_m + size_t(cus) * 2 * group;
+    a.cu_over = reinterpret_cast<float*>(base + states);
+    a.over_slots = over;
+    a.bw_count = reinterpret_cast<unsigned long long*>(base + states + overflow);
+    a.static_permille = 1000;
+    a.chunk_min = kCuStaticChunkMin;
+    a.grid_waves = cus;
+    cu_form = true;
+  } else {
     waves = balanced ? balanced_waves() : 0;
     if (balanced && waves <= 0) return PKV_ERR_HIP;
     const size_t need =
@@ -3044,6 +3096,22 @@ pkv_status paged_attention_decode_window(const void* q, const void* k_cache, con
                      num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len,
                      scale, window, partition_size, workspace, workspace_bytes, kv_dtype, k_scale,
                      v_scale, out, stream);
+}
+
+pkv_status paged_attention_decode_noalloc(const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t num_blocks,
+                                          int32_t max_blocks_per_seq, int32_t max_context_len,
+                                          float scale, int32_t window, pkv_dtype kv_dtype,
+                                          float k_scale, float v_scale, float* out,
+                                          hipStream_t stream) {
+  if (kv_dtype != PKV_FP8_E4M3) k_scale = v_scale = 1.0f;
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len,
+                     scale, window, 0, nullptr, 0, kv_dtype, k_scale, v_scale, out, stream,
+                     true);
 }
 
 pkv_status paged_attention_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
