@@ -2,20 +2,24 @@
 
 A step is one pass of the whole hot path for a batch of sequences, each
 gaining one token:
-  host slot planning + block allocation (C++), one pinned host-to-device
-  upload, block-table deltas, copy-on-write copies (when a shared block is
-  hit), the K/V write, and decode attention (split-K partitions + LSE
-  merge).
+  host slot planning + block allocation (C++), the step's small inputs
+  (slots, table and length deltas, copy-on-write pairs) staged in pinned
+  host memory and read in place by the kernels, block-table deltas,
+  copy-on-write copies (when a shared block is hit), the K/V write, and
+  decode attention (balanced split + log-sum-exp merges inside the launch).
 Contexts grow by one token per step, exactly as in serving.
 
-Workload: gqa-8b-bf16 -- 256 sequences, 32 query / 8 kv heads, head_dim 128,
-bf16 cache, log-normal lengths (median 1000, sigma 1, clipped to [16, 8192],
-one sequence at 273), scattered 16-token blocks.
+Headline workload: gqa-8b-bf16 -- 256 sequences, 32 query / 8 kv heads,
+head_dim 128, bf16 cache, log-normal lengths (median 1000, sigma 1, clipped
+to [16, 8192], one sequence at 273), scattered 16-token blocks.
 
 Prints ONE JSON line.  value = effective KV GB/s of the whole step (K+V
 bytes the decode reads / step time); roofline = the decode main kernel's
 own average duration (HIP events recorded by the library on the kernel's
-stream) against 8 TB/s; cpu_baseline = the CPU oracle timed on this host.
+stream) against 8 TB/s; configs = every workload of the configs table at
+full size (decode with cold caches, decode back to back, whole steps);
+cpu_baseline = the CPU oracle timed on this host, on one core and on all
+cores, per workload (a bounded sample of each).
 """
 from __future__ import annotations
 
@@ -67,53 +71,259 @@ def kernel_name(partition: int) -> str:
     return "decode_bf16_cu_kernel<128,2,2> (per-CU split, LDS fold, merge inside)"
 
 
-def all_configs(path: str, dev):
-    """Decode alone (back to back, after warm-up) on every bf16 workload at
-    its full size; written to ``path`` as JSON."""
+# The five workloads of the configs table, each measured at full size in the
+# default run; gqa-8b-bf16 is also the headline step above.
+CONFIG_KEYS = ("tiny-fp32", "mha-7b-bf16", "gqa-8b-bf16", "long-70b-bf16", "shared-prefix-bf16")
+# bounded CPU samples of each workload: every k-th sequence (all of tiny)
+CPU_SAMPLE_STRIDE = {"tiny-fp32": 1, "mha-7b-bf16": 4, "gqa-8b-bf16": 4, "long-70b-bf16": 2,
+                     "shared-prefix-bf16": 4}
+FLUSH_BYTES = 1 << 30   # written between cold launches: more than L2 + the 256 MB MALL
+
+
+def unique_kv_bytes(w, lens, elem) -> int:
+    """K+V bytes of distinct cached tokens: a shared prefix counts once."""
+    s = w.spec
+    toks = int(lens.astype("int64").sum())
+    if s.prefix_len:
+        toks -= (s.num_seqs - 1) * s.prefix_len
+    return toks * 2 * s.num_kv_heads * s.head_dim * elem
+
+
+def config_measure(dev, key: str, flush, cold: int = 30, b2b: int = 50, steps: int = 30,
+                   warm: int = 5, partition: int = 0):
+    """One workload at full size, three ways:
+      decode_cold  -- median of ``cold`` single decode calls, each timed by
+                      the library's events on the call's stream, with a
+                      1 GiB buffer written before each (L2 and MALL evicted);
+      decode_b2b   -- mean of ``b2b`` decode calls back to back;
+      step         -- mean of ``steps`` whole steps (append one token per
+                      sequence, then decode), timed on the host clock with
+                      synchronizations around the loop, as the headline.
+    Bytes: logical = every sequence's K+V; unique = distinct blocks' tokens
+    (a shared prefix once), the bytes HBM has to deliver."""
     import numpy as np
     import torch
+    from paged_kv_cache_102_amd import _capi as capi
     from paged_kv_cache_102_amd.driver import PagedKV, replay_prefill
     from workloads import synth
-    res = {}
-    for key in ("mha-7b-bf16", "gqa-8b-bf16", "long-70b-bf16", "shared-prefix-bf16"):
-        w = synth.generate(key)
-        s = w.spec
+    w = synth.generate(key, extra_tokens=steps + warm + 2)
+    s = w.spec
+    elem = 4 if s.dtype == "f32" else 2
 
-        def to_dev(rows):
-            return torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).to(dev).view(
-                torch.bfloat16)
-        kv = PagedKV(num_blocks=w.num_blocks, num_seqs=s.num_seqs,
-                     max_blocks_per_seq=w.max_blocks_per_seq, num_q_heads=s.num_q_heads,
-                     num_kv_heads=s.num_kv_heads, head_dim=s.head_dim, dtype=s.dtype, device=dev,
-                     init_order=w.pool_order)
-        replay_prefill(kv, w, to_dev)
-        q = to_dev(w.q)
-        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-        for _ in range(20):
-            kv.decode(q, s.scale, out=out)
-        torch.cuda.synchronize()
-        n = 100
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n):
-            kv.decode(q, s.scale, out=out)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / n
-        logical = kv_bytes(kv.lens, s.num_kv_heads, s.head_dim)
-        blocks = -(-kv.lens.astype(np.int64) // 16)
-        unique = (int(blocks.sum()) if s.prefix_len == 0 else
-                  int(blocks.sum()) - (s.num_seqs - 1) * (s.prefix_len // 16)) * 16 \
-            * 2 * s.num_kv_heads * s.head_dim * 2
-        res[key] = {"ms": round(ms, 4), "seqs_per_s": round(s.num_seqs / ms * 1e3, 1),
-                    "logical_kv_bytes": logical, "unique_kv_bytes": unique,
-                    "effective_kv_gb_per_s": round(logical / ms / 1e6, 1),
-                    "frac_of_hbm_peak_unique": round(unique / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    def to_dev(rows):
+        if s.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(rows)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+    kv = PagedKV(num_blocks=w.num_blocks, num_seqs=s.num_seqs,
+                 max_blocks_per_seq=w.max_blocks_per_seq, num_q_heads=s.num_q_heads,
+                 num_kv_heads=s.num_kv_heads, head_dim=s.head_dim, dtype=s.dtype, device=dev,
+                 init_order=w.pool_order, partition_size=partition)
+    replay_prefill(kv, w, to_dev)
+    q = to_dev(w.q)
+    ones = np.ones(s.num_seqs, np.int32)
+    k1, v1 = to_dev(w.k_app[:s.num_seqs]), to_dev(w.v_app[:s.num_seqs])
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        kv.decode(q, s.scale, out=out)
+    torch.cuda.synchronize()
+    logical = kv_bytes(kv.lens, s.num_kv_heads, s.head_dim, elem)
+    unique = unique_kv_bytes(w, kv.lens, elem)
+    # cold single calls
+    capi.pkv_profile_begin(1)
+    for i in range(cold):
+        flush.fill_(float(i & 7))
+        kv.decode(q, s.scale, out=out)
+    each = capi.pkv_profile_durations()
+    capi.pkv_profile_end()
+    cold_ms = float(np.median(each))
+    # back to back
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(b2b):
+        kv.decode(q, s.scale, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    b2b_ms = e0.elapsed_time(e1) / b2b
+
+    # whole steps (the contexts grow by one token per step)
+    def step():
+        kv.append(k1, v1, ones)
+        kv.decode(q, s.scale, out=out)
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    step_bytes = 0
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+        step_bytes += kv_bytes(kv.lens, s.num_kv_heads, s.head_dim, elem)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / steps
+    step_logical = step_bytes / steps
+    step_unique = step_logical - (logical - unique)
+    gbs = lambda b, ms: round(b / ms / 1e6, 1)
+    frac = lambda b, ms: round(b / ms / 1e6 / HBM_PEAK_GBS, 4)
+    res = {"num_seqs": s.num_seqs, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
+           "head_dim": s.head_dim, "kv_dtype": s.dtype,
+           "mean_context": round(float(kv.lens.mean()) - steps - warm, 1),
+           "split": (f"{partition}-token partitions + log-sum-exp reduce" if partition else
+                     "512-token partitions + reduce (fp32 default)" if s.dtype == "f32" else
+                     "balanced per-CU"),
+           "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+           "decode_cold_ms": round(cold_ms, 4), "decode_b2b_ms": round(b2b_ms, 4),
+           "step_ms": round(step_ms, 4),
+           "decode_cold_gb_per_s": gbs(logical, cold_ms),
+           "decode_cold_frac_of_hbm_peak": frac(unique, cold_ms),
+           "decode_b2b_gb_per_s": gbs(logical, b2b_ms),
+           "decode_b2b_frac_of_hbm_peak": frac(unique, b2b_ms),
+           "step_gb_per_s": gbs(step_logical, step_ms),
+           "step_frac_of_hbm_peak": frac(step_unique, step_ms),
+           "decode_seqs_per_s": round(s.num_seqs / cold_ms * 1e3, 1),
+           "step_seqs_per_s": round(s.num_seqs / step_ms * 1e3, 1)}
+    if s.dtype == "f32":
+        res["decode_cold_latency_us"] = round(cold_ms * 1e3, 2)
+        res["step_latency_us"] = round(step_ms * 1e3, 2)
+        res["note"] = "launch- and latency-bound at this size; the rates are context only"
+    if s.prefix_len:
+        res["note"] = ("logical bytes read the shared prefix once per sequence (served from "
+                       "L2 / MALL after the first reads); frac_of_hbm_peak counts unique bytes")
+    del kv, q, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def configs_measure(dev):
+    """Every workload of the configs table at full size (config_measure),
+    plus the long-context one with the split it is specified with."""
+    import torch
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    res = {}
+    for key in CONFIG_KEYS:
+        log(f"[bench] config {key} ...")
+        res[key] = config_measure(dev, key, flush)
         log(f"[bench] {key}: {res[key]}")
-        del kv, q, out
-        torch.cuda.empty_cache()
-    with open(path, "w") as f:
-        json.dump(res, f, indent=1)
+    log("[bench] gqa-8b shape at 512 sequences ...")
+    res["gqa-8b-bf16-b512"] = config_measure(dev, "gqa-8b-bf16-b512", flush)
+    log("[bench] config long-70b-bf16, 512-token partitions ...")
+    res["long-70b-bf16/partitions-512"] = config_measure(dev, "long-70b-bf16", flush,
+                                                         partition=512)
+    del flush
+    torch.cuda.empty_cache()
+    return res
+
+
+_CPU_STATE = None   # the oracle state the forked workers of cpu_child read
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+    global _CPU_LIMIT
+    _CPU_LIMIT = threadpool_limits(1)   # one BLAS thread per worker process
+
+
+def _cpu_worker(seqs):
+    from oracle import attention
+    w, st = _CPU_STATE
+    s = w.spec
+    out = attention.decode(w.q, st.cache, st.tables, st.lens, s.num_q_heads, s.num_kv_heads,
+                           s.scale, seqs=seqs)
+    return seqs, out[seqs]
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_child(seconds: float):
+    """The oracle, as it stands, on this host's cores: for every workload, a
+    bounded sample (every k-th sequence, CPU_SAMPLE_STRIDE) replayed on the
+    oracle, then its decode timed (a) on one core (BLAS limited to one
+    thread) and (b) on all cores of this process's affinity (at most 16, the
+    host share of one GPU): a fork pool of that many single-threaded
+    workers, each decoding a share of the sequences.  Runs in a process of
+    its own that never touches the GPU.  Prints one JSON line."""
+    import multiprocessing
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attention, replay
+    from workloads import synth
+    global _CPU_STATE
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    res = {}
+    for key in CONFIG_KEYS:
+        w = synth.generate(key)
+        k = CPU_SAMPLE_STRIDE[key]
+        sub = synth.subset(w, range(0, w.spec.num_seqs, k), seed=77) if k > 1 else w
+        del w
+        st = replay.prefill(sub)
+        s = sub.spec
+        elem = 4 if s.dtype == "f32" else 2
+        nbytes = kv_bytes(st.lens, s.num_kv_heads, s.head_dim, elem)
+        B = s.num_seqs
+        with threadpool_limits(1):
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                attention.decode(sub.q, st.cache, st.tables, st.lens, s.num_q_heads,
+                                 s.num_kv_heads, s.scale)
+                reps += 1
+                if time.perf_counter() - t0 >= seconds or reps >= 200:
+                    break
+            one = time.perf_counter() - t0
+        _CPU_STATE = (sub, st)
+        n = min(cores, B)
+        parts = [list(range(i, B, n)) for i in range(n)]
+        with multiprocessing.get_context("fork").Pool(n, initializer=_cpu_worker_init) as pool:
+            pool.map(_cpu_worker, parts)          # warm the workers
+            reps_all, t0 = 0, time.perf_counter()
+            while True:
+                pool.map(_cpu_worker, parts)
+                reps_all += 1
+                if time.perf_counter() - t0 >= seconds or reps_all >= 400:
+                    break
+            allc = time.perf_counter() - t0
+        _CPU_STATE = None
+        res[key] = {"sample": f"{B} of {B * k} sequences (one in {k})"
+                              if k > 1 else f"all {B} sequences",
+                    "kv_bytes": nbytes,
+                    "one_core": {"gb_per_s": round(nbytes * reps / one / 1e9, 4),
+                                 "seqs_per_s": round(B * reps / one, 2), "passes": reps,
+                                 "seconds": round(one, 2)},
+                    "all_cores": {"cores": n, "gb_per_s": round(nbytes * reps_all / allc / 1e9, 4),
+                                  "seqs_per_s": round(B * reps_all / allc, 2),
+                                  "passes": reps_all, "seconds": round(allc, 2)}}
+        log(f"[cpu] {key}: {res[key]}")
+        del sub, st
+    print(json.dumps({"cores": cores, "cpu_model": cpu_model(), "configs": res}), flush=True)
+
+
+def cpu_baseline(seconds: float = 3.0):
+    """Runs cpu_child in a fresh interpreter (this process has the GPU open)
+    and shapes its result: value = the headline workload on all cores."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-child",
+                        str(seconds)], capture_output=True, text=True)
+    sys.stderr.write(r.stderr)
+    if r.returncode != 0:
+        raise RuntimeError(f"CPU baseline child failed ({r.returncode})")
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    head = d["configs"][WORKLOAD]
+    return {"value": head["all_cores"]["gb_per_s"], "unit": "GB/s",
+            "cores": head["all_cores"]["cores"], "kind": "oracle",
+            "sample": f"{WORKLOAD}: {head['sample']} at their prefill lengths, numpy float64 "
+                      f"decode, {head['all_cores']['passes']} passes over "
+                      f"{head['all_cores']['seconds']} s on a pool of "
+                      f"{head['all_cores']['cores']} single-threaded processes",
+            "seqs_per_s": head["all_cores"]["seqs_per_s"],
+            "one_core": head["one_core"], "cpu_model": d["cpu_model"],
+            "host_cores_available": d["cores"], "per_config": d["configs"]}
 
 
 BF16_MFMA_PEAK_TFLOPS = 2500.0
@@ -410,30 +620,6 @@ def paged_vs_contiguous(dev, w, q, out, reps: int):
                     "sequence's blocks consecutive in the pool"}
 
 
-def cpu_baseline(w, seconds: float = 12.0):
-    """The oracle, as it stands, on this host: decode over the whole batch,
-    repeated until ``seconds`` of CPU work, single-threaded BLAS."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-    from oracle import attention, replay
-    st = replay.prefill(w)
-    s = w.spec
-    reps, t0 = 0, time.perf_counter()
-    with threadpool_limits(1):
-        while True:
-            attention.decode(w.q, st.cache, st.tables, st.lens, s.num_q_heads, s.num_kv_heads,
-                             s.scale)
-            reps += 1
-            if time.perf_counter() - t0 >= seconds or reps >= 4:
-                break
-    dt = time.perf_counter() - t0
-    gbs = kv_bytes(st.lens, s.num_kv_heads, s.head_dim) * reps / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seqs_per_s": round(s.num_seqs * reps / dt, 2),
-            "sample": f"full {s.num_seqs}-sequence batch at its prefill lengths, {reps} pass(es), "
-                      f"{dt:.1f} s, numpy float64, 1 thread"}
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -454,9 +640,15 @@ def main():
                     help="skip the multi-query (chunked prefill) measurement")
     ap.add_argument("--no-extras", dest="extras", action="store_false",
                     help="skip the sliding-window, swap and prefix-cache measurements")
-    ap.add_argument("--all-configs", metavar="PATH", default=None,
-                    help="also time decode alone on every workload and write them to PATH (JSON)")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip the per-workload measurements of every config")
+    ap.add_argument("--cpu-seconds", type=float, default=3.0,
+                    help="seconds of oracle work per workload and core setting")
+    ap.add_argument("--cpu-child", type=float, default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_child is not None:      # the CPU baseline's own process: no GPU
+        cpu_child(args.cpu_child)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path "
               "runs on a single GPU.", file=sys.stderr)
@@ -620,13 +812,12 @@ def main():
         "hbm_read_ceiling_gbs": round(ceiling, 1) if ceiling else None,
         "decode_frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None,
     }
-    if args.all_configs:
-        del kv
-        torch.cuda.empty_cache()
-        all_configs(args.all_configs, dev)
+    del kv
+    torch.cuda.empty_cache()
+    result["configs"] = configs_measure(dev) if args.configs else None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
