@@ -45,8 +45,11 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    src = os.path.join(ROOT, "paged_kv_cache_102_amd", "csrc", "kernels.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    """Hash of the sources the decode kernels are built from."""
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "device_common.h"):
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_102_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def committed_traffic():

@@ -9,7 +9,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpagedkv.so")
-SOURCES = [os.path.join(HERE, "csrc", "kernels.hip"), os.path.join(HERE, "csrc", "pool.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", "kernels.hip"), os.path.join(HERE, "csrc", "prefill.hip"),
+           os.path.join(HERE, "csrc", "pool.cpp")]
 
 
 def hipcc() -> str:

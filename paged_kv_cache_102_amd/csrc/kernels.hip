@@ -14,9 +14,8 @@
 //                     sliding window
 //   decode_bf16_balanced  the same split per wavefront (fallback form)
 //   decode_bf16 / decode_f32 + lse_reduce  fixed split-K partitions
-//   prefill_bf16      chunked prefill (multi-query, causal) on the matrix cores,
-//                     bf16 or FP8 cache, optional sliding window
 //   stream_read       plain streaming read, the bandwidth reference
+// (chunked prefill is in prefill.hip; shared helpers in device_common.h)
 //
 // Sources: "PagedAttention por dentro" (blog.lo0.es), sections "La tabla de
 // paginas (block table)", "Copy-on-write para sampling paralelo", "El kernel
@@ -54,84 +53,13 @@
 #include <mutex>
 #include <vector>
 
+#include "device_common.h"
 #include "pagedkv.h"
 
 // The allocation-free decode's scratch (see scratch_device below).
 static __device__ __align__(256) unsigned char scratch[size_t(16) << 20];
 
 namespace {
-
-constexpr int kBlock = PKV_BLOCK_SIZE;
-constexpr int kDefaultPartition = 512;
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// ------------------------------------------------------------------ in-tile order
-__host__ __device__ inline int k_elem(int t, int d) { return (d >> 3) * 128 + t * 8 + (d & 7); }
-__host__ __device__ inline int v_elem(int t, int d) {
-  return (d >> 5) * 512 + (t >> 2) * 128 + (d & 15) * 8 + ((d >> 4) & 1) * 4 + (t & 3);
-}
-
-// ------------------------------------------------------------------ wave helpers
-// Reductions over the four lanes l, l^16, l^32, l^48 (one per 16-lane row)
-// with the gfx950 row-swap permutes: permlane16_swap pairs rows (0,1) and
-// (2,3), permlane32_swap pairs rows (0,2) and (1,3); both results of a swap
-// hold the two partners, so combining them gives the pair's value in every lane.
-__device__ inline float group_max(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ inline float group_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-__device__ inline float wave_sum(float x) {
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
-}
-
-// Two weights as packed bf16 pairs: hi = the weights rounded to nearest even
-// (gfx950's packed conversion), lo = the rounded remainders, so hi + lo
-// carries each weight to about 16 significant bits.  Inputs are finite.
-__device__ inline void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
-  const f32x2 rest = {a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u)};
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
-}
-
-// Two bf16 -> two f16, exact for magnitudes below 65520 (8 significant bits
-// fit in 11; under 2^-14 f16 is subnormal, within 2^-25 of the value).
-__device__ inline uint32_t bf16x2_to_f16x2(uint32_t w) {
-  const f32x2 f = {__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
-}
-// Bit 15 / 31 set where a bf16 half has magnitude >= 65536 (0x4780), inf or
-// NaN: the halves that have no f16 equal.  The add cannot carry across halves.
-__device__ inline uint32_t bf16x2_beyond_f16(uint32_t w) {
-  return ((w & 0x7FFF7FFFu) + 0x38803880u) & 0x80008000u;
-}
-
-// Small index inputs of the cache-update kernels (slots, table deltas, block
-// pairs) may sit in pinned host memory that the host refills between
-// launches.  System-scope loads are never served from a cached copy, so a
-// refilled buffer is seen as the host wrote it; within a wave, lanes reading
-// the same word share one request.
-__device__ inline int64_t ld_sys(const int64_t* p) {
-  return __hip_atomic_load(const_cast<int64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ inline int32_t ld_sys(const int32_t* p) {
-  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
 
 // ------------------------------------------------------------------ A2: table deltas
 __global__ void table_update_kernel(int32_t* __restrict__ tables, int64_t elems,
@@ -315,14 +243,6 @@ __device__ inline int first_block_of(const DecodeArgs& a, int L) {
   return win_lo<WIN>(a, L) / kBlock;
 }
 
-// Buffer resource over one cache tile: loads at byte offsets below `bytes`
-// read memory; with bytes == 0 every load returns zeros without a memory
-// request.  That lets the pipeline issue the same loads on every trip
-// (so the load counter waits are static) while prefetches past the end of
-// a partition cost nothing.
-__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
 
 // AUX is the cache policy of the K/V loads: 2 = non-temporal (the cache is
 // streamed once per step; on MI355X this lifts the read rate by ~12 %),
@@ -534,13 +454,6 @@ void decode_bf16_kernel(DecodeArgs a) {
 // (output written directly); at most the first and the last segment of a
 // wave are partial, and their (o, m, l) states go to slots 0 and 1 of that
 // wave for the merge kernel.
-// Load of a wave-uniform element through the scalar data cache (read-only
-// constant address space): it waits on the scalar counter, so it does not
-// drain the vector loads in flight, as a vector load with a full wait would.
-__device__ inline int load_uniform(const int* p, int64_t i) {
-  using const_int_ptr = const __attribute__((address_space(4))) int*;
-  return *((const_int_ptr)p + i);
-}
 
 // Tiles of a sequence in the work list: its blocks from the window's first.
 template <bool WIN = true>
@@ -966,39 +879,6 @@ void decode_bf16_balanced_kernel(DecodeArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ FP8 E4M3 (OCP) codes
-// Decode: every E4M3 value has at most 4 significant bits and an exponent
-// inside bf16's range, so each code has an exact bf16.  gfx950's
-// v_cvt_scalef32_pk_bf16_fp8 with scale 1 produces it for two codes in one
-// instruction; it reads the OCP E4M3 encoding, and on MI355X its output
-// equals the format's definition for all 256 codes (NaN codes give NaN).
-typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
-template <bool HIGH>  // bytes 2, 3 of w when set, else bytes 0, 1
-__device__ inline uint32_t e4m3x2_to_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
-}
-// 8 codes (bytes of lo then hi) -> 8 bf16 in the same order
-__device__ inline uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  uint4 r;
-  r.x = e4m3x2_to_bf16x2<false>(lo);
-  r.y = e4m3x2_to_bf16x2<true>(lo);
-  r.z = e4m3x2_to_bf16x2<false>(hi);
-  r.w = e4m3x2_to_bf16x2<true>(hi);
-  return r;
-}
-// The same 8 codes as f16 (v_cvt_scalef32_pk_f16_fp8, scale 1)
-template <bool HIGH>
-__device__ inline uint32_t e4m3x2_to_f16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HIGH));
-}
-__device__ inline uint4 e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
-  uint4 r;
-  r.x = e4m3x2_to_f16x2<false>(lo);
-  r.y = e4m3x2_to_f16x2<true>(lo);
-  r.z = e4m3x2_to_f16x2<false>(hi);
-  r.w = e4m3x2_to_f16x2<true>(hi);
-  return r;
-}
 // Byte offset in an FP8 tile of lane `lane`'s 8-byte piece `j` (the codes of
 // its bf16 operand piece j).  Pieces 2i and 2i + 1 of all lanes fill bytes
 // [1024 i, 1024 i + 1024) as 64 lanes x 16 bytes, so one 16-byte load per
@@ -1728,542 +1608,6 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ next: multi-query (chunked prefill), bf16
-// Several new query tokens per sequence over the same paged cache: sequence
-// b's chunk of n_b tokens holds the last n_b of its L_b cached positions
-// (their K/V written before the call); chunk token i sits at position
-// p = L_b - n_b + i and attends to positions 0..p (causal inside the chunk;
-// with a sliding window of W tokens, p-W+1..p).  A decode step is the case
-// n_b = 1.
-//
-// One workgroup of 8 wavefronts per (sequence, kv head, tile of query
-// positions), two per SIMD.  The tile's score columns are (position,
-// head-in-group) pairs, 256 of them (32 per wavefront, as two 16-column MFMA
-// tiles), so 256 / g positions per tile.  The K and V tiles of SB consecutive
-// blocks (one stage) are loaded once per workgroup into LDS (double-buffered,
-// the next stage's global loads in flight during this stage's compute) and
-// every wavefront reads them from there:
-//   S^T = K . Q^T   v_mfma_f32_16x16x32_bf16, A = K piece j (16 tokens x 32
-//                   channels, the cache's lane order), B = Q^T chunk j;
-//   O  += P . V     v_mfma_f32_16x16x32_f16 over each pair of blocks (32
-//                   tokens): a lane's k-index i < 4 is token 4(l/16)+i of the
-//                   first block, i >= 4 the same token of the second block --
-//                   the layout S^T comes out in, and the halves of the V
-//                   tile's lane pieces of the two blocks;
-// with P and V as f16 (V converted on its way into LDS; a bf16 V element
-// beyond f16's range makes the workgroup run again with P as a bf16 high
-// part plus residual and V as bf16).  The running max
-// is raised only when a block's max exceeds it by more than 2^8 (the
-// normaliser uses the same reference, so the result is unchanged, and the
-// accumulator is rescaled rarely).
-struct PrefillArgs {
-  const void* q;          // [T][Hq][D] bf16, T = qstart[B]
-  const void* kc;
-  const void* vc;
-  const int32_t* tables;
-  const int32_t* lens;
-  const int32_t* qstart;  // [B + 1] first chunk row of each sequence
-  float* out;             // [T][Hq][D] fp32
-  int num_seqs, num_q_heads, num_kv_heads, group;
-  int qtp;                // query positions per workgroup tile: 256 / group
-  int tiles;              // tiles per sequence: ceil(max_query_len / qtp)
-  int num_blocks, max_blocks, max_ctx;
-  float scale_log2e;
-  int window;  // sliding window in tokens: position p sees p-window+1 .. p (0: 0 .. p)
-  float out_scale;  // 1, or the V scale of an FP8 cache
-};
-
-constexpr int kPfWaves = 8;
-constexpr int kPfColTiles = 2;                       // 16-column tiles per wavefront
-constexpr int kPfCols = kPfWaves * kPfColTiles * 16;  // score columns per workgroup
-constexpr float kPfRescale = 8.0f;                   // lazy max threshold (log2 domain)
-constexpr int kPfStageBlocks = 4;                    // default blocks per pipeline stage
-template <bool B>
-struct PfF16 {  // P.V operand type of a prefill pass: f16 (true) or bf16 high + residual
-  static constexpr bool value = B;
-};
-
-// SB: blocks per pipeline stage (even: P.V takes them in pairs).  F8: the
-// cache holds FP8 E4M3 codes; each lane's 16 codes of a 1 KiB run are
-// expanded to its two bf16 pieces on the way into LDS, so everything after
-// the staging is the bf16 path (K scale folded into the score scale, V
-// scale into out_scale).
-template <int D, bool WIN, int SB, bool F8 = false>
-__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_bf16_kernel(PrefillArgs a) {
-  static_assert(SB % 2 == 0, "blocks per stage come in pairs");
-  constexpr int NJ = D / 32;                  // K / V pieces per tile
-  constexpr int NT = D / 16;                  // 16-channel output tiles
-  constexpr int NQ = kPfColTiles;
-  constexpr int TILE_BYTES = kBlock * D * 2;
-  constexpr int STAGE_BYTES = 2 * SB * TILE_BYTES;  // blocks 0 .. SB-1 x (K, V)
-  constexpr int TILE_PIECES = TILE_BYTES / 16;
-  // tiles in global memory: as in LDS, or FP8 at one byte per element
-  constexpr int TILE_G = F8 ? kBlock * D : TILE_BYTES;
-  constexpr int TILE_PIECES_G = TILE_G / 16;
-  constexpr int PT_G = 2 * SB * TILE_PIECES_G / (64 * kPfWaves);  // global pieces per thread
-  static_assert(PT_G >= 1 && (2 * SB * TILE_PIECES_G) % (64 * kPfWaves) == 0,
-                "a stage's global pieces spread evenly over the threads");
-  constexpr int NBUF = 2;  // stage s, and stage s + 1 being filled
-  __shared__ __align__(16) unsigned char lds[NBUF * STAGE_BYTES];
-
-  // Work item: workgroup i runs on XCD i % 8, and all query tiles of one
-  // (sequence, kv head) pair run on one XCD, so they read its K/V through
-  // one L2.  When the pairs are a multiple of 8, XCD x takes the pairs
-  // p = x (mod 8) -- with 8 kv heads, head x of every sequence -- so every
-  // XCD gets the same mix of context lengths; inside an XCD the longer items
-  // go first, so the shorter ones fill in at the end.  Otherwise each XCD
-  // takes a contiguous run of items.
-  const int N = gridDim.x, id = blockIdx.x;
-  const int npairs = a.num_seqs * a.num_kv_heads;
-  int pair, qt;
-  if (npairs % 8 == 0) {
-    const int x = id % 8, j = id / 8;
-    const int items = npairs / 8 * a.tiles;  // of this XCD: pairs x + 8 m, all tiles
-    if (items <= 64) {
-      // Longest first: lane i holds item i's stage count (the same arithmetic
-      // as below), ranks by descending count with ties by index (a
-      // permutation, identical in every workgroup), and this workgroup takes
-      // the item of rank j.
-      const int i = threadIdx.x & 63;
-      int work = -1;
-      if (i < items) {
-        const int ib = (x + 8 * (i / a.tiles)) / a.num_kv_heads;
-        const int iq0 = (i % a.tiles) * a.qtp;
-        const int ins = a.qstart[ib], in = a.qstart[ib + 1] - ins, iL = a.lens[ib];
-        work = 0;
-        if (iq0 < in && in > 0 && iL >= in) {
-          const int pf = iL - in + iq0, pl = pf + min(a.qtp, in - iq0) - 1;
-          const int i0w = (WIN ? max(0, pf - a.window + 1) : 0) / kBlock;
-          work = pl / kBlock + 1 - i0w;
-        }
-      }
-      int rank = 0;
-      for (int k = 0; k < items; ++k) {
-        const int wk = __builtin_amdgcn_readlane(work, k);
-        rank += (wk > work || (wk == work && k < i)) ? 1 : 0;
-      }
-      const int sel = static_cast<int>(__builtin_ctzll(
-          __builtin_amdgcn_ballot_w64(i < items && rank == j)));
-      pair = x + 8 * (sel / a.tiles);
-      qt = sel % a.tiles;
-    } else {
-      pair = x + 8 * (j / a.tiles);
-      qt = a.tiles - 1 - j % a.tiles;
-    }
-  } else {
-    const int full = N / 8 * 8;
-    const int w = id < full ? (id % 8) * (N / 8) + id / 8 : id;
-    qt = w % a.tiles;
-    pair = w / a.tiles;
-  }
-  const int kvh = pair % a.num_kv_heads;
-  const int b = pair / a.num_kv_heads;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hcol = lane & 15;
-  const int grp = lane >> 4;
-  const int g = a.group;
-  const int QTP = a.qtp;
-  const int qs = load_uniform(a.qstart, b);
-  const int n = load_uniform(a.qstart, b + 1) - qs;
-  const int q0 = qt * QTP;
-  if (qt == a.tiles - 1 && n > a.tiles * QTP) {
-    // chunk rows beyond the grid's tiles (max_query_len below this chunk):
-    // NaN, so that no row of the output is left unwritten
-    const int r0 = a.tiles * QTP;
-    for (int c = wave; c < (n - r0) * g; c += kPfWaves) {
-      float* dst = a.out + ((int64_t(qs) + r0 + c / g) * a.num_q_heads + int64_t(kvh) * g + c % g) * D;
-      for (int e = lane; e < D; e += 64) dst[e] = __builtin_nanf("");
-    }
-  }
-  if (q0 >= n || n <= 0) return;
-  const int L = load_uniform(a.lens, b);
-  const int nq = min(QTP, n - q0);  // positions in this tile
-  const int ncol = nq * g;          // live columns
-  auto out_row = [&](int c) -> float* {  // output row of column c
-    return a.out + ((int64_t(qs) + q0 + c / g) * a.num_q_heads + int64_t(kvh) * g + c % g) * D;
-  };
-  const bool len_bad = L < 0 || L > a.max_ctx || int64_t(L) > int64_t(a.max_blocks) * kBlock ||
-                       n > L;
-  if (len_bad) {
-    for (int c = wave; c < ncol; c += kPfWaves)
-      for (int e = lane; e < D; e += 64) out_row(c)[e] = __builtin_nanf("");
-    return;
-  }
-  const int p_first = L - n + q0;  // first and last position of the tile
-  const int p_last = p_first + nq - 1;
-  const int t_lo = WIN ? max(0, p_first - a.window + 1) : 0;  // earliest visible position
-  const int i0 = t_lo / kBlock;
-  const int nblk = p_last / kBlock + 1 - i0;
-  const int nst = (nblk + SB - 1) / SB;
-  const int32_t* row = a.tables + int64_t(b) * a.max_blocks + i0;
-
-  // this lane's columns: c = 16 (NQ wave + t) + hcol -> (position, head)
-  int pos[NQ], lo_c[NQ];
-#pragma unroll
-  for (int t = 0; t < NQ; ++t) {
-    const int c = (NQ * wave + t) * 16 + hcol;
-    pos[t] = c < ncol ? p_first + c / g : p_last;
-    lo_c[t] = WIN ? pos[t] - a.window + 1 : 0;
-  }
-
-  // Q^T as B operands: lane holds q[row of column hcol][32j + 8 grp .. +8];
-  // one resource over the tile's query rows, padding columns read past it (0)
-  bf16x8 qf[NQ][NJ];
-  {
-    const int row_bytes = a.num_q_heads * D * 2;
-    const char* qb = static_cast<const char*>(a.q) + (int64_t(qs) + q0) * row_bytes;
-    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(qb, nq * row_bytes);
-#pragma unroll
-    for (int t = 0; t < NQ; ++t) {
-      const int c = (NQ * wave + t) * 16 + hcol;
-      const int qoff = c < ncol ? (c / g) * row_bytes + (kvh * g + c % g) * D * 2 : nq * row_bytes;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        qf[t][j] = __builtin_bit_cast(
-            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + (32 * j + grp * 8) * 2, 0, 0));
-    }
-  }
-
-  const char* kc = static_cast<const char*>(a.kc) + int64_t(kvh) * TILE_G;
-  const char* vc = static_cast<const char*>(a.vc) + int64_t(kvh) * TILE_G;
-  const int64_t block_bytes = int64_t(a.num_kv_heads) * TILE_G;
-  bool bad = false;
-
-  // Stage loader: thread tid moves pieces 512 u + tid (u < PT) of the stage's
-  // tiles (block 0 K, block 0 V, block 1 K, ...); a wavefront's 64 pieces lie
-  // in one tile, so the tile (and its block id, read once per stage through
-  // the scalar cache) is wave-uniform.  V slots outside [t_lo, L) are zeroed
-  // when the pieces go into LDS, a trip after their loads (they may hold
-  // anything; masking them at load time would wait for the loads at once).
-  // An FP8 run expands to two bf16 runs as it goes into LDS.
-  uint4 st[PT_G];
-  auto gload = [&](int s) {
-    int ph[SB], by[SB];
-#pragma unroll
-    for (int k = 0; k < SB; ++k) {
-      const int rel = SB * s + k;
-      ph[k] = 0;
-      by[k] = 0;
-      if (rel < nblk) {
-        ph[k] = load_uniform(row, rel);
-        if (ph[k] < 0 || ph[k] >= a.num_blocks)
-          bad = true;
-        else
-          by[k] = TILE_G;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < PT_G; ++u) {
-      // the wavefront's 64 pieces: a 1 KiB run at a uniform offset of its tile
-      const int first = 64 * kPfWaves * u + 64 * wave;
-      const int tile = first / TILE_PIECES_G;
-      const int off0 = (first % TILE_PIECES_G) * 16;
-      int phys = 0, bytes = 0;  // selected, not indexed: ph and by stay in registers
-#pragma unroll
-      for (int k = 0; k < SB; ++k)
-        if ((tile >> 1) == k) {
-          phys = ph[k];
-          bytes = by[k];
-        }
-      const char* base = ((tile & 1) ? vc : kc) + (bytes ? int64_t(phys) * block_bytes : 0) + off0;
-      const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, bytes ? bytes - off0 : 0);
-      st[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, 0));
-    }
-  };
-  // V slots of stage s outside [t_lo, L): lane l of a 1 KiB V run holds
-  // tokens 4 (l / 16) .. + 3 of its block
-  auto vmask = [&](int s, int tile, uint4& x) {
-    if (tile & 1) {
-      const int t0 = (i0 + SB * s + (tile >> 1)) * kBlock + 4 * grp;
-      if (t0 < t_lo || t0 + 4 > L) {
-        auto in = [&](int t) { return t < L && t >= t_lo; };
-        const uint32_t m01 = (in(t0) ? 0x0000FFFFu : 0u) | (in(t0 + 1) ? 0xFFFF0000u : 0u);
-        const uint32_t m23 = (in(t0 + 2) ? 0x0000FFFFu : 0u) | (in(t0 + 3) ? 0xFFFF0000u : 0u);
-        x.x &= m01;
-        x.y &= m23;
-        x.z &= m01;
-        x.w &= m23;
-      }
-    }
-  };
-  // V goes into LDS as f16 when P.V runs on f16 operands (H); a bf16 V
-  // element with no f16 equal is noted in `wide` (the workgroup then runs
-  // again with bf16 operands)
-  uint32_t wide = 0;
-  auto lwrite = [&](int s, auto h) {
-    constexpr bool H = decltype(h)::value;
-    unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
-#pragma unroll
-    for (int u = 0; u < PT_G; ++u) {
-      const int first = 64 * kPfWaves * u + 64 * wave;  // same run as in gload
-      const int tile = first / TILE_PIECES_G;
-      if constexpr (F8) {
-        // FP8 run i of the tile holds operand pieces 2i and 2i + 1 of each
-        // lane (E4M3 values are exact in both bf16 and f16)
-        const uint4 w = st[u];
-        uint4 x, y;
-        if (H && (tile & 1)) {
-          x = e4m3x8_to_f16x8(w.x, w.y);
-          y = e4m3x8_to_f16x8(w.z, w.w);
-        } else {
-          x = e4m3x8_to_bf16x8(w.x, w.y);
-          y = e4m3x8_to_bf16x8(w.z, w.w);
-        }
-        vmask(s, tile, x);
-        vmask(s, tile, y);
-        unsigned char* d = sb + tile * TILE_BYTES + 2048 * ((first % TILE_PIECES_G) / 64) + lane * 16;
-        *reinterpret_cast<uint4*>(d) = x;
-        *reinterpret_cast<uint4*>(d + 1024) = y;
-      } else {
-        uint4 x = st[u];
-        vmask(s, tile, x);  // first: slots outside the context may hold anything
-        if (H && (tile & 1)) {
-          wide |= bf16x2_beyond_f16(x.x) | bf16x2_beyond_f16(x.y) | bf16x2_beyond_f16(x.z) |
-                  bf16x2_beyond_f16(x.w);
-          x = make_uint4(bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
-                         bf16x2_to_f16x2(x.w));
-        }
-        *reinterpret_cast<uint4*>(sb + tile * TILE_BYTES + (first % TILE_PIECES) * 16 + lane * 16) = x;
-      }
-    }
-  };
-
-  f32x4 o[NQ][NT];
-  // running max per column (log2 domain, scaled; a finite floor, so that a
-  // column with nothing visible yet gets weights exp2(-inf - floor) = 0),
-  // and the normalisers: row sums of the same bf16 weight parts that P.V
-  // uses, formed by the matrix cores (P times a column of ones) in the
-  // output layout, so numerator and denominator share every rounding
-  float m[NQ];
-  f32x4 lacc[NQ];
-  const f16x8 ones16 = __builtin_bit_cast(f16x8, make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
-  // weights exp2(cs * s - m) with cs >= 0: a negative scale negates Q
-  // instead (exact in bf16), so the scaled max is the raw max times cs
-  const float cs = fabsf(a.scale_log2e);
-  if (a.scale_log2e < 0.f) {
-#pragma unroll
-    for (int t = 0; t < NQ; ++t)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        uint4 x = __builtin_bit_cast(uint4, qf[t][j]);
-        x.x ^= 0x80008000u;
-        x.y ^= 0x80008000u;
-        x.z ^= 0x80008000u;
-        x.w ^= 0x80008000u;
-        qf[t][j] = __builtin_bit_cast(bf16x8, x);
-      }
-  }
-
-  // weights of the stage being processed: f16 pairs (H), else bf16 high
-  // parts and residuals
-  uint32_t phi[NQ][2 * SB], plo[NQ][2 * SB];
-  // O += P . V over each pair of blocks of stage s (k < 4: the pair's first
-  // block, k >= 4: its second); each V piece is read once and used by all
-  // column tiles
-  auto pv = [&](int s, auto h) {
-    constexpr bool H = decltype(h)::value;
-    const unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
-    // the matrix-core phases (here and the scores) run at raised wave
-    // priority: the two wavefronts of a SIMD pass each barrier together, and
-    // the issue arbiter then favours the one that reaches its products first,
-    // so the other's vector work fills in beside them (-3 % on the bf16 form)
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int pp = 0; pp < SB / 2; ++pp) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const uint4 v0 = *reinterpret_cast<const uint4*>(sb + (4 * pp + 1) * TILE_BYTES + 1024 * j + lane * 16);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(sb + (4 * pp + 3) * TILE_BYTES + 1024 * j + lane * 16);
-        if constexpr (H) {
-          const f16x8 vlo = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-          const f16x8 vhi = __builtin_bit_cast(f16x8, make_uint4(v0.z, v0.w, v1.z, v1.w));
-#pragma unroll
-          for (int t = 0; t < NQ; ++t) {
-            const f16x8 ph = __builtin_bit_cast(f16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
-                                                                  phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
-            o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vlo, o[t][2 * j], 0, 0, 0);
-            o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vhi, o[t][2 * j + 1], 0, 0, 0);
-          }
-          continue;
-        }
-        const bf16x8 vlo = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-        const bf16x8 vhi = __builtin_bit_cast(bf16x8, make_uint4(v0.z, v0.w, v1.z, v1.w));
-#pragma unroll
-        for (int t = 0; t < NQ; ++t) {
-          const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
-                                                                  phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
-          const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(plo[t][4 * pp], plo[t][4 * pp + 1],
-                                                                  plo[t][4 * pp + 2], plo[t][4 * pp + 3]));
-          o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vlo, o[t][2 * j], 0, 0, 0);
-          o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vlo, o[t][2 * j], 0, 0, 0);
-          o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vhi, o[t][2 * j + 1], 0, 0, 0);
-          o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vhi, o[t][2 * j + 1], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < NQ; ++t) {
-        if constexpr (H) {
-          const f16x8 ph = __builtin_bit_cast(f16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
-                                                                phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
-          lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, ones16, lacc[t], 0, 0, 0);
-          continue;
-        }
-        const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
-                                                                phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
-        const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(plo[t][4 * pp], plo[t][4 * pp + 1],
-                                                                plo[t][4 * pp + 2], plo[t][4 * pp + 3]));
-        lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ones, lacc[t], 0, 0, 0);
-        lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, ones, lacc[t], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-  };
-
-  // scores of stage s, softmax update, weights into phi / plo
-  auto score = [&](int s, auto h) {
-    constexpr bool H = decltype(h)::value;
-    const unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
-    const int tb0 = (i0 + SB * s) * kBlock;  // first position of the stage
-    // scores of all blocks of the stage for every column tile
-    f32x4 sc[NQ][SB];
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int bb = 0; bb < SB; ++bb) {
-      bf16x8 kx[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        kx[j] = *reinterpret_cast<const bf16x8*>(sb + (2 * bb) * TILE_BYTES + 1024 * j + lane * 16);
-#pragma unroll
-      for (int t = 0; t < NQ; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx[j], qf[t][j], acc, 0, 0, 0);
-        sc[t][bb] = acc;
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    // masks are needed only where the stage reaches past the tile's first
-    // position (causal) or before its last column's window start
-    const bool edge = tb0 + SB * kBlock - 1 > p_first || (WIN && tb0 < p_last - a.window + 1);
-#pragma unroll
-    for (int t = 0; t < NQ; ++t) {
-      // raw scores; masked ones become -inf (exp2 of them is 0)
-      float sv[4 * SB];
-#pragma unroll
-      for (int bb = 0; bb < SB; ++bb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sv[4 * bb + r] = sc[t][bb][r];
-      if (edge) {
-#pragma unroll
-        for (int e = 0; e < 4 * SB; ++e) {
-          const int tp = tb0 + (e >> 2) * kBlock + grp * 4 + (e & 3);
-          if (tp > pos[t] || tp < lo_c[t]) sv[e] = -INFINITY;
-        }
-      }
-      float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-#pragma unroll
-      for (int e = 8; e < 4 * SB; e += 4)
-        mloc = fmaxf(mloc, fmaxf(fmaxf(sv[e], sv[e + 1]), fmaxf(sv[e + 2], sv[e + 3])));
-      mloc = group_max(mloc) * cs;
-      // lazy max: raise it only when the stage max exceeds it by 2^8
-      const bool raise = mloc > m[t] + kPfRescale;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m[t] - mloc) : 1.0f;
-        m[t] = raise ? mloc : m[t];
-        // output rows are columns 4 grp + r of the tile; their factors sit in lanes 4 grp + r
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float ar = __shfl(alpha, grp * 4 + r);
-          lacc[t][r] *= ar;
-#pragma unroll
-          for (int k = 0; k < NT; ++k) o[t][k][r] *= ar;
-        }
-      }
-      // (a column's masked scores are -inf, its unmasked ones finite: the
-      // fma gives -inf or a finite value for any cs >= 0 except cs = 0,
-      // where -inf * 0 is NaN; masks therefore select 0 after exp2)
-      float p[4 * SB];
-#pragma unroll
-      for (int e = 0; e < 4 * SB; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], cs, -m[t]));
-      if (edge) {
-#pragma unroll
-        for (int e = 0; e < 4 * SB; ++e)
-          if (sv[e] == -INFINITY) p[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 2 * SB; ++e) {
-        if constexpr (H)
-          phi[t][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p[2 * e], p[2 * e + 1]}), f16x2));
-        else
-          split_bf16x2(p[2 * e], p[2 * e + 1], phi[t][e], plo[t][e]);
-      }
-    }
-  };
-
-  // Pipeline: stage s is in LDS buffer s % 2.  At the top of each trip the
-  // barrier makes stage s visible and frees buffer (s + 1) % 2 (every
-  // wavefront has finished stage s - 1), which then takes stage s + 1 from
-  // registers while stage s + 2's global loads go out.
-  auto run = [&](auto h) {
-#pragma unroll
-    for (int t = 0; t < NQ; ++t) {
-#pragma unroll
-      for (int k = 0; k < NT; ++k) o[t][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      m[t] = -1e30f;
-      lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    gload(0);
-    lwrite(0, h);
-    gload(1);
-    for (int s = 0; s < nst; ++s) {
-      __syncthreads();
-      if (s + 1 < nst) {
-        lwrite(s + 1, h);
-        gload(s + 2);
-      }
-      score(s, h);
-      pv(s, h);
-    }
-  };
-  // P.V on f16 operands: the weights lie in [0, 2^8] and round to 11
-  // significant bits (bf16 would keep 8, and needs a residual product to
-  // stay inside the tolerance).  A bf16 cache can hold V elements that f16
-  // cannot; when a stage held one, the workgroup runs again with bf16
-  // operands (the weights as high part plus residual).
-  run(PfF16<true>{});
-  if constexpr (!F8) {
-    __shared__ int s_wide[kPfWaves];
-    const bool mine = __builtin_amdgcn_ballot_w64(wide != 0) != 0;
-    if (lane == 0) s_wide[wave] = mine;
-    __syncthreads();  // also: every wavefront is done with the last stage's LDS
-    int any = 0;
-#pragma unroll
-    for (int w = 0; w < kPfWaves; ++w) any |= s_wide[w];
-    if (any) run(PfF16<false>{});
-  }
-
-#pragma unroll
-  for (int t = 0; t < NQ; ++t) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int cl = grp * 4 + r;  // output row = column of the tile
-      const int c = (NQ * wave + t) * 16 + cl;
-      const float inv = bad ? __builtin_nanf("") : a.out_scale / lacc[t][r];
-      if (c < ncol) {
-        float* dst = out_row(c) + hcol;
-#pragma unroll
-        for (int k = 0; k < NT; ++k) dst[16 * k] = o[t][k][r] * inv;
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------------ A5: decode, fp32
 // One wave per (sequence, query head, partition); lane holds channels lane
 // and lane + 64.  Plain vector-ALU form for the fp32 cache.
@@ -2436,9 +1780,6 @@ pkv_status check_slots(const int64_t* slot_mapping, int32_t num_tokens, int64_t 
   return PKV_OK;
 }
 
-pkv_status launch_status() {
-  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
-}
 
 // Blocks kept in flight per wavefront by the bf16 decode kernel (2..4);
 // PKV_DECODE_STAGES overrides the default for tuning.
@@ -2540,12 +1881,6 @@ void* g_scratch_ptr[kScratchMaxDevices] = {};
 // others), and chunks only add partial states.  PKV_CU_STATIC_PERMILLE and
 // PKV_CU_CHUNK_MIN override them for tuning and tests, PKV_DECODE_SPLIT=wave
 // selects the per-wave form.
-int env_int(const char* name, int dflt, int lo, int hi) {
-  const char* v = std::getenv(name);
-  if (!v) return dflt;
-  const int x = std::atoi(v);
-  return x < lo ? lo : (x > hi ? hi : x);
-}
 bool cu_split_enabled() {
   const char* v = std::getenv("PKV_DECODE_SPLIT");
   return !(v && std::strcmp(v, "wave") == 0);
@@ -2635,83 +1970,7 @@ void launch_decode_bf16_cu(unsigned grid, hipStream_t stream, const DecodeArgs& 
     launch_decode_bf16_cu_w<false>(grid, stream, a, head_dim, fp8);
 }
 
-template <int SB, bool F8>
-void launch_prefill_bf16_sb(unsigned grid, hipStream_t stream, const PrefillArgs& a,
-                            int head_dim) {
-  const dim3 block(64 * kPfWaves);
-  const bool win = a.window > 0;
-  if (head_dim == 64) {
-    if (win)
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, true, SB, F8>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, false, SB, F8>), grid, block, 0, stream, a);
-  } else if (win) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, true, SB, F8>), grid, block, 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, false, SB, F8>), grid, block, 0, stream, a);
-  }
-}
-
-// Blocks per pipeline stage: PKV_PF_STAGE_BLOCKS = 2 or 4 (default kPfStageBlocks)
-// for bf16 caches; FP8 caches always take 4 (a 2-block FP8 stage at head_dim
-// 64 has fewer 16-byte pieces than threads).
-void launch_prefill_bf16(unsigned grid, hipStream_t stream, const PrefillArgs& a, int head_dim,
-                         bool fp8) {
-  if (fp8)
-    launch_prefill_bf16_sb<4, true>(grid, stream, a, head_dim);
-  else if (env_int("PKV_PF_STAGE_BLOCKS", kPfStageBlocks, 2, 4) == 4)
-    launch_prefill_bf16_sb<4, false>(grid, stream, a, head_dim);
-  else
-    launch_prefill_bf16_sb<2, false>(grid, stream, a, head_dim);
-}
-
 // ============================================================================ C ABI
-namespace {
-// Chunked prefill for a bf16 cache, or an FP8 one with tensor scales.
-pkv_status prefill_impl(const void* q, const void* k_cache, const void* v_cache,
-                        const int32_t* block_tables, const int32_t* context_lens,
-                        const int32_t* query_start, int32_t num_seqs, int32_t num_q_heads,
-                        int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
-                        int32_t max_blocks_per_seq, int32_t max_context_len,
-                        int32_t max_query_len, float scale, int32_t window, bool fp8,
-                        float k_scale, float v_scale, float* out, hipStream_t stream) {
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
-      max_blocks_per_seq <= 0 || max_context_len < 0 || max_query_len < 0 || window < 0)
-    return PKV_ERR_INVALID;
-  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
-  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
-  const int group = num_q_heads / num_kv_heads;
-  if (group > 16) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
-    return PKV_ERR_INVALID;
-  PrefillArgs a;
-  a.q = q;
-  a.kc = k_cache;
-  a.vc = v_cache;
-  a.tables = block_tables;
-  a.lens = context_lens;
-  a.qstart = query_start;
-  a.out = out;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.group = group;
-  a.qtp = kPfCols / group;
-  a.num_blocks = num_blocks;
-  a.max_blocks = max_blocks_per_seq;
-  a.max_ctx = max_context_len;
-  a.scale_log2e = scale * k_scale * 1.4426950408889634f;
-  a.window = window;
-  a.out_scale = v_scale;
-  const int64_t tiles = (int64_t(max_query_len) + a.qtp - 1) / a.qtp;
-  const int64_t grid = tiles * num_seqs * num_kv_heads;
-  if (grid > 0x7FFFFFFF) return PKV_ERR_UNSUPPORTED;
-  a.tiles = static_cast<int>(tiles);
-  launch_prefill_bf16(static_cast<unsigned>(grid), stream, a, head_dim, fp8);
-  return launch_status();
-}
-}  // namespace
 
 extern "C" {
 
@@ -2850,38 +2109,6 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
   const size_t bal = balanced_workspace_bytes(balanced_waves(), group < 16 ? group : 16, head_dim,
                                               num_seqs, num_kv_heads);
   return fixed > bal ? fixed : bal;
-}
-
-pkv_status paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
-                                   const int32_t* block_tables, const int32_t* context_lens,
-                                   const int32_t* query_start, int32_t num_seqs,
-                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                   int32_t num_blocks, int32_t max_blocks_per_seq,
-                                   int32_t max_context_len, int32_t max_query_len, float scale,
-                                   int32_t window, pkv_dtype kv_dtype, float* out,
-                                   hipStream_t stream) {
-  if (kv_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-  return prefill_impl(q, k_cache, v_cache, block_tables, context_lens, query_start, num_seqs,
-                      num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
-                      max_context_len, max_query_len, scale, window, false, 1.0f, 1.0f, out,
-                      stream);
-}
-
-pkv_status paged_attention_prefill_fp8(const void* q, const void* k_cache, const void* v_cache,
-                                       const int32_t* block_tables, const int32_t* context_lens,
-                                       const int32_t* query_start, int32_t num_seqs,
-                                       int32_t num_q_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t num_blocks,
-                                       int32_t max_blocks_per_seq, int32_t max_context_len,
-                                       int32_t max_query_len, float scale, int32_t window,
-                                       float k_scale, float v_scale, float* out,
-                                       hipStream_t stream) {
-  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
-    return PKV_ERR_INVALID;
-  return prefill_impl(q, k_cache, v_cache, block_tables, context_lens, query_start, num_seqs,
-                      num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
-                      max_context_len, max_query_len, scale, window, true, k_scale, v_scale, out,
-                      stream);
 }
 
 }  // extern "C"
