@@ -177,7 +177,11 @@ pkv_status kv_block_cow(pkv_pool* pool, int32_t id, int32_t* out_id, int32_t* ne
 /* Current reference count of `id` (0 = free). */
 pkv_status kv_block_refcount(const pkv_pool* pool, int32_t id, int32_t* out_refcount);
 
-/* Pool occupancy counters. */
+/* Pool occupancy counters: free, used and shared blocks and the share of
+ * the pool in use -- the cache-usage figure a serving engine exports for
+ * autoscaling ["vLLM en Kubernetes: la pieza de inferencia LLM que si
+ * escala", «Autoscaling: HPA estandar no sirve»: the vLLM metric
+ * gpu_cache_usage_perc]. */
 pkv_status kv_pool_stats(const pkv_pool* pool, pkv_stats* out_stats);
 
 /* Snapshot of the free list, next id to be allocated first.  Writes
