@@ -1687,50 +1687,67 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ A6: LSE reduce
-// One wave per (sequence, kv head) -- kv head fastest, like the main kernel --
-// merging the partitions of each of its query heads:
+// One wave per (sequence, query head) merging its partitions:
 //   M = max_p m_p,  l = sum_p l_p 2^(m_p - M),  out = sum_p o_p 2^(m_p - M) / l
-// The wave's lanes are split evenly over the group's heads when the group
-// size divides 64 (each lane owns D*g/64 channels of one head); other group
-// sizes take the heads one after another with all 64 lanes.
+// The maximum and the normaliser are reduced over the lanes (partition p on
+// lane p % 64); the output sum walks the partitions with lane l holding
+// channels l + 64 k, so each partition's D values are read in coalesced
+// 256-byte rows and the loads of several partitions are in flight at once.
 template <int D>
 __global__ __launch_bounds__(64) void lse_reduce_kernel(DecodeArgs a) {
+  // one wavefront per (sequence, query head): lane l holds channels l + 64 k
+  constexpr int NK = D / 64;
   const int lane = threadIdx.x;
-  const int kvh = static_cast<int>(blockIdx.x % a.num_kv_heads);
-  const int b = static_cast<int>(blockIdx.x / a.num_kv_heads);
+  const int64_t head = blockIdx.x;
+  const int b = static_cast<int>(head / a.num_q_heads);
   const int L = a.lens[b];
   if (!len_ok(L, a) || L == 0) return;
   const int base = first_block_of(a, L) * kBlock;
   const int nparts = (L - base + a.part_tokens - 1) / a.part_tokens;
   if (nparts <= 1) return;
-  const int g = a.group;
-  const bool split = (64 % g) == 0;
-  const int lanes_per_head = split ? 64 / g : 64;
-  const int h_first = split ? lane / lanes_per_head : 0;
-  const int h_step = split ? g : 1;
-  const int sub = split ? lane % lanes_per_head : lane;
-  for (int h = h_first; h < g; h += h_step) {
-    const int64_t head = int64_t(b) * a.num_q_heads + int64_t(kvh) * g + h;
-    const float* mp = a.ws_m + head * a.max_parts;
-    const float* lp = a.ws_l + head * a.max_parts;
-    const float* op = a.ws_o + head * a.max_parts * D;
-    float M = -INFINITY;
-    bool bad = false;
-    for (int p = 0; p < nparts; ++p) {
-      const float mv = mp[p];
-      bad |= (mv != mv);
-      M = fmaxf(M, mv);
-    }
-    float den = 0.f;
-    for (int p = 0; p < nparts; ++p) den = fmaf(__builtin_amdgcn_exp2f(mp[p] - M), lp[p], den);
-    const float inv = bad ? __builtin_nanf("") : 1.0f / den;
-    for (int d = sub; d < D; d += lanes_per_head) {
-      float acc = 0.f;
-      for (int p = 0; p < nparts; ++p)
-        acc = fmaf(__builtin_amdgcn_exp2f(mp[p] - M), op[int64_t(p) * D + d], acc);
-      a.out[head * D + d] = acc * inv;
-    }
+  const float* mp = a.ws_m + head * a.max_parts;
+  const float* lp = a.ws_l + head * a.max_parts;
+  const float* op = a.ws_o + head * a.max_parts * D;
+  // reference max and normaliser, partitions spread over the lanes
+  float M = -INFINITY;
+  bool bad = false;
+  for (int p = lane; p < nparts; p += 64) {
+    const float mv = mp[p];
+    bad |= (mv != mv);
+    M = fmaxf(M, mv);
   }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
+  bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+  float den = 0.f;
+  for (int p = lane; p < nparts; p += 64) den = fmaf(__builtin_amdgcn_exp2f(mp[p] - M), lp[p], den);
+  den = wave_sum(den);
+  const float inv = bad ? __builtin_nanf("") : 1.0f / den;
+  // out = sum_p 2^(m_p - M) o_p / den: partition p's factor is computed by
+  // lane p % 64 and read from it; its D values are one coalesced load per k
+  float acc[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) acc[k] = 0.f;
+  for (int p0 = 0; p0 < nparts; p0 += 64) {
+    const int n = min(64, nparts - p0);
+    const float w = lane < n ? __builtin_amdgcn_exp2f(mp[p0 + lane] - M) : 0.f;
+    const float* o0 = op + int64_t(p0) * D + lane;
+    auto fold = [&](int i) {
+      const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), i));
+#pragma unroll
+      for (int k = 0; k < NK; ++k) acc[k] = fmaf(wi, o0[int64_t(i) * D + 64 * k], acc[k]);
+    };
+    int i = 0;
+    for (; i + 4 <= n; i += 4) {  // four partitions' loads in flight together
+      fold(i);
+      fold(i + 1);
+      fold(i + 2);
+      fold(i + 3);
+    }
+    for (; i < n; ++i) fold(i);
+  }
+#pragma unroll
+  for (int k = 0; k < NK; ++k) a.out[head * D + 64 * k + lane] = acc[k] * inv;
 }
 
 // ------------------------------------------------------------------ measurement
@@ -2276,7 +2293,7 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   }
   pkv_status st = launch_status();
   if (st == PKV_OK && max_parts > 1) {
-    const unsigned rgrid = static_cast<unsigned>(int64_t(num_seqs) * num_kv_heads);
+    const unsigned rgrid = static_cast<unsigned>(int64_t(num_seqs) * num_q_heads);
     if (head_dim == 128)
       hipLaunchKernelGGL(lse_reduce_kernel<128>, dim3(rgrid), dim3(64), 0, stream, a);
     else
