@@ -674,7 +674,7 @@ def main():
         log(f"[bench] calibration copy: {n} bytes read, {n} bytes written")
         del src, dst
     steps, warm = args.steps, args.warmup
-    w = synth.generate(WORKLOAD, extra_tokens=steps + warm + args.decode_only_steps + 1)
+    w = synth.generate(WORKLOAD, extra_tokens=steps + warm + max(10, steps // 2) + args.decode_only_steps + 1)
     s = w.spec
     log(f"[bench] {WORKLOAD}: B={s.num_seqs} Hq={s.num_q_heads} Hkv={s.num_kv_heads} "
         f"D={s.head_dim} pool={w.num_blocks} blocks, {int(w.lens.sum())} tokens")
@@ -722,6 +722,21 @@ def main():
     bytes_per_launch = bytes_prof / max(nlaunch, 1)   # of the timed launches
     avg_kernel_ms = kern_ms / max(nlaunch, 1)
     achieved = bytes_per_launch / (avg_kernel_ms * 1e-3) / 1e9
+
+    # the same step in one launch (paged_kv_append_decode), for context
+    fused = None
+    if args.partition == 0 and args.decode_only_steps > 0:
+        n2 = max(10, steps // 2)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(n2):
+            kv.decode_step(q, k_new, v_new, s.scale, out=out)
+        torch.cuda.synchronize()
+        fms = (time.perf_counter() - t2) * 1e3 / n2
+        fused = {"ms": round(fms, 4), "steps": n2,
+                 "kv_gb_per_s": round(kv_bytes(kv.lens, s.num_kv_heads, s.head_dim) / fms / 1e6, 1),
+                 "note": "one launch per step: the new tokens attended from their rows and written "
+                         "at the end of the launch; timed after the headline steps"}
 
     # decode alone, back to back (no appends), for context
     dec = {}
@@ -795,6 +810,7 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(s.num_seqs * steps / dt, 1),
         "decode_only": dec,
+        "fused_step": fused,
         "host_issue_ms_per_step": round((t_issued - t0) * 1e3 / steps, 4),
         "kv_waste_fraction": round(waste, 5),
         "pool_usage_percent": round(stats["usage_percent"], 2),

@@ -460,6 +460,42 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
                                   size_t workspace_bytes, pkv_dtype kv_dtype, float* out,
                                   hipStream_t stream);
 
+/* One decode step in one launch: paged_kv_append for one new token per
+ * sequence, then paged_attention_decode_window over the grown contexts
+ * ["PagedAttention por dentro", «La tabla de páginas (block table)»: each
+ * step stores the new token's K/V in its sequence's last block, taking a
+ * new block when that one is full; «El kernel CUDA»: attention then reads
+ * the context block by block through the table].  Every sequence s with
+ * context_lens_in[s] > 0 gains one token: its K and V are row s of k_new /
+ * v_new ([num_seqs][num_kv_heads][head_dim], bf16) and slot_mapping[s] is
+ * its slot (from paged_kv_append_slots; read only for those sequences).
+ * Attention over the context_lens_in[s] + 1 tokens takes the new token from
+ * its rows, so the launch never reads what it writes: the rows are stored in
+ * their slots (as paged_kv_write; a slot outside the pool is skipped), the
+ * table updates (flat index, block id) with an index inside
+ * [0, num_seqs * max_blocks_per_seq) are applied, and context_lens_out[s] =
+ * context_lens_in[s] + 1 (an empty or negative length is copied as it is);
+ * the next launch on the stream sees all of them.  context_lens_out must
+ * not be context_lens_in (a driver alternates two buffers).  The updates
+ * may only change table entries this step does not read: a new block's
+ * entry, a copy-on-write replacement of the last block whose copy
+ * (paged_kv_copy_blocks) is enqueued before this call, or a sliding-window
+ * release (pkv_window_release with the grown lengths).  max_context_len
+ * bounds the grown lengths.  bf16 cache and the per-CU balanced split (up to
+ * 16384 sequences); workspace as paged_attention_decode with partition_size
+ * 0; other dtypes or shapes -> PKV_ERR_UNSUPPORTED.  slot_mapping and
+ * updates: device or pinned host memory; other arguments and errors as
+ * paged_kv_append and paged_attention_decode_window. */
+pkv_status paged_kv_append_decode(const void* q, const void* k_new, const void* v_new,
+                                  const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                  int32_t* block_tables, const int32_t* context_lens_in,
+                                  int32_t* context_lens_out, const int32_t* updates,
+                                  int32_t num_updates, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                  int32_t window, void* workspace, size_t workspace_bytes,
+                                  pkv_dtype kv_dtype, float* out, hipStream_t stream);
+
 /* FP8 cache write: like paged_kv_write, but k_new / v_new (bf16 or fp32,
  * src_dtype) are quantised into an FP8 E4M3 cache: y = x * (1 / scale) in
  * float32 (1 / scale rounded to float32 on the host), then the nearest E4M3

@@ -79,6 +79,10 @@ _SIGS = {
                                                 C.c_int32, C.c_float, C.c_int32, C.c_int32, _vp,
                                                 C.c_size_t, C.c_int, C.c_float, C.c_float, _vp,
                                                 _vp]),
+    "paged_kv_append_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                         C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int32,
+                                         _vp, C.c_size_t, C.c_int, _vp, _vp]),
     "paged_attention_decode_noalloc": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int32, C.c_int32,
                                                  C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                                  C.c_int32, C.c_float, C.c_int32, C.c_int,
@@ -486,6 +490,32 @@ def paged_attention_decode_window(q, k_cache, v_cache, block_tables, context_len
                                               _dtype_code(k_cache), k_scale, v_scale,
                                               _dev(out, "out"), _stream(stream)),
            "paged_attention_decode_window")
+
+
+def paged_kv_append_decode(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                           lens_in, lens_out, updates, out, *, num_kv_heads: int, num_blocks: int,
+                           max_context_len: int, scale: float, window: int = 0, workspace=None,
+                           stream=None) -> None:
+    """One decode step in one launch (see pagedkv.h): k_new / v_new [B][Hkv][D]
+    bf16 rows, slot_mapping int64 [B] and updates int32 [n][2] (device or
+    pinned host tensors), lens_in / lens_out two distinct int32 [B] device
+    buffers."""
+    B, Hq, D = q.shape
+    mb = block_tables.shape[1]
+    n_upd = int(updates.shape[0]) if updates is not None and updates.numel() else 0
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.paged_kv_append_decode(_dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                       _dev_or_pinned(slot_mapping, "slot_mapping"),
+                                       _dev(k_cache, "k_cache"),
+                                       _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+                                       _dev(lens_in, "lens_in"), _dev(lens_out, "lens_out"),
+                                       _dev_or_pinned(updates, "updates") if n_upd else None,
+                                       n_upd, B, Hq,
+                                       num_kv_heads, D, num_blocks, mb, max_context_len, scale,
+                                       window, ws_ptr, ws_bytes, _dtype_code(k_cache),
+                                       _dev(out, "out"), _stream(stream)),
+           "paged_kv_append_decode")
 
 
 def paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, out, *,

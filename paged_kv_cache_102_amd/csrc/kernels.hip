@@ -222,6 +222,19 @@ struct DecodeArgs {
   int static_permille, chunk_min;
   float out_scale;  // FP8 cache: the V tensor scale (1 otherwise)
   int window;       // sliding window in tokens (0: the whole context)
+  // fused decode step (paged_kv_append_decode): each sequence with a context
+  // gains the token of row s of k_new / v_new ([B][Hkv][D]); it is attended
+  // from those rows and written to slots[s] at the end, with the table
+  // deltas upd[n_upd][2] applied to tables_w[table_elems] and the new
+  // lengths stored in lens_out (lens holds the lengths before the step)
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slots;
+  int32_t* tables_w;
+  int64_t table_elems;
+  const int32_t* upd;
+  int n_upd;
+  int32_t* lens_out;
 };
 
 // Length check shared by the kernels: a bad length poisons the sequence.
@@ -999,9 +1012,10 @@ __host__ __device__ inline int cu_lds_slots(int group, int head_dim, int num_seq
 // F8: the cache holds FP8 E4M3 codes (tiles of 16 D bytes, converted to
 // bf16 in registers; scales folded into the score scale and out_scale).
 // WIN: sliding window on (a.window > 0); off, the window code compiles out.
-template <int D, int ST, int AUX, bool F8 = false, bool WIN = false>
+template <int D, int ST, int AUX, bool F8 = false, bool WIN = false, bool STEP = false>
 __global__ __launch_bounds__(64 * kCuWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_bf16_cu_kernel(DecodeArgs a) {
+  static_assert(!(STEP && F8), "the fused step takes bf16 caches");
   constexpr int NJ = D / 32;
   constexpr int NT = D / 16;
   constexpr int NJ8 = NJ / 2;  // 16-byte loads per lane per FP8 tile (K and V each)
@@ -1038,6 +1052,11 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   const int wg = blockIdx.x;
   const int NWG = gridDim.x;
 
+  // Context length seen by this launch: in the fused step every sequence
+  // with a context holds one more token (its row of k_new / v_new).
+  auto grown = [](int L) { return (STEP && L > 0) ? L + 1 : L; };
+  int64_t step_slot = -1;
+  int32_t step_idx = -1, step_val = 0;
   // Tile counts of the B sequences and their prefix, in LDS.  Thread i takes
   // sequences [i k, i k + k); the length loads go through a buffer resource
   // sized to the B lengths (reads past them return 0, i.e. no tiles).
@@ -1047,7 +1066,8 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     const __amdgpu_buffer_rsrc_t rl = tile_rsrc(a.lens, B * 4);
     int part = 0;
     for (int j = 0; j < k; ++j)
-      part += nblocks_of<WIN>(a, __builtin_amdgcn_raw_buffer_load_b32(rl, (tid * k + j) * 4, 0, 0));
+      part += nblocks_of<WIN>(a, grown(__builtin_amdgcn_raw_buffer_load_b32(rl, (tid * k + j) * 4, 0, 0)));
+
     int incl = part;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -1068,7 +1088,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
       const int b = tid * k + j;
       if (b < B) {
         s_cum[b] = run;
-        run += nblocks_of<WIN>(a, __builtin_amdgcn_raw_buffer_load_b32(rl, b * 4, 0, 0));
+        run += nblocks_of<WIN>(a, grown(__builtin_amdgcn_raw_buffer_load_b32(rl, b * 4, 0, 0)));
       }
     }
     if (tid == 0) s_cum[B] = total;
@@ -1076,7 +1096,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   // rows of sequences with no work: zeros for an empty context, NaN for a
   // bad length, spread over all wavefronts of the grid
   for (int b = wg * NW + wave; b < B; b += NWG * NW) {
-    const int L = load_uniform(a.lens, b);
+    const int L = grown(load_uniform(a.lens, b));
     if (!len_ok(L, a) || L == 0) {
       const float fill = (L == 0) ? 0.f : __builtin_nanf("");
       for (int e = lane; e < a.num_q_heads * D; e += 64)
@@ -1122,7 +1142,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     const uint64_t le = __builtin_amdgcn_ballot_w64(v <= rem);
     b = __builtin_amdgcn_readfirstlane(lo + 63 - static_cast<int>(__builtin_clzll(le)));
     blk = __builtin_amdgcn_readfirstlane(rem - s_cum[b]);
-    L = load_uniform(a.lens, b);
+    L = grown(load_uniform(a.lens, b));
     nb = nblocks_of<WIN>(a, L);
   };
   auto advance = [&](int& kvh, int& b, int& blk, int& L, int& nb) {
@@ -1137,7 +1157,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
           break;
         }
       }
-      L = load_uniform(a.lens, b);
+      L = grown(load_uniform(a.lens, b));
       nb = nblocks_of<WIN>(a, L);
     }
   };
@@ -1164,7 +1184,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   const int qbytes = g * D * 2;
 
   uint4 kr[ST][F8 ? NJ8 : NJ], vr[ST][F8 ? NJ8 : NJ], qr[ST][NJ];
-  bool st_bad[ST], rec_live[ST], rec_first[ST], rec_last[ST];
+  bool st_bad[ST], rec_live[ST], rec_first[ST], rec_last[ST], rec_new[ST];
   int rec_kvh[ST], rec_b[ST], rec_blk[ST], rec_L[ST], rec_nb[ST], rec_idx[ST];
 
   auto issue = [&](int st) {
@@ -1178,12 +1198,18 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     rec_idx[st] = l_idx;
     rec_first[st] = l_idx == l_us;
     rec_last[st] = l_idx == l_ue - 1;
-    int phys = live ? load_uniform(a.tables, int64_t(l_b) * a.max_blocks +
-                                                 first_block_of<WIN>(a, l_L) + l_blk)
-                    : 0;
+    // fused step: the sequence's last tile holds the new token, which is
+    // taken from its k_new / v_new row; when it opens a new block, nothing
+    // of that block is in the cache yet (nor its table entry)
+    const bool newtok = STEP && live && l_blk == l_nb - 1;
+    const bool fresh = newtok && (l_L - 1) % kBlock == 0;
+    rec_new[st] = newtok;
+    int phys = (live && !fresh) ? load_uniform(a.tables, int64_t(l_b) * a.max_blocks +
+                                                            first_block_of<WIN>(a, l_L) + l_blk)
+                                : 0;
     bool bad = false;
-    int bytes = live ? TILE_BYTES : 0;
-    if (live && (phys < 0 || phys >= a.num_blocks)) {
+    int bytes = (live && !fresh) ? TILE_BYTES : 0;
+    if (live && !fresh && (phys < 0 || phys >= a.num_blocks)) {
       bad = true;
       bytes = 0;
     }
@@ -1319,6 +1345,36 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
         vx[j] = vr[st][j];
       }
     }
+    if constexpr (STEP) {
+      if (rec_new[st]) {
+        // the new token (slot tn of this tile) from its rows: K lanes l with
+        // l % 16 == tn take channels 32 j + 8 (l / 16) .. + 8; V lanes with
+        // l / 16 == tn / 4 take channels 32 j + l % 16 and 32 j + 16 + l % 16
+        // into 16-bit field tn % 4 of their low and high halves
+        const int tn = (c_L - 1) % kBlock;
+        const int64_t row = (int64_t(rec_b[st]) * Hkv + rec_kvh[st]) * D;
+        const uint16_t* kn = static_cast<const uint16_t*>(a.k_new) + row;
+        const uint16_t* vn = static_cast<const uint16_t*>(a.v_new) + row;
+        const bool kl = hcol == tn, vl = grp == (tn >> 2);
+        const int sh = (tn & 1) * 16;
+        const uint32_t keep = 0xFFFF0000u >> sh;  // the other token's half
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const uint4 kp = *reinterpret_cast<const uint4*>(kn + 32 * j + 8 * grp);
+          const uint32_t vlo = vn[32 * j + hcol], vhi = vn[32 * j + 16 + hcol];
+          if (kl) kx[j] = kp;
+          if (vl) {
+            if (tn & 2) {
+              vx[j].y = (vx[j].y & keep) | (vlo << sh);
+              vx[j].w = (vx[j].w & keep) | (vhi << sh);
+            } else {
+              vx[j].x = (vx[j].x & keep) | (vlo << sh);
+              vx[j].z = (vx[j].z & keep) | (vhi << sh);
+            }
+          }
+        }
+      }
+    }
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
@@ -1417,10 +1473,33 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
       issue(st);
     }
   }
+  if constexpr (STEP) {
+    // this workgroup's first new-token slot and table delta, possibly read
+    // over the host link: issued after the walk (a wait inside it would wait
+    // for them too), they arrive during the fold and are used after it
+    if (wg < B) step_slot = ld_sys(a.slots + wg);
+    const int i = wg + NWG * static_cast<int>(threadIdx.x);
+    if (i < a.n_upd) {
+      step_idx = ld_sys(a.upd + 2 * int64_t(i));
+      step_val = ld_sys(a.upd + 2 * int64_t(i) + 1);
+    }
+  }
   // overflow slots were written with plain stores by other wavefronts of
   // this workgroup: complete them before the barrier
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  // fused step: the first new rows this workgroup stores at the end, read
+  // now so that they arrive during the fold
+  constexpr int kStepCh = D / 8;  // 8-channel chunks per row and kv head
+  uint4 step_k = make_uint4(0, 0, 0, 0), step_v = make_uint4(0, 0, 0, 0);
+  if constexpr (STEP) {
+    const int i = threadIdx.x;
+    if (wg < B && i < Hkv * kStepCh) {
+      const int64_t src = (int64_t(wg) * Hkv + i / kStepCh) * D + (i % kStepCh) * 8;
+      step_k = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_new) + src);
+      step_v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_new) + src);
+    }
+  }
 
   // Fold the slots of each sequence.  Wavefront w leads the slots s = w
   // (mod 8) that are the first slot of their sequence; lane element k is
@@ -1604,6 +1683,45 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
       for (int u = 0; u < 8; ++u)
         if (k0 + u < nk)
           a.out[head0 * D + 64 * (k0 + u) + lane] = gbad ? __builtin_nanf("") : acc[u] / den[u] * a.out_scale;
+    }
+  }
+
+  if constexpr (STEP) {
+    // The step's cache updates, which nothing in this launch reads: every
+    // sequence s = wg, wg + NWG, ... with a context stores its new K/V row
+    // in its slot (as paged_kv_write: slots outside the pool are skipped),
+    // table deltas i = wg + NWG t are applied, and the new lengths go to
+    // lens_out.
+    const int tid = threadIdx.x;
+    constexpr int CH = kStepCh;
+    for (int sq = wg; sq < B; sq += NWG) {
+      const int L0 = load_uniform(a.lens, sq);
+      if (tid == 0) a.lens_out[sq] = grown(L0);
+      const int64_t slot = sq == wg ? step_slot : ld_sys(a.slots + sq);
+      if (!(L0 > 0) || slot < 0 || slot >= int64_t(a.num_blocks) * kBlock) continue;
+      const int64_t blk = slot >> 4;
+      const int t = static_cast<int>(slot & 15);
+      for (int i = tid; i < Hkv * CH; i += 64 * NW) {
+        const int h = i / CH, c = i % CH;
+        const int64_t src = (int64_t(sq) * Hkv + h) * D + c * 8;
+        const int64_t tile = (blk * Hkv + h) * int64_t(kBlock) * D;
+        const bool pre = sq == wg && i == tid;  // read after the main loop
+        const uint4 kw = pre ? step_k : *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_new) + src);
+        const uint4 vw = pre ? step_v : *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_new) + src);
+        uint16_t* kc = static_cast<uint16_t*>(const_cast<void*>(a.kc)) + tile;
+        uint16_t* vc = static_cast<uint16_t*>(const_cast<void*>(a.vc)) + tile;
+        const uint16_t ve[8] = {uint16_t(vw.x), uint16_t(vw.x >> 16), uint16_t(vw.y), uint16_t(vw.y >> 16),
+                                uint16_t(vw.z), uint16_t(vw.z >> 16), uint16_t(vw.w), uint16_t(vw.w >> 16)};
+        // K: the 8 channels of a group are 16 contiguous bytes for a token
+        *reinterpret_cast<uint4*>(kc + k_elem(t, c * 8)) = kw;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vc[v_elem(t, c * 8 + e)] = ve[e];
+      }
+    }
+    for (int i = wg + NWG * tid, r = 0; i < a.n_upd; i += NWG * 64 * NW, ++r) {
+      const int32_t idx = r == 0 ? step_idx : ld_sys(a.upd + 2 * int64_t(i));
+      const int32_t val = r == 0 ? step_val : ld_sys(a.upd + 2 * int64_t(i) + 1);
+      if (idx >= 0 && idx < a.table_elems) a.tables_w[idx] = val;
     }
   }
 }
@@ -1979,6 +2097,16 @@ void launch_decode_bf16_cu_w(unsigned grid, hipStream_t stream, const DecodeArgs
   }
 }
 
+// The fused decode step (bf16 cache): per-CU kernel with STEP = true.
+template <bool WIN>
+void launch_decode_step_w(unsigned grid, hipStream_t stream, const DecodeArgs& a, int head_dim) {
+  const dim3 block(64 * kCuWaves);
+  if (head_dim == 64)
+    hipLaunchKernelGGL((decode_bf16_cu_kernel<64, 3, 2, false, WIN, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_bf16_cu_kernel<128, 2, 2, false, WIN, true>), grid, block, 0, stream, a);
+}
+
 void launch_decode_bf16_cu(unsigned grid, hipStream_t stream, const DecodeArgs& a, int head_dim,
                            bool fp8) {
   if (a.window > 0)
@@ -2155,7 +2283,8 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                        int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                        float scale, int32_t window, int32_t partition_size, void* workspace,
                        size_t workspace_bytes, pkv_dtype kv_dtype, float k_scale, float v_scale,
-                       float* out, hipStream_t stream, bool fixed_scratch = false) {
+                       float* out, hipStream_t stream, bool fixed_scratch = false,
+                       const DecodeArgs* step = nullptr) {
   const bool fp8 = kv_dtype == PKV_FP8_E4M3;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || partition_size < 0 ||
@@ -2169,6 +2298,7 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
               !std::isfinite(v_scale)))
     return PKV_ERR_INVALID;
   if (fp8 && partition_size != 0) return PKV_ERR_UNSUPPORTED;
+  if (step && (kv_dtype != PKV_BF16 || partition_size != 0)) return PKV_ERR_UNSUPPORTED;
   if (fixed_scratch && (kv_dtype == PKV_F32 || partition_size != 0)) return PKV_ERR_UNSUPPORTED;
   const int group = num_q_heads / num_kv_heads;
   if ((kv_dtype == PKV_BF16 || fp8) && group > 16) return PKV_ERR_UNSUPPORTED;
@@ -2188,7 +2318,7 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                         int64_t(num_seqs) * max_blocks_per_seq * num_kv_heads <
                             (int64_t(1) << 31) &&
                         cus > 0;
-  DecodeArgs a;
+  DecodeArgs a{};
   a.q = q;
   a.kc = k_cache;
   a.vc = v_cache;
@@ -2266,12 +2396,27 @@ pkv_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   }
   a.epoch = balanced ? next_epoch() : 0;
   if (fp8 && !cu_form) return PKV_ERR_UNSUPPORTED;
+  if (step) {
+    if (!cu_form) return PKV_ERR_UNSUPPORTED;
+    a.k_new = step->k_new;
+    a.v_new = step->v_new;
+    a.slots = step->slots;
+    a.tables_w = step->tables_w;
+    a.table_elems = step->table_elems;
+    a.upd = step->upd;
+    a.n_upd = step->n_upd;
+    a.lens_out = step->lens_out;
+  }
 
   const bool prof = g_prof.on && g_prof.calls++ % g_prof.every == 0 &&
                     g_prof.used + 2 <= g_prof.pool.size();
   if (prof) (void)hipEventRecord(g_prof.pool[g_prof.used], stream);
   if (balanced) {
-    if (cu_form)
+    if (step && a.window > 0)
+      launch_decode_step_w<true>(static_cast<unsigned>(cus), stream, a, head_dim);
+    else if (step)
+      launch_decode_step_w<false>(static_cast<unsigned>(cus), stream, a, head_dim);
+    else if (cu_form)
       launch_decode_bf16_cu(static_cast<unsigned>(cus), stream, a, head_dim, fp8);
     else
       launch_decode_bf16_balanced(static_cast<unsigned>(waves), stream, a, head_dim);
@@ -2340,6 +2485,35 @@ pkv_status paged_attention_decode_window(const void* q, const void* k_cache, con
                      num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len,
                      scale, window, partition_size, workspace, workspace_bytes, kv_dtype, k_scale,
                      v_scale, out, stream);
+}
+
+pkv_status paged_kv_append_decode(const void* q, const void* k_new, const void* v_new,
+                                  const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                  int32_t* block_tables, const int32_t* context_lens_in,
+                                  int32_t* context_lens_out, const int32_t* updates,
+                                  int32_t num_updates, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                  int32_t window, void* workspace, size_t workspace_bytes,
+                                  pkv_dtype kv_dtype, float* out, hipStream_t stream) {
+  if (num_updates < 0 || num_seqs < 0) return PKV_ERR_INVALID;
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping || !context_lens_out ||
+                       context_lens_out == context_lens_in))
+    return PKV_ERR_INVALID;
+  if (num_updates > 0 && !updates) return PKV_ERR_INVALID;
+  DecodeArgs st{};
+  st.k_new = k_new;
+  st.v_new = v_new;
+  st.slots = slot_mapping;
+  st.tables_w = block_tables;
+  st.table_elems = int64_t(num_seqs) * max_blocks_per_seq;
+  st.upd = updates;
+  st.n_upd = num_updates;
+  st.lens_out = context_lens_out;
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens_in, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, max_context_len,
+                     scale, window, 0, workspace, workspace_bytes, kv_dtype, 1.0f, 1.0f, out,
+                     stream, false, &st);
 }
 
 pkv_status paged_attention_decode_noalloc(const void* q, const void* k_cache,

@@ -5,12 +5,18 @@ lengths (with their host mirrors), the host pool and a decode workspace, and
 sequences the C-ABI calls of one decode step:
 
   1. plan the appended tokens' slots on the host (paged_kv_append_slots);
-  2. upload slots, table deltas, copy-on-write pairs and lengths (one
-     host-to-device copy from pinned staging memory);
-  3. apply the table deltas (paged_block_table_update);
-  4. copy shared blocks that are about to be written (paged_kv_copy_blocks);
-  5. write the new K/V (paged_kv_write);
-  6. attend (paged_attention_decode).
+  2. stage slots, table and length deltas and copy-on-write pairs in pinned
+     host memory, which the kernels read in place;
+  3. copy shared blocks that are about to be written (paged_kv_copy_blocks,
+     only when there are such blocks);
+  4. write the new K/V and apply the deltas (paged_kv_append, one launch;
+     an FP8 cache: paged_block_table_update, then paged_kv_write_fp8);
+  5. attend (paged_attention_decode).
+
+decode_step does 4 and 5 in one launch (paged_kv_append_decode): the new
+tokens are attended from their rows and stored at the end of the launch;
+the device lengths alternate between two buffers, one read and one written
+per step.
 
 With a sliding window, blocks wholly before every upcoming query's window
 are released before step 1 (pkv_window_release), so the same step can reuse
@@ -129,13 +135,15 @@ class PagedKV:
         self.tables = np.full((num_seqs, max_blocks_per_seq), -1, dtype=np.int32)
         self.lens = np.zeros(num_seqs, dtype=np.int32)
         # device tables and lengths share one int32 buffer, so that a step's
-        # length changes travel as table deltas at flat index S*mb + s
+        # length changes travel as table deltas at flat index S*mb + s; the
+        # lengths have two copies, the current one and the one a fused step
+        # (decode_step) writes
         nt = num_seqs * max_blocks_per_seq
-        if nt + num_seqs >= 2 ** 31:
-            raise ValueError("num_seqs * (max_blocks_per_seq + 1) must be < 2^31")
-        self.state_d = torch.empty(nt + num_seqs, dtype=torch.int32, device=self.device)
+        if nt + 2 * num_seqs >= 2 ** 31:
+            raise ValueError("num_seqs * (max_blocks_per_seq + 2) must be < 2^31")
+        self.state_d = torch.empty(nt + 2 * num_seqs, dtype=torch.int32, device=self.device)
         self.tables_d = self.state_d[:nt].view(num_seqs, max_blocks_per_seq)
-        self.lens_d = self.state_d[nt:]
+        self._cur = 0
         self.tables_d.copy_(torch.from_numpy(self.tables))
         self.lens_d.copy_(torch.from_numpy(self.lens))
         ws = capi.paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
@@ -145,6 +153,12 @@ class PagedKV:
         self.window = window
         self.host_pool = None
         self.swapped = {}   # sequence -> (host table row, length)
+
+    @property
+    def lens_d(self):
+        """The device context lengths currently in use (int32 [num_seqs])."""
+        nt = self.tables.size
+        return self.state_d[nt + self._cur * self.num_seqs:nt + (self._cur + 1) * self.num_seqs]
 
     # ------------------------------------------------------------------ host helpers
     def _stage(self, arrays):
@@ -184,7 +198,7 @@ class PagedKV:
         # new lengths of the sequences that grew, as deltas into the state buffer
         grown = np.flatnonzero(nn)
         lupd = np.empty((len(grown), 2), dtype=np.int32)
-        lupd[:, 0] = self.tables.size + grown
+        lupd[:, 0] = self.tables.size + self._cur * self.num_seqs + grown
         lupd[:, 1] = self.lens[grown]
         h_slots, h_upd, h_cows = self._stage([slots, np.concatenate([upd, lupd]), cows])
         s = stream.cuda_stream
@@ -203,6 +217,51 @@ class PagedKV:
         finally:
             self._staging.release(stream)
         return slots, upd, cows
+
+    def decode_step(self, q, k_new, v_new, scale: float, out=None, stream=None):
+        """One decode step in one launch (paged_kv_append_decode): every
+        sequence with a context gains one token (row s of k_new / v_new,
+        device [num_seqs][Hkv][D], bf16) and attends over its grown context.
+        The host plans the slots and any copy-on-write first, as in append."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        live = self.lens > 0
+        nn = live.astype(np.int32)
+        rel = None
+        if self.window > 0:
+            rel = capi.pkv_window_release(self.pool, self.tables, self.lens + nn, self.window)
+        slots, upd, cows = capi.paged_kv_append_slots(self.pool, self.tables, self.lens, nn)
+        if rel is not None and len(rel):
+            upd = np.concatenate([rel, upd]) if len(upd) else rel
+        slot_seq = np.full(self.num_seqs, -1, dtype=np.int64)
+        slot_seq[live] = slots
+        h_slots, h_upd, h_cows = self._stage([slot_seq, np.ascontiguousarray(upd, np.int32),
+                                              np.ascontiguousarray(cows, np.int32)])
+        s = stream.cuda_stream
+        max_ctx = int(self.lens.max()) if self.lens.size else 0
+        ws = self.workspace
+        need = capi.paged_attention_workspace_size(self.num_seqs, self.num_q_heads,
+                                                   self.num_kv_heads, self.head_dim, max_ctx, 0)
+        if need > ws.numel() * 4:
+            ws = self.workspace = torch.empty(need // 4, dtype=torch.float32, device=self.device)
+        lens_in = self.lens_d
+        self._cur ^= 1
+        lens_out = self.lens_d
+        try:
+            capi.paged_kv_copy_blocks(self.k_cache, self.v_cache, h_cows, self.num_kv_heads,
+                                      self.head_dim, self.num_blocks, s)
+            capi.paged_kv_append_decode(q, k_new, v_new, h_slots, self.k_cache, self.v_cache,
+                                        self.tables_d, lens_in, lens_out, h_upd, out,
+                                        num_kv_heads=self.num_kv_heads, num_blocks=self.num_blocks,
+                                        max_context_len=max_ctx, scale=scale, window=self.window,
+                                        workspace=ws, stream=s)
+        except Exception:
+            self._cur ^= 1
+            raise
+        finally:
+            self._staging.release(stream)
+        return out
 
     def decode(self, q, scale: float, out=None, stream=None, partition_size=None):
         stream = stream or torch.cuda.current_stream(self.device)
