@@ -84,18 +84,20 @@ __global__ void kv_write_kernel(const T* __restrict__ k_new, const T* __restrict
   const int64_t ih = idx / chunks;
   const int h = static_cast<int>(ih % num_kv_heads);
   const int64_t i = ih / num_kv_heads;
-  const int64_t slot = ld_sys(slots + i);
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot >> 4;
-  const int t = static_cast<int>(slot & 15);
+  // the row chunk first: its loads and the slot's read (possibly over the
+  // host link) are then in flight together
   const int64_t src = (i * num_kv_heads + h) * head_dim + c * 8;
-  const int64_t tile = (blk * num_kv_heads + h) * int64_t(kBlock) * head_dim;
   T kv[8], vv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     kv[e] = k_new[src + e];
     vv[e] = v_new[src + e];
   }
+  const int64_t slot = ld_sys(slots + i);
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot >> 4;
+  const int t = static_cast<int>(slot & 15);
+  const int64_t tile = (blk * num_kv_heads + h) * int64_t(kBlock) * head_dim;
   // K: the 8 channels of a group are contiguous for a token
 #pragma unroll
   for (int e = 0; e < 8; ++e) kc[tile + k_elem(t, c * 8 + e)] = kv[e];
@@ -127,18 +129,20 @@ __global__ void append_kernel(const T* __restrict__ k_new, const T* __restrict__
   const int64_t ih = idx / chunks;
   const int h = static_cast<int>(ih % num_kv_heads);
   const int64_t i = ih / num_kv_heads;
-  const int64_t slot = ld_sys(slots + i);
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot >> 4;
-  const int t = static_cast<int>(slot & 15);
+  // the row chunk first: its loads and the slot's read (possibly over the
+  // host link) are then in flight together
   const int64_t src = (i * num_kv_heads + h) * head_dim + c * 8;
-  const int64_t tile = (blk * num_kv_heads + h) * int64_t(kBlock) * head_dim;
   T kv[8], vv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     kv[e] = k_new[src + e];
     vv[e] = v_new[src + e];
   }
+  const int64_t slot = ld_sys(slots + i);
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot >> 4;
+  const int t = static_cast<int>(slot & 15);
+  const int64_t tile = (blk * num_kv_heads + h) * int64_t(kBlock) * head_dim;
   // Streaming stores: the rows are read again only by the next launch, and
   // lines left dirty in the L2 of each XCD slow that launch's start.
 #pragma unroll
