@@ -46,10 +46,15 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources the decode kernels are built from."""
+    """Hash of the code the decode kernels are built from: their sources with
+    comments removed and whitespace runs collapsed (a change of wording in a
+    comment leaves the kernels, and their counters, as they were)."""
     h = hashlib.sha256()
     for name in ("kernels.hip", "device_common.h"):
-        h.update(open(os.path.join(ROOT, "paged_kv_cache_102_amd", "csrc", name), "rb").read())
+        text = open(os.path.join(ROOT, "paged_kv_cache_102_amd", "csrc", name)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -470,12 +470,13 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
  * v_new ([num_seqs][num_kv_heads][head_dim], bf16) and slot_mapping[s] is
  * its slot (from paged_kv_append_slots; read only for those sequences).
  * Attention over the context_lens_in[s] + 1 tokens takes the new token from
- * its rows, so the launch never reads what it writes: the rows are stored in
- * their slots (as paged_kv_write; a slot outside the pool is skipped), the
- * table updates (flat index, block id) with an index inside
- * [0, num_seqs * max_blocks_per_seq) are applied, and context_lens_out[s] =
- * context_lens_in[s] + 1 (an empty or negative length is copied as it is);
- * the next launch on the stream sees all of them.  context_lens_out must
+ * its rows: a tile that holds the new token's slot is used with those bytes
+ * replaced, so nothing the launch computes depends on when its own stores
+ * land.  The rows are stored in their slots (as paged_kv_write; a slot
+ * outside the pool is skipped), the table updates (flat index, block id)
+ * with an index inside [0, num_seqs * max_blocks_per_seq) are applied, and
+ * context_lens_out[s] = context_lens_in[s] + 1 (an empty or negative length
+ * is copied as it is); the next launch on the stream sees all of them.  context_lens_out must
  * not be context_lens_in (a driver alternates two buffers).  The updates
  * may only change table entries this step does not read: a new block's
  * entry, a copy-on-write replacement of the last block whose copy

@@ -1691,11 +1691,15 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   }
 
   if constexpr (STEP) {
-    // The step's cache updates, which nothing in this launch reads: every
-    // sequence s = wg, wg + NWG, ... with a context stores its new K/V row
-    // in its slot (as paged_kv_write: slots outside the pool are skipped),
-    // table deltas i = wg + NWG t are applied, and the new lengths go to
-    // lens_out.
+    // The step's cache updates, on which nothing in this launch depends
+    // (other workgroups may still be walking: a tile read after a row landed
+    // has that token's bytes replaced from the rows all the same, the walk
+    // skips the table entry of a block the new token opens, a copy-on-write
+    // entry changes to a copy of the same bytes, and a released block lies
+    // outside the window): every sequence s = wg, wg + NWG, ... with a
+    // context stores its new K/V row in its slot (as paged_kv_write: slots
+    // outside the pool are skipped), table deltas i = wg + NWG t are
+    // applied, and the new lengths go to lens_out.
     const int tid = threadIdx.x;
     constexpr int CH = kStepCh;
     for (int sq = wg; sq < B; sq += NWG) {
