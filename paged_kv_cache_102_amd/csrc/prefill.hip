@@ -224,40 +224,31 @@ void prefill_bf16_kernel(PrefillArgs a) {
 
   // Stage loader: thread tid moves pieces 512 u + tid (u < PT) of the stage's
   // tiles (block 0 K, block 0 V, block 1 K, ...); a wavefront's 64 pieces lie
-  // in one tile, so the tile (and its block id, read once per stage through
-  // the scalar cache) is wave-uniform.  V slots outside [t_lo, L) are zeroed
+  // in one tile, so the tile and its block id are wave-uniform: each run
+  // reads its own block id through the scalar cache (a run needs one entry;
+  // reading the stage's entries and selecting among them cost 3-6 % of the
+  // kernel in scalar work).  V slots outside [t_lo, L) are zeroed
   // when the pieces go into LDS, a trip after their loads (they may hold
   // anything; masking them at load time would wait for the loads at once).
   // An FP8 run expands to two bf16 runs as it goes into LDS.
   uint4 st[PT_G];
   auto gload = [&](int s) {
-    int ph[SB], by[SB];
-#pragma unroll
-    for (int k = 0; k < SB; ++k) {
-      const int rel = SB * s + k;
-      ph[k] = 0;
-      by[k] = 0;
-      if (rel < nblk) {
-        ph[k] = load_uniform(row, rel);
-        if (ph[k] < 0 || ph[k] >= a.num_blocks)
-          bad = true;
-        else
-          by[k] = TILE_G;
-      }
-    }
 #pragma unroll
     for (int u = 0; u < PT_G; ++u) {
       // the wavefront's 64 pieces: a 1 KiB run at a uniform offset of its tile
       const int first = 64 * kPfWaves * u + 64 * wave;
       const int tile = first / TILE_PIECES_G;
       const int off0 = (first % TILE_PIECES_G) * 16;
-      int phys = 0, bytes = 0;  // selected, not indexed: ph and by stay in registers
-#pragma unroll
-      for (int k = 0; k < SB; ++k)
-        if ((tile >> 1) == k) {
-          phys = ph[k];
-          bytes = by[k];
-        }
+      // this run's block id, read for this run alone (wave-uniform)
+      const int rel = SB * s + (tile >> 1);
+      int phys = 0, bytes = 0;
+      if (rel < nblk) {
+        phys = load_uniform(row, rel);
+        if (phys < 0 || phys >= a.num_blocks)
+          bad = true;
+        else
+          bytes = TILE_G;
+      }
       const char* base = ((tile & 1) ? vc : kc) + (bytes ? int64_t(phys) * block_bytes : 0) + off0;
       const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, bytes ? bytes - off0 : 0);
       st[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, 0));
