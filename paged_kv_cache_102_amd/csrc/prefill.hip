@@ -239,17 +239,16 @@ void prefill_bf16_kernel(PrefillArgs a) {
       const int first = 64 * kPfWaves * u + 64 * wave;
       const int tile = first / TILE_PIECES_G;
       const int off0 = (first % TILE_PIECES_G) * 16;
-      // this run's block id, read for this run alone (wave-uniform)
+      // this run's block id, read for this run alone (wave-uniform); past the
+      // last block the read is of the last entry and the run loads nothing
       const int rel = SB * s + (tile >> 1);
-      int phys = 0, bytes = 0;
-      if (rel < nblk) {
-        phys = load_uniform(row, rel);
-        if (phys < 0 || phys >= a.num_blocks)
-          bad = true;
-        else
-          bytes = TILE_G;
-      }
-      const char* base = ((tile & 1) ? vc : kc) + (bytes ? int64_t(phys) * block_bytes : 0) + off0;
+      const bool live = rel < nblk;
+      const int phys = load_uniform(row, live ? rel : nblk - 1);
+      const bool ok = static_cast<unsigned>(phys) < static_cast<unsigned>(a.num_blocks);
+      bad |= live && !ok;
+      const int bytes = (live && ok) ? TILE_G : 0;
+      const char* base = ((tile & 1) ? vc : kc) +
+                         (bytes ? int64_t(static_cast<uint32_t>(phys)) * block_bytes : 0) + off0;
       const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, bytes ? bytes - off0 : 0);
       st[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, 0));
     }
