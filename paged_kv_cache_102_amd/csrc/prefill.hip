@@ -256,8 +256,11 @@ void prefill_bf16_kernel(PrefillArgs a) {
   // V slots of stage s outside [t_lo, L): lane l of a 1 KiB V run holds
   // tokens 4 (l / 16) .. + 3 of its block
   auto vmask = [&](int s, int tile, uint4& x) {
-    if (tile & 1) {
-      const int t0 = (i0 + SB * s + (tile >> 1)) * kBlock + 4 * grp;
+    // only a block that holds positions before t_lo or from L on (tested
+    // once per block, wave-uniform) needs the per-lane test
+    const int b0 = (i0 + SB * s + (tile >> 1)) * kBlock;
+    if ((tile & 1) && (b0 < t_lo || b0 + kBlock > L)) {
+      const int t0 = b0 + 4 * grp;
       if (t0 < t_lo || t0 + 4 > L) {
         auto in = [&](int t) { return t < L && t >= t_lo; };
         const uint32_t m01 = (in(t0) ? 0x0000FFFFu : 0u) | (in(t0 + 1) ? 0xFFFF0000u : 0u);
