@@ -1208,16 +1208,17 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
     const bool newtok = STEP && live && l_blk == l_nb - 1;
     const bool fresh = newtok && (l_L - 1) % kBlock == 0;
     rec_new[st] = newtok;
-    int phys = (live && !fresh) ? load_uniform(a.tables, int64_t(l_b) * a.max_blocks +
-                                                            first_block_of<WIN>(a, l_L) + l_blk)
-                                : 0;
-    bool bad = false;
-    int bytes = (live && !fresh) ? TILE_BYTES : 0;
-    if (live && !fresh && (phys < 0 || phys >= a.num_blocks)) {
-      bad = true;
-      bytes = 0;
-    }
-    const int64_t off = (bytes ? int64_t(phys) * block_bytes : 0) + int64_t(l_kvh) * TILE_BYTES;
+    // without branches: a stage with no tile reads entry 0 of the tables
+    // (always there) and loads nothing
+    const bool want = live && !fresh;
+    const int phys = load_uniform(a.tables, want ? int64_t(l_b) * a.max_blocks +
+                                                       first_block_of<WIN>(a, l_L) + l_blk
+                                                 : int64_t(0));
+    const bool ok = static_cast<unsigned>(phys) < static_cast<unsigned>(a.num_blocks);
+    const bool bad = want && !ok;
+    const int bytes = (want && ok) ? TILE_BYTES : 0;
+    const int64_t off = (bytes ? int64_t(static_cast<uint32_t>(phys)) * block_bytes : 0) +
+                        int64_t(l_kvh) * TILE_BYTES;
     const char* kc = static_cast<const char*>(a.kc) + off;
     const char* vc = static_cast<const char*>(a.vc) + off;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc, bytes);
