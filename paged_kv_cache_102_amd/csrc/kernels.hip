@@ -1480,8 +1480,9 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   }
   if constexpr (STEP) {
     // this workgroup's first new-token slot and table delta, possibly read
-    // over the host link: issued after the walk (a wait inside it would wait
-    // for them too), they arrive during the fold and are used after it
+    // over the host link: issued after the walk (inside it, every load wait
+    // of the walk would wait for them too) and before the wait below, which
+    // then covers them together with the walk's last loads
     if (wg < B) step_slot = ld_sys(a.slots + wg);
     const int i = wg + NWG * static_cast<int>(threadIdx.x);
     if (i < a.n_upd) {
@@ -1494,7 +1495,7 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // fused step: the first new rows this workgroup stores at the end, read
-  // now so that they arrive during the fold
+  // now so that their latency overlaps the fold
   constexpr int kStepCh = D / 8;  // 8-channel chunks per row and kv head
   uint4 step_k = make_uint4(0, 0, 0, 0), step_v = make_uint4(0, 0, 0, 0);
   if constexpr (STEP) {
