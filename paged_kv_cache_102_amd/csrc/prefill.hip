@@ -272,6 +272,19 @@ void prefill_bf16_kernel(PrefillArgs a) {
       }
     }
   };
+  // FP8 cache: V tiles are stored in LDS as P.V reads them.  For the blocks
+  // 2p and 2p + 1 of a stage, the tile slot of block 2p holds, at each
+  // 16-byte chunk, the chunk's low 8 bytes of block 2p then those of block
+  // 2p + 1, and the slot of block 2p + 1 the high 8 bytes of both, so each
+  // chunk is one operand of the pair's product, read as it lies (-4 % on the
+  // FP8 form).  A bf16 cache keeps each block's tile whole (8-byte stores
+  // made its form 1.5 % slower) and P.V assembles the operands.
+  constexpr bool VPAIR = F8;
+  auto vstore = [&](unsigned char* sb, int blk, int o, uint4 x) {
+    const int lo = (4 * (blk >> 1) + 1) * TILE_BYTES + o + 8 * (blk & 1);
+    *reinterpret_cast<uint2*>(sb + lo) = make_uint2(x.x, x.y);
+    *reinterpret_cast<uint2*>(sb + lo + 2 * TILE_BYTES) = make_uint2(x.z, x.w);
+  };
   // V goes into LDS as f16 when P.V runs on f16 operands (H); a bf16 V
   // element with no f16 equal is noted in `wide` (the workgroup then runs
   // again with bf16 operands)
@@ -297,9 +310,14 @@ void prefill_bf16_kernel(PrefillArgs a) {
         }
         vmask(s, tile, x);
         vmask(s, tile, y);
-        unsigned char* d = sb + tile * TILE_BYTES + 2048 * ((first % TILE_PIECES_G) / 64) + lane * 16;
-        *reinterpret_cast<uint4*>(d) = x;
-        *reinterpret_cast<uint4*>(d + 1024) = y;
+        const int o = 2048 * ((first % TILE_PIECES_G) / 64) + lane * 16;
+        if (tile & 1) {
+          vstore(sb, tile >> 1, o, x);
+          vstore(sb, tile >> 1, o + 1024, y);
+        } else {
+          *reinterpret_cast<uint4*>(sb + tile * TILE_BYTES + o) = x;
+          *reinterpret_cast<uint4*>(sb + tile * TILE_BYTES + o + 1024) = y;
+        }
       } else {
         uint4 x = st[u];
         vmask(s, tile, x);  // first: slots outside the context may hold anything
@@ -359,11 +377,11 @@ void prefill_bf16_kernel(PrefillArgs a) {
     for (int pp = 0; pp < SB / 2; ++pp) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const uint4 v0 = *reinterpret_cast<const uint4*>(sb + (4 * pp + 1) * TILE_BYTES + 1024 * j + lane * 16);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(sb + (4 * pp + 3) * TILE_BYTES + 1024 * j + lane * 16);
+        const uint4 vl = *reinterpret_cast<const uint4*>(sb + (4 * pp + 1) * TILE_BYTES + 1024 * j + lane * 16);
+        const uint4 vh = *reinterpret_cast<const uint4*>(sb + (4 * pp + 3) * TILE_BYTES + 1024 * j + lane * 16);
         if constexpr (H) {
-          const f16x8 vlo = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-          const f16x8 vhi = __builtin_bit_cast(f16x8, make_uint4(v0.z, v0.w, v1.z, v1.w));
+          const f16x8 vlo = __builtin_bit_cast(f16x8, VPAIR ? vl : make_uint4(vl.x, vl.y, vh.x, vh.y));
+          const f16x8 vhi = __builtin_bit_cast(f16x8, VPAIR ? vh : make_uint4(vl.z, vl.w, vh.z, vh.w));
 #pragma unroll
           for (int t = 0; t < NQ; ++t) {
             const f16x8 ph = __builtin_bit_cast(f16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
@@ -373,8 +391,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
           }
           continue;
         }
-        const bf16x8 vlo = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-        const bf16x8 vhi = __builtin_bit_cast(bf16x8, make_uint4(v0.z, v0.w, v1.z, v1.w));
+        const bf16x8 vlo = __builtin_bit_cast(bf16x8, VPAIR ? vl : make_uint4(vl.x, vl.y, vh.x, vh.y));
+        const bf16x8 vhi = __builtin_bit_cast(bf16x8, VPAIR ? vh : make_uint4(vl.z, vl.w, vh.z, vh.w));
 #pragma unroll
         for (int t = 0; t < NQ; ++t) {
           const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
