@@ -232,13 +232,33 @@ void prefill_bf16_kernel(PrefillArgs a) {
   // anything; masking them at load time would wait for the loads at once).
   // An FP8 run expands to two bf16 runs as it goes into LDS.
   uint4 st[PT_G];
+  // bf16 cache, PT_G even: runs 2i and 2i + 1 of a wavefront are the same
+  // 1 KiB piece of K or V of the two blocks of a pair (pair-run i * 8 + w:
+  // K pairs first, then V), so a lane holds both halves of each P.V operand
+  constexpr bool PAIRED = !F8 && PT_G % 2 == 0;
+  constexpr int RPT = TILE_PIECES_G / 64;  // runs per tile
+  constexpr int HALF_PAIRS = SB / 2 * RPT;  // pair-runs of K (or of V) per stage
+  auto run_tile = [&](int u) {
+    if constexpr (PAIRED) {
+      const int k = (u >> 1) * kPfWaves + wave;
+      const int rem = k % HALF_PAIRS;
+      return 2 * (2 * (rem / RPT) + (u & 1)) + k / HALF_PAIRS;
+    } else {
+      return (64 * kPfWaves * u + 64 * wave) / TILE_PIECES_G;
+    }
+  };
+  auto run_off = [&](int u) {  // byte offset of the run in its tile (global memory)
+    if constexpr (PAIRED)
+      return (((u >> 1) * kPfWaves + wave) % HALF_PAIRS % RPT) * 1024;
+    else
+      return ((64 * kPfWaves * u + 64 * wave) % TILE_PIECES_G) * 16;
+  };
   auto gload = [&](int s) {
 #pragma unroll
     for (int u = 0; u < PT_G; ++u) {
       // the wavefront's 64 pieces: a 1 KiB run at a uniform offset of its tile
-      const int first = 64 * kPfWaves * u + 64 * wave;
-      const int tile = first / TILE_PIECES_G;
-      const int off0 = (first % TILE_PIECES_G) * 16;
+      const int tile = run_tile(u);
+      const int off0 = run_off(u);
       // this run's block id, read for this run alone (wave-uniform); past the
       // last block the read is of the last entry and the run loads nothing
       const int rel = SB * s + (tile >> 1);
@@ -272,14 +292,15 @@ void prefill_bf16_kernel(PrefillArgs a) {
       }
     }
   };
-  // FP8 cache: V tiles are stored in LDS as P.V reads them.  For the blocks
-  // 2p and 2p + 1 of a stage, the tile slot of block 2p holds, at each
-  // 16-byte chunk, the chunk's low 8 bytes of block 2p then those of block
-  // 2p + 1, and the slot of block 2p + 1 the high 8 bytes of both, so each
-  // chunk is one operand of the pair's product, read as it lies (-4 % on the
-  // FP8 form).  A bf16 cache keeps each block's tile whole (8-byte stores
-  // made its form 1.5 % slower) and P.V assembles the operands.
-  constexpr bool VPAIR = F8;
+  // V tiles are stored in LDS as P.V reads them.  For the blocks 2p and
+  // 2p + 1 of a stage, the tile slot of block 2p holds, at each 16-byte
+  // chunk, the chunk's low 8 bytes of block 2p then those of block 2p + 1,
+  // and the slot of block 2p + 1 the high 8 bytes of both, so each chunk is
+  // one operand of the pair's product, read as it lies (no register moves
+  // in P.V: -4 % on the FP8 form, -1.7 % on the bf16 one).  A bf16 lane holds
+  // the same piece of both blocks (paired runs above) and writes the two
+  // chunks whole; an FP8 run holds one block, written as 8-byte halves.
+  constexpr bool VPAIR = F8 || PAIRED;
   auto vstore = [&](unsigned char* sb, int blk, int o, uint4 x) {
     const int lo = (4 * (blk >> 1) + 1) * TILE_BYTES + o + 8 * (blk & 1);
     *reinterpret_cast<uint2*>(sb + lo) = make_uint2(x.x, x.y);
@@ -292,6 +313,35 @@ void prefill_bf16_kernel(PrefillArgs a) {
   auto lwrite = [&](int s, auto h) {
     constexpr bool H = decltype(h)::value;
     unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
+    if constexpr (PAIRED) {
+#pragma unroll
+      for (int i = 0; i < PT_G / 2; ++i) {
+        const int t0 = run_tile(2 * i), t1 = run_tile(2 * i + 1);
+        uint4 x0 = st[2 * i], x1 = st[2 * i + 1];
+        vmask(s, t0, x0);
+        vmask(s, t1, x1);
+        const int o = run_off(2 * i) + lane * 16;
+        if (t0 & 1) {
+          if constexpr (H) {
+            wide |= bf16x2_beyond_f16(x0.x) | bf16x2_beyond_f16(x0.y) | bf16x2_beyond_f16(x0.z) |
+                    bf16x2_beyond_f16(x0.w) | bf16x2_beyond_f16(x1.x) | bf16x2_beyond_f16(x1.y) |
+                    bf16x2_beyond_f16(x1.z) | bf16x2_beyond_f16(x1.w);
+            x0 = make_uint4(bf16x2_to_f16x2(x0.x), bf16x2_to_f16x2(x0.y), bf16x2_to_f16x2(x0.z),
+                            bf16x2_to_f16x2(x0.w));
+            x1 = make_uint4(bf16x2_to_f16x2(x1.x), bf16x2_to_f16x2(x1.y), bf16x2_to_f16x2(x1.z),
+                            bf16x2_to_f16x2(x1.w));
+          }
+          // the pair's operand halves: low 8 bytes of both into block 2p's
+          // slot, high 8 bytes of both into block 2p + 1's
+          *reinterpret_cast<uint4*>(sb + t0 * TILE_BYTES + o) = make_uint4(x0.x, x0.y, x1.x, x1.y);
+          *reinterpret_cast<uint4*>(sb + t1 * TILE_BYTES + o) = make_uint4(x0.z, x0.w, x1.z, x1.w);
+        } else {
+          *reinterpret_cast<uint4*>(sb + t0 * TILE_BYTES + o) = x0;
+          *reinterpret_cast<uint4*>(sb + t1 * TILE_BYTES + o) = x1;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < PT_G; ++u) {
       const int first = 64 * kPfWaves * u + 64 * wave;  // same run as in gload
