@@ -36,11 +36,15 @@ __host__ __device__ inline int v_elem(int t, int d) {
 // with the gfx950 row-swap permutes: permlane16_swap pairs rows (0,1) and
 // (2,3), permlane32_swap pairs rows (0,2) and (1,3); both results of a swap
 // hold the two partners, so combining them gives the pair's value in every lane.
+// Maximum that propagates NaN (v_maximum3_f32 on gfx950): unlike fmaxf it
+// needs no quieting of operands that come from the matrix cores or lane
+// permutes, and two in a row fuse into one instruction.
+__device__ inline float max_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ inline float group_max(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max_nan(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_nan(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ inline float group_sum(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -63,15 +67,11 @@ __device__ inline void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo
 }
 
 // Two bf16 -> two f16, exact for magnitudes below 65520 (8 significant bits
-// fit in 11; under 2^-14 f16 is subnormal, within 2^-25 of the value).
+// fit in 11; under 2^-14 f16 is subnormal, within 2^-25 of the value);
+// magnitudes of 65536 and up become infinities, and NaN stays NaN.
 __device__ inline uint32_t bf16x2_to_f16x2(uint32_t w) {
   const f32x2 f = {__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
-}
-// Bit 15 / 31 set where a bf16 half has magnitude >= 65536 (0x4780), inf or
-// NaN: the halves that have no f16 equal.  The add cannot carry across halves.
-__device__ inline uint32_t bf16x2_beyond_f16(uint32_t w) {
-  return ((w & 0x7FFF7FFFu) + 0x38803880u) & 0x80008000u;
 }
 
 // Small index inputs of the cache-update kernels (slots, table deltas, block

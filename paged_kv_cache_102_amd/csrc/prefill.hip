@@ -307,9 +307,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     *reinterpret_cast<uint2*>(sb + lo + 2 * TILE_BYTES) = make_uint2(x.z, x.w);
   };
   // V goes into LDS as f16 when P.V runs on f16 operands (H); a bf16 V
-  // element with no f16 equal is noted in `wide` (the workgroup then runs
-  // again with bf16 operands)
-  uint32_t wide = 0;
+  // element with no f16 equal becomes an f16 infinity or NaN there
   auto lwrite = [&](int s, auto h) {
     constexpr bool H = decltype(h)::value;
     unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
@@ -323,9 +321,6 @@ void prefill_bf16_kernel(PrefillArgs a) {
         const int o = run_off(2 * i) + lane * 16;
         if (t0 & 1) {
           if constexpr (H) {
-            wide |= bf16x2_beyond_f16(x0.x) | bf16x2_beyond_f16(x0.y) | bf16x2_beyond_f16(x0.z) |
-                    bf16x2_beyond_f16(x0.w) | bf16x2_beyond_f16(x1.x) | bf16x2_beyond_f16(x1.y) |
-                    bf16x2_beyond_f16(x1.z) | bf16x2_beyond_f16(x1.w);
             x0 = make_uint4(bf16x2_to_f16x2(x0.x), bf16x2_to_f16x2(x0.y), bf16x2_to_f16x2(x0.z),
                             bf16x2_to_f16x2(x0.w));
             x1 = make_uint4(bf16x2_to_f16x2(x1.x), bf16x2_to_f16x2(x1.y), bf16x2_to_f16x2(x1.z),
@@ -372,8 +367,6 @@ void prefill_bf16_kernel(PrefillArgs a) {
         uint4 x = st[u];
         vmask(s, tile, x);  // first: slots outside the context may hold anything
         if (H && (tile & 1)) {
-          wide |= bf16x2_beyond_f16(x.x) | bf16x2_beyond_f16(x.y) | bf16x2_beyond_f16(x.z) |
-                  bf16x2_beyond_f16(x.w);
           x = make_uint4(bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
                          bf16x2_to_f16x2(x.w));
         }
@@ -515,11 +508,11 @@ void prefill_bf16_kernel(PrefillArgs a) {
           if (tp > pos[t] || tp < lo_c[t]) sv[e] = -INFINITY;
         }
       }
-      float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      // a chain of three-way maxima (a NaN score, from NaN inputs, makes
+      // the column's output NaN either way)
+      float mloc = max_nan(sv[0], sv[1]);
 #pragma unroll
-      for (int e = 8; e < 4 * SB; e += 4)
-        mloc = fmaxf(mloc, fmaxf(fmaxf(sv[e], sv[e + 1]), fmaxf(sv[e + 2], sv[e + 3])));
+      for (int e = 2; e < 4 * SB; e += 2) mloc = max_nan(max_nan(mloc, sv[e]), sv[e + 1]);
       mloc = group_max(mloc) * cs;
       // lazy max: raise it only when the stage max exceeds it by 2^8
       const bool raise = mloc > m[t] + kPfRescale;
@@ -584,12 +577,23 @@ void prefill_bf16_kernel(PrefillArgs a) {
   // P.V on f16 operands: the weights lie in [0, 2^8] and round to 11
   // significant bits (bf16 would keep 8, and needs a residual product to
   // stay inside the tolerance).  A bf16 cache can hold V elements that f16
-  // cannot; when a stage held one, the workgroup runs again with bf16
-  // operands (the weights as high part plus residual).
+  // cannot (magnitude 2^16 and up, infinities, NaN); their f16 forms are
+  // infinities or NaN, and the weight of every column times one of them
+  // (weights are >= 0; 0 times infinity is NaN) leaves that accumulator
+  // non-finite for the rest of the run, while finite operands cannot
+  // overflow it (|o| < 2^8 * 65504 per position).  A workgroup with any
+  // non-finite accumulator runs again with bf16 operands (the weights as
+  // high part plus residual); so does one whose scores were NaN or infinite,
+  // which then gives the same NaN output.
   run(PfF16<true>{});
   if constexpr (!F8) {
+    float chk = 0.f;
+#pragma unroll
+    for (int t = 0; t < NQ; ++t)
+#pragma unroll
+      for (int k = 0; k < NT; ++k) chk += (o[t][k][0] + o[t][k][1]) + (o[t][k][2] + o[t][k][3]);
     __shared__ int s_wide[kPfWaves];
-    const bool mine = __builtin_amdgcn_ballot_w64(wide != 0) != 0;
+    const bool mine = __builtin_amdgcn_ballot_w64(!__builtin_isfinite(chk)) != 0;
     if (lane == 0) s_wide[wave] = mine;
     __syncthreads();  // also: every wavefront is done with the last stage's LDS
     int any = 0;
