@@ -551,8 +551,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
 
   // Pipeline: stage s is in LDS buffer s % 2.  At the top of each trip the
   // barrier makes stage s visible and frees buffer (s + 1) % 2 (every
-  // wavefront has finished stage s - 1), which then takes stage s + 1 from
-  // registers while stage s + 2's global loads go out.
+  // wavefront has finished stage s - 1), which takes stage s + 1 from
+  // registers during the trip; stage s + 2's global loads go out after it.
   auto run = [&](auto h) {
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
@@ -564,14 +564,24 @@ void prefill_bf16_kernel(PrefillArgs a) {
     gload(0);
     lwrite(0, h);
     gload(1);
+    // The second half of the wavefronts (one per SIMD) stages after its
+    // products, so that on each SIMD one wavefront's LDS stores and loads run
+    // beside the other's scores instead of every wavefront doing the same
+    // thing after the barrier (buffer (s + 1) % 2 is free from the barrier
+    // on, and stage s + 1's data is written before the next one).
+    const bool late = wave >= kPfWaves / 2;
     for (int s = 0; s < nst; ++s) {
       __syncthreads();
-      if (s + 1 < nst) {
+      if (!late && s + 1 < nst) {
         lwrite(s + 1, h);
         gload(s + 2);
       }
       score(s, h);
       pv(s, h);
+      if (late && s + 1 < nst) {
+        lwrite(s + 1, h);
+        gload(s + 2);
+      }
     }
   };
   // P.V on f16 operands: the weights lie in [0, 2^8] and round to 11
