@@ -493,32 +493,44 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // masks are needed only where the stage reaches past the tile's first
     // position (causal) or before its last column's window start
     const bool edge = tb0 + SB * kBlock - 1 > p_first || (WIN && tb0 < p_last - a.window + 1);
+    // Both column tiles go through each step together (one test for a
+    // raised maximum, independent chains side by side).
+    // raw scores; masked ones become -inf (exp2 of them is 0)
+    float sv[NQ][4 * SB];
+    float mloc[NQ];
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
-      // raw scores; masked ones become -inf (exp2 of them is 0)
-      float sv[4 * SB];
 #pragma unroll
       for (int bb = 0; bb < SB; ++bb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sv[4 * bb + r] = sc[t][bb][r];
+        for (int r = 0; r < 4; ++r) sv[t][4 * bb + r] = sc[t][bb][r];
       if (edge) {
 #pragma unroll
         for (int e = 0; e < 4 * SB; ++e) {
           const int tp = tb0 + (e >> 2) * kBlock + grp * 4 + (e & 3);
-          if (tp > pos[t] || tp < lo_c[t]) sv[e] = -INFINITY;
+          if (tp > pos[t] || tp < lo_c[t]) sv[t][e] = -INFINITY;
         }
       }
       // a chain of three-way maxima (a NaN score, from NaN inputs, makes
       // the column's output NaN either way)
-      float mloc = max_nan(sv[0], sv[1]);
+      mloc[t] = max_nan(sv[t][0], sv[t][1]);
 #pragma unroll
-      for (int e = 2; e < 4 * SB; e += 2) mloc = max_nan(max_nan(mloc, sv[e]), sv[e + 1]);
-      mloc = group_max(mloc) * cs;
-      // lazy max: raise it only when the stage max exceeds it by 2^8
-      const bool raise = mloc > m[t] + kPfRescale;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m[t] - mloc) : 1.0f;
-        m[t] = raise ? mloc : m[t];
+      for (int e = 2; e < 4 * SB; e += 2) mloc[t] = max_nan(max_nan(mloc[t], sv[t][e]), sv[t][e + 1]);
+    }
+    // lazy max: raise it only when the stage max exceeds it by 2^8
+    bool raise[NQ];
+    bool any = false;
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) {
+      mloc[t] = group_max(mloc[t]) * cs;
+      raise[t] = mloc[t] > m[t] + kPfRescale;
+      any |= raise[t];
+    }
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) {
+        const float alpha = raise[t] ? __builtin_amdgcn_exp2f(m[t] - mloc[t]) : 1.0f;
+        m[t] = raise[t] ? mloc[t] : m[t];
         // output rows are columns 4 grp + r of the tile; their factors sit in lanes 4 grp + r
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -528,16 +540,19 @@ void prefill_bf16_kernel(PrefillArgs a) {
           for (int k = 0; k < NT; ++k) o[t][k][r] *= ar;
         }
       }
-      // (a column's masked scores are -inf, its unmasked ones finite: the
-      // fma gives -inf or a finite value for any cs >= 0 except cs = 0,
-      // where -inf * 0 is NaN; masks therefore select 0 after exp2)
+    }
+    // (a column's masked scores are -inf, its unmasked ones finite: the
+    // fma gives -inf or a finite value for any cs >= 0 except cs = 0,
+    // where -inf * 0 is NaN; masks therefore select 0 after exp2)
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) {
       float p[4 * SB];
 #pragma unroll
-      for (int e = 0; e < 4 * SB; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], cs, -m[t]));
+      for (int e = 0; e < 4 * SB; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][e], cs, -m[t]));
       if (edge) {
 #pragma unroll
         for (int e = 0; e < 4 * SB; ++e)
-          if (sv[e] == -INFINITY) p[e] = 0.f;
+          if (sv[t][e] == -INFINITY) p[e] = 0.f;
       }
 #pragma unroll
       for (int e = 0; e < 2 * SB; ++e) {
