@@ -9,6 +9,7 @@
 // cuaderno sea más fino» (an 8-bit cache).
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 
@@ -66,13 +67,14 @@ constexpr int kPfWaves = 8;
 constexpr int kPfColTiles = 2;                       // 16-column tiles per wavefront
 constexpr int kPfCols = kPfWaves * kPfColTiles * 16;  // score columns per workgroup
 constexpr float kPfRescale = 8.0f;                   // lazy max threshold (log2 domain)
-constexpr int kPfStageBlocks = 4;                    // default blocks per pipeline stage
+constexpr int kPfStageBlocks = 4;                    // blocks per pipeline stage
 template <bool B>
-struct PfF16 {  // P.V operand type of a prefill pass: f16 (true) or bf16 high + residual
+struct PfF16 {  // a compile-time flag: the P.V operand type of a prefill pass, f16
+                // (true) or bf16 high + residual, or whether a stage needs masks
   static constexpr bool value = B;
 };
 
-// SB: blocks per pipeline stage (even: P.V takes them in pairs).  F8: the
+// SB: blocks per pipeline stage (two pairs: P.V takes them in pairs).  F8: the
 // cache holds FP8 E4M3 codes; each lane's 16 codes of a 1 KiB run are
 // expanded to its two bf16 pieces on the way into LDS, so everything after
 // the staging is the bf16 path (K scale folded into the score scale, V
@@ -80,20 +82,19 @@ struct PfF16 {  // P.V operand type of a prefill pass: f16 (true) or bf16 high +
 template <int D, bool WIN, int SB, bool F8 = false>
 __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillArgs a) {
-  static_assert(SB % 2 == 0, "blocks per stage come in pairs");
+  static_assert(SB == 4, "a stage is two pairs of blocks");
   constexpr int NJ = D / 32;                  // K / V pieces per tile
   constexpr int NT = D / 16;                  // 16-channel output tiles
   constexpr int NQ = kPfColTiles;
   constexpr int TILE_BYTES = kBlock * D * 2;
   constexpr int STAGE_BYTES = 2 * SB * TILE_BYTES;  // blocks 0 .. SB-1 x (K, V)
-  constexpr int TILE_PIECES = TILE_BYTES / 16;
   // tiles in global memory: as in LDS, or FP8 at one byte per element
   constexpr int TILE_G = F8 ? kBlock * D : TILE_BYTES;
   constexpr int TILE_PIECES_G = TILE_G / 16;
   constexpr int PT_G = 2 * SB * TILE_PIECES_G / (64 * kPfWaves);  // global pieces per thread
   static_assert(PT_G >= 1 && (2 * SB * TILE_PIECES_G) % (64 * kPfWaves) == 0,
                 "a stage's global pieces spread evenly over the threads");
-  constexpr int NBUF = 2;  // stage s, and stage s + 1 being filled
+  constexpr int NBUF = 3;  // stage s, stage s + 1 (its first pair's scores), stage s + 2 being filled
   __shared__ __align__(16) unsigned char lds[NBUF * STAGE_BYTES];
 
   // Work item: workgroup i runs on XCD i % 8, and all query tiles of one
@@ -151,7 +152,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (kPfWaves - 1);
   const int hcol = lane & 15;
   const int grp = lane >> 4;
   const int g = a.group;
@@ -220,75 +221,87 @@ void prefill_bf16_kernel(PrefillArgs a) {
   const char* kc = static_cast<const char*>(a.kc) + int64_t(kvh) * TILE_G;
   const char* vc = static_cast<const char*>(a.vc) + int64_t(kvh) * TILE_G;
   const int64_t block_bytes = int64_t(a.num_kv_heads) * TILE_G;
+  // a live block id outside the pool makes the tile's output NaN (its runs
+  // load nothing)
   bool bad = false;
+  for (int i = lane; i < nblk; i += 64)
+    bad |= static_cast<unsigned>(row[i]) >= static_cast<unsigned>(a.num_blocks);
+  bad = __builtin_amdgcn_ballot_w64(bad) != 0;
 
-  // Stage loader: thread tid moves pieces 512 u + tid (u < PT) of the stage's
-  // tiles (block 0 K, block 0 V, block 1 K, ...); a wavefront's 64 pieces lie
-  // in one tile, so the tile and its block id are wave-uniform: each run
-  // reads its own block id through the scalar cache (a run needs one entry;
-  // reading the stage's entries and selecting among them cost 3-6 % of the
-  // kernel in scalar work).  V slots outside [t_lo, L) are zeroed
-  // when the pieces go into LDS, a trip after their loads (they may hold
-  // anything; masking them at load time would wait for the loads at once).
-  // An FP8 run expands to two bf16 runs as it goes into LDS.
+  // Stage loader.  A stage is SB blocks (tiles block 0 K, block 0 V, block
+  // 1 K, ...), moved as 1 KiB runs (64 lanes x 16 bytes), each run by one
+  // wavefront, so a run's tile and block id are wave-uniform: each run reads
+  // its own block id through the scalar cache (reading the stage's entries
+  // and selecting among them cost 3-6 % of the kernel in scalar work).  A
+  // wavefront's runs are grouped in slots, the first half of them K and the
+  // second V (with one slot per wavefront: the first four wavefronts K), so
+  // the staging code has no branch on the tile kind.  bf16 cache: a slot is
+  // the same 1 KiB piece of both blocks of a pair, so a lane holds both
+  // halves of each P.V operand; FP8 cache: a slot is one run of codes, which
+  // expands to two bf16 runs in LDS.  V slots outside [t_lo, L) are zeroed a
+  // stage after their loads (they may hold anything; masking them at load
+  // time would wait for the loads at once).
   uint4 st[PT_G];
-  // bf16 cache, PT_G even: runs 2i and 2i + 1 of a wavefront are the same
-  // 1 KiB piece of K or V of the two blocks of a pair (pair-run i * 8 + w:
-  // K pairs first, then V), so a lane holds both halves of each P.V operand
-  constexpr bool PAIRED = !F8 && PT_G % 2 == 0;
-  constexpr int RPT = TILE_PIECES_G / 64;  // runs per tile
-  constexpr int HALF_PAIRS = SB / 2 * RPT;  // pair-runs of K (or of V) per stage
-  auto run_tile = [&](int u) {
-    if constexpr (PAIRED) {
-      const int k = (u >> 1) * kPfWaves + wave;
-      const int rem = k % HALF_PAIRS;
-      return 2 * (2 * (rem / RPT) + (u & 1)) + k / HALF_PAIRS;
-    } else {
-      return (64 * kPfWaves * u + 64 * wave) / TILE_PIECES_G;
-    }
+  constexpr bool PAIRED = !F8;
+  constexpr int RPT = TILE_PIECES_G / 64;        // runs per tile
+  constexpr int PR = PAIRED ? 2 : 1;             // runs per slot
+  constexpr int NS = PT_G / PR;                  // slots per wavefront
+  constexpr int KIND = SB * RPT / PR;            // slots of K (and of V) per stage
+  static_assert(PT_G % PR == 0 && (NS == 1 ? 2 * KIND == kPfWaves
+                                           : NS % 2 == 0 && NS / 2 * kPfWaves == KIND),
+                "a stage's slots spread evenly over the wavefronts, K and V apart");
+  auto slot_v = [&](int i) { return NS == 1 ? wave >= kPfWaves / 2 : i >= NS / 2; };
+  auto slot_k = [&](int i) {  // index among the stage's slots of its kind
+    return NS == 1 ? wave % (kPfWaves / 2) : (i % (NS / 2)) * kPfWaves + wave;
   };
-  auto run_off = [&](int u) {  // byte offset of the run in its tile (global memory)
-    if constexpr (PAIRED)
-      return (((u >> 1) * kPfWaves + wave) % HALF_PAIRS % RPT) * 1024;
-    else
-      return ((64 * kPfWaves * u + 64 * wave) % TILE_PIECES_G) * 16;
-  };
+  // run u (slot u / PR): V or K, its block in the stage, its byte offset in the tile
+  auto run_v = [&](int u) { return slot_v(u / PR); };
+  auto run_blk = [&](int u) { return PR * (slot_k(u / PR) / RPT) + u % PR; };
+  auto run_off = [&](int u) { return (slot_k(u / PR) % RPT) * 1024; };
   auto gload = [&](int s) {
 #pragma unroll
     for (int u = 0; u < PT_G; ++u) {
-      // the wavefront's 64 pieces: a 1 KiB run at a uniform offset of its tile
-      const int tile = run_tile(u);
-      const int off0 = run_off(u);
-      // this run's block id, read for this run alone (wave-uniform); past the
-      // last block the read is of the last entry and the run loads nothing
-      const int rel = SB * s + (tile >> 1);
+      // this run's block id (wave-uniform); past the last block the read is
+      // of the last entry and the run loads nothing
+      const int rel = SB * s + run_blk(u);
       const bool live = rel < nblk;
       const int phys = load_uniform(row, live ? rel : nblk - 1);
-      const bool ok = static_cast<unsigned>(phys) < static_cast<unsigned>(a.num_blocks);
-      bad |= live && !ok;
-      const int bytes = (live && ok) ? TILE_G : 0;
-      const char* base = ((tile & 1) ? vc : kc) +
-                         (bytes ? int64_t(static_cast<uint32_t>(phys)) * block_bytes : 0) + off0;
-      const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, bytes ? bytes - off0 : 0);
+      const bool use = live && static_cast<unsigned>(phys) < static_cast<unsigned>(a.num_blocks);
+      const int off0 = run_off(u);
+      // (an unused run points at block 0 with no bytes: selects, not branches)
+      const uint32_t pid = use ? static_cast<uint32_t>(phys) : 0u;
+      const __amdgpu_buffer_rsrc_t r =
+          tile_rsrc((run_v(u) ? vc : kc) + int64_t(pid) * block_bytes + off0, use ? TILE_G - off0 : 0);
       st[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 0, 0));
     }
   };
-  // V slots of stage s outside [t_lo, L): lane l of a 1 KiB V run holds
-  // tokens 4 (l / 16) .. + 3 of its block
-  auto vmask = [&](int s, int tile, uint4& x) {
-    // only a block that holds positions before t_lo or from L on (tested
-    // once per block, wave-uniform) needs the per-lane test
-    const int b0 = (i0 + SB * s + (tile >> 1)) * kBlock;
-    if ((tile & 1) && (b0 < t_lo || b0 + kBlock > L)) {
-      const int t0 = b0 + 4 * grp;
-      if (t0 < t_lo || t0 + 4 > L) {
+  // V slots of stage s outside [t_lo, L): lane l of a V run holds tokens
+  // 4 (l / 16) .. + 3 of its block (16-bit fields t % 4 and 4 + t % 4 of
+  // each 8-element piece; FP8: bytes).  Only a block that holds positions
+  // before t_lo or from L on (tested once per block, wave-uniform) is masked.
+  auto vmask = [&](int s) {
+#pragma unroll
+    for (int u = 0; u < PT_G; ++u) {
+      const int b0 = (i0 + SB * s + run_blk(u)) * kBlock;
+      if (run_v(u) && (b0 < t_lo || b0 + kBlock > L)) {
+        const int t0 = b0 + 4 * grp;
         auto in = [&](int t) { return t < L && t >= t_lo; };
-        const uint32_t m01 = (in(t0) ? 0x0000FFFFu : 0u) | (in(t0 + 1) ? 0xFFFF0000u : 0u);
-        const uint32_t m23 = (in(t0 + 2) ? 0x0000FFFFu : 0u) | (in(t0 + 3) ? 0xFFFF0000u : 0u);
-        x.x &= m01;
-        x.y &= m23;
-        x.z &= m01;
-        x.w &= m23;
+        uint4& x = st[u];
+        if constexpr (F8) {
+          const uint32_t mk = (in(t0) ? 0x000000FFu : 0u) | (in(t0 + 1) ? 0x0000FF00u : 0u) |
+                              (in(t0 + 2) ? 0x00FF0000u : 0u) | (in(t0 + 3) ? 0xFF000000u : 0u);
+          x.x &= mk;
+          x.y &= mk;
+          x.z &= mk;
+          x.w &= mk;
+        } else {
+          const uint32_t m01 = (in(t0) ? 0x0000FFFFu : 0u) | (in(t0 + 1) ? 0xFFFF0000u : 0u);
+          const uint32_t m23 = (in(t0 + 2) ? 0x0000FFFFu : 0u) | (in(t0 + 3) ? 0xFFFF0000u : 0u);
+          x.x &= m01;
+          x.y &= m23;
+          x.z &= m01;
+          x.w &= m23;
+        }
       }
     }
   };
@@ -296,30 +309,27 @@ void prefill_bf16_kernel(PrefillArgs a) {
   // 2p + 1 of a stage, the tile slot of block 2p holds, at each 16-byte
   // chunk, the chunk's low 8 bytes of block 2p then those of block 2p + 1,
   // and the slot of block 2p + 1 the high 8 bytes of both, so each chunk is
-  // one operand of the pair's product, read as it lies (no register moves
-  // in P.V: -4 % on the FP8 form, -1.7 % on the bf16 one).  A bf16 lane holds
-  // the same piece of both blocks (paired runs above) and writes the two
-  // chunks whole; an FP8 run holds one block, written as 8-byte halves.
-  constexpr bool VPAIR = F8 || PAIRED;
+  // one operand of the pair's product, read as it lies.  A bf16 lane holds
+  // the same piece of both blocks and writes the two chunks whole; an FP8
+  // run holds one block, written as 8-byte halves.
   auto vstore = [&](unsigned char* sb, int blk, int o, uint4 x) {
     const int lo = (4 * (blk >> 1) + 1) * TILE_BYTES + o + 8 * (blk & 1);
     *reinterpret_cast<uint2*>(sb + lo) = make_uint2(x.x, x.y);
     *reinterpret_cast<uint2*>(sb + lo + 2 * TILE_BYTES) = make_uint2(x.z, x.w);
   };
-  // V goes into LDS as f16 when P.V runs on f16 operands (H); a bf16 V
-  // element with no f16 equal becomes an f16 infinity or NaN there
-  auto lwrite = [&](int s, auto h) {
+  // stage s from the staging registers into its LDS buffer; V goes in as
+  // f16 when P.V runs on f16 operands (H), where a bf16 V element with no
+  // f16 equal becomes an f16 infinity or NaN
+  auto lstore = [&](int s, auto h) {
     constexpr bool H = decltype(h)::value;
     unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
     if constexpr (PAIRED) {
 #pragma unroll
-      for (int i = 0; i < PT_G / 2; ++i) {
-        const int t0 = run_tile(2 * i), t1 = run_tile(2 * i + 1);
+      for (int i = 0; i < NS; ++i) {
         uint4 x0 = st[2 * i], x1 = st[2 * i + 1];
-        vmask(s, t0, x0);
-        vmask(s, t1, x1);
+        const int blk = run_blk(2 * i);  // the pair's first block
         const int o = run_off(2 * i) + lane * 16;
-        if (t0 & 1) {
+        if (slot_v(i)) {
           if constexpr (H) {
             x0 = make_uint4(bf16x2_to_f16x2(x0.x), bf16x2_to_f16x2(x0.y), bf16x2_to_f16x2(x0.z),
                             bf16x2_to_f16x2(x0.w));
@@ -328,49 +338,30 @@ void prefill_bf16_kernel(PrefillArgs a) {
           }
           // the pair's operand halves: low 8 bytes of both into block 2p's
           // slot, high 8 bytes of both into block 2p + 1's
-          *reinterpret_cast<uint4*>(sb + t0 * TILE_BYTES + o) = make_uint4(x0.x, x0.y, x1.x, x1.y);
-          *reinterpret_cast<uint4*>(sb + t1 * TILE_BYTES + o) = make_uint4(x0.z, x0.w, x1.z, x1.w);
+          *reinterpret_cast<uint4*>(sb + (2 * blk + 1) * TILE_BYTES + o) = make_uint4(x0.x, x0.y, x1.x, x1.y);
+          *reinterpret_cast<uint4*>(sb + (2 * blk + 3) * TILE_BYTES + o) = make_uint4(x0.z, x0.w, x1.z, x1.w);
         } else {
-          *reinterpret_cast<uint4*>(sb + t0 * TILE_BYTES + o) = x0;
-          *reinterpret_cast<uint4*>(sb + t1 * TILE_BYTES + o) = x1;
+          *reinterpret_cast<uint4*>(sb + (2 * blk) * TILE_BYTES + o) = x0;
+          *reinterpret_cast<uint4*>(sb + (2 * blk + 2) * TILE_BYTES + o) = x1;
         }
       }
-      return;
-    }
+    } else {
 #pragma unroll
-    for (int u = 0; u < PT_G; ++u) {
-      const int first = 64 * kPfWaves * u + 64 * wave;  // same run as in gload
-      const int tile = first / TILE_PIECES_G;
-      if constexpr (F8) {
-        // FP8 run i of the tile holds operand pieces 2i and 2i + 1 of each
+      for (int u = 0; u < PT_G; ++u) {
+        // FP8 run i of a tile holds operand pieces 2i and 2i + 1 of each
         // lane (E4M3 values are exact in both bf16 and f16)
         const uint4 w = st[u];
-        uint4 x, y;
-        if (H && (tile & 1)) {
-          x = e4m3x8_to_f16x8(w.x, w.y);
-          y = e4m3x8_to_f16x8(w.z, w.w);
+        const int blk = run_blk(u);
+        const int o = 2 * run_off(u) + lane * 16;
+        if (run_v(u)) {
+          const uint4 x = H ? e4m3x8_to_f16x8(w.x, w.y) : e4m3x8_to_bf16x8(w.x, w.y);
+          const uint4 y = H ? e4m3x8_to_f16x8(w.z, w.w) : e4m3x8_to_bf16x8(w.z, w.w);
+          vstore(sb, blk, o, x);
+          vstore(sb, blk, o + 1024, y);
         } else {
-          x = e4m3x8_to_bf16x8(w.x, w.y);
-          y = e4m3x8_to_bf16x8(w.z, w.w);
+          *reinterpret_cast<uint4*>(sb + 2 * blk * TILE_BYTES + o) = e4m3x8_to_bf16x8(w.x, w.y);
+          *reinterpret_cast<uint4*>(sb + 2 * blk * TILE_BYTES + o + 1024) = e4m3x8_to_bf16x8(w.z, w.w);
         }
-        vmask(s, tile, x);
-        vmask(s, tile, y);
-        const int o = 2048 * ((first % TILE_PIECES_G) / 64) + lane * 16;
-        if (tile & 1) {
-          vstore(sb, tile >> 1, o, x);
-          vstore(sb, tile >> 1, o + 1024, y);
-        } else {
-          *reinterpret_cast<uint4*>(sb + tile * TILE_BYTES + o) = x;
-          *reinterpret_cast<uint4*>(sb + tile * TILE_BYTES + o + 1024) = y;
-        }
-      } else {
-        uint4 x = st[u];
-        vmask(s, tile, x);  // first: slots outside the context may hold anything
-        if (H && (tile & 1)) {
-          x = make_uint4(bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
-                         bf16x2_to_f16x2(x.w));
-        }
-        *reinterpret_cast<uint4*>(sb + tile * TILE_BYTES + (first % TILE_PIECES) * 16 + lane * 16) = x;
       }
     }
   };
@@ -378,16 +369,20 @@ void prefill_bf16_kernel(PrefillArgs a) {
   f32x4 o[NQ][NT];
   // running max per column (log2 domain, scaled; a finite floor, so that a
   // column with nothing visible yet gets weights exp2(-inf - floor) = 0),
-  // and the normalisers: row sums of the same bf16 weight parts that P.V
-  // uses, formed by the matrix cores (P times a column of ones) in the
-  // output layout, so numerator and denominator share every rounding
+  // and the normalisers: row sums of the same weights that P.V uses,
+  // formed by the matrix cores (P times a column of ones) in the output
+  // layout, so numerator and denominator share every rounding
   float m[NQ];
   f32x4 lacc[NQ];
   const f16x8 ones16 = __builtin_bit_cast(f16x8, make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
-  // weights exp2(cs * s - m) with cs >= 0: a negative scale negates Q
-  // instead (exact in bf16), so the scaled max is the raw max times cs
-  const float cs = fabsf(a.scale_log2e);
+  // weights exp2(cs * s - m) with cs > 0: a negative scale negates Q
+  // instead (exact in bf16), so the scaled max is the raw max times cs.  A
+  // scale below the smallest normal float (zero included) is taken as that
+  // smallest normal: every finite score (|s| < 2^40) times it is below
+  // 2^-86, so every visible weight is exactly 1 either way, while a masked
+  // score (-inf) keeps weight 0 (with cs = 0 it would give -inf * 0 = NaN).
+  const float cs = fabsf(a.scale_log2e) < FLT_MIN ? FLT_MIN : fabsf(a.scale_log2e);
   if (a.scale_log2e < 0.f) {
 #pragma unroll
     for (int t = 0; t < NQ; ++t)
@@ -402,135 +397,70 @@ void prefill_bf16_kernel(PrefillArgs a) {
       }
   }
 
-  // weights of the stage being processed: f16 pairs (H), else bf16 high
-  // parts and residuals
-  uint32_t phi[NQ][2 * SB], plo[NQ][2 * SB];
-  // O += P . V over each pair of blocks of stage s (k < 4: the pair's first
-  // block, k >= 4: its second); each V piece is read once and used by all
-  // column tiles
-  auto pv = [&](int s, auto h) {
-    constexpr bool H = decltype(h)::value;
-    const unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
-    // the matrix-core phases (here and the scores) run at raised wave
-    // priority: the two wavefronts of a SIMD pass each barrier together, and
-    // the issue arbiter then favours the one that reaches its products first,
-    // so the other's vector work fills in beside them (-3 % on the bf16 form)
-    __builtin_amdgcn_s_setprio(1);
+  // The unit of work is a pair of blocks (32 tokens).  Pair q of stage s:
+  // K tiles 4q and 4q + 2 of the stage's buffer, V (in operand order)
+  // tiles 4q + 1 and 4q + 3.  Its scores: S^T tiles per column tile and block.
+  typedef f32x4 Scores[NQ][2];
+  auto qk = [&](const unsigned char* kb, Scores& S) {
 #pragma unroll
-    for (int pp = 0; pp < SB / 2; ++pp) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const uint4 vl = *reinterpret_cast<const uint4*>(sb + (4 * pp + 1) * TILE_BYTES + 1024 * j + lane * 16);
-        const uint4 vh = *reinterpret_cast<const uint4*>(sb + (4 * pp + 3) * TILE_BYTES + 1024 * j + lane * 16);
-        if constexpr (H) {
-          const f16x8 vlo = __builtin_bit_cast(f16x8, VPAIR ? vl : make_uint4(vl.x, vl.y, vh.x, vh.y));
-          const f16x8 vhi = __builtin_bit_cast(f16x8, VPAIR ? vh : make_uint4(vl.z, vl.w, vh.z, vh.w));
-#pragma unroll
-          for (int t = 0; t < NQ; ++t) {
-            const f16x8 ph = __builtin_bit_cast(f16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
-                                                                  phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
-            o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vlo, o[t][2 * j], 0, 0, 0);
-            o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vhi, o[t][2 * j + 1], 0, 0, 0);
-          }
-          continue;
-        }
-        const bf16x8 vlo = __builtin_bit_cast(bf16x8, VPAIR ? vl : make_uint4(vl.x, vl.y, vh.x, vh.y));
-        const bf16x8 vhi = __builtin_bit_cast(bf16x8, VPAIR ? vh : make_uint4(vl.z, vl.w, vh.z, vh.w));
-#pragma unroll
-        for (int t = 0; t < NQ; ++t) {
-          const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
-                                                                  phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
-          const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(plo[t][4 * pp], plo[t][4 * pp + 1],
-                                                                  plo[t][4 * pp + 2], plo[t][4 * pp + 3]));
-          o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vlo, o[t][2 * j], 0, 0, 0);
-          o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vlo, o[t][2 * j], 0, 0, 0);
-          o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vhi, o[t][2 * j + 1], 0, 0, 0);
-          o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vhi, o[t][2 * j + 1], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < NQ; ++t) {
-        if constexpr (H) {
-          const f16x8 ph = __builtin_bit_cast(f16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
-                                                                phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
-          lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, ones16, lacc[t], 0, 0, 0);
-          continue;
-        }
-        const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(phi[t][4 * pp], phi[t][4 * pp + 1],
-                                                                phi[t][4 * pp + 2], phi[t][4 * pp + 3]));
-        const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(plo[t][4 * pp], plo[t][4 * pp + 1],
-                                                                plo[t][4 * pp + 2], plo[t][4 * pp + 3]));
-        lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ones, lacc[t], 0, 0, 0);
-        lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, ones, lacc[t], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-  };
-
-  // scores of stage s, softmax update, weights into phi / plo
-  auto score = [&](int s, auto h) {
-    constexpr bool H = decltype(h)::value;
-    const unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
-    const int tb0 = (i0 + SB * s) * kBlock;  // first position of the stage
-    // scores of all blocks of the stage for every column tile
-    f32x4 sc[NQ][SB];
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int bb = 0; bb < SB; ++bb) {
+    for (int bb = 0; bb < 2; ++bb) {
       bf16x8 kx[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        kx[j] = *reinterpret_cast<const bf16x8*>(sb + (2 * bb) * TILE_BYTES + 1024 * j + lane * 16);
+        kx[j] = *reinterpret_cast<const bf16x8*>(kb + 2 * bb * TILE_BYTES + 1024 * j + lane * 16);
 #pragma unroll
       for (int t = 0; t < NQ; ++t) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx[j], qf[t][j], acc, 0, 0, 0);
-        sc[t][bb] = acc;
+        S[t][bb] = acc;
       }
     }
-    __builtin_amdgcn_s_setprio(0);
-    // masks are needed only where the stage reaches past the tile's first
-    // position (causal) or before its last column's window start
-    const bool edge = tb0 + SB * kBlock - 1 > p_first || (WIN && tb0 < p_last - a.window + 1);
-    // Both column tiles go through each step together (one test for a
-    // raised maximum, independent chains side by side).
-    // raw scores; masked ones become -inf (exp2 of them is 0)
-    float sv[NQ][4 * SB];
-    float mloc[NQ];
+  };
+  // Masks of a stage's two pairs (edge: the stage reaches past the tile's
+  // first position, or before its last column's window start; masked
+  // scores become -inf) and the lazy max: it is raised only when a column's
+  // max over the stage exceeds it by 2^8, which a lane sees from its own
+  // scores (any lane of the column), so the reduction over the column's
+  // four lanes and the rescale of the accumulators run only then (once per
+  // stage: a second rescale site per loop trip made the compiler copy every
+  // accumulator at each trip).  tb0: the stage's first position.
+  auto smax = [&](Scores& S0, Scores& S1, int tb0, bool edge) {
+    if (edge) {
+#pragma unroll
+      for (int t = 0; t < NQ; ++t)
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tp = tb0 + bb * kBlock + grp * 4 + r;
+            if (tp > pos[t] || tp < lo_c[t]) S0[t][bb][r] = -INFINITY;
+            if (tp + 2 * kBlock > pos[t] || tp + 2 * kBlock < lo_c[t]) S1[t][bb][r] = -INFINITY;
+          }
+    }
+    float ml[NQ];
+    bool need = false;
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
-#pragma unroll
-      for (int bb = 0; bb < SB; ++bb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sv[t][4 * bb + r] = sc[t][bb][r];
-      if (edge) {
-#pragma unroll
-        for (int e = 0; e < 4 * SB; ++e) {
-          const int tp = tb0 + (e >> 2) * kBlock + grp * 4 + (e & 3);
-          if (tp > pos[t] || tp < lo_c[t]) sv[t][e] = -INFINITY;
-        }
-      }
-      // a chain of three-way maxima (a NaN score, from NaN inputs, makes
-      // the column's output NaN either way)
-      mloc[t] = max_nan(sv[t][0], sv[t][1]);
-#pragma unroll
-      for (int e = 2; e < 4 * SB; e += 2) mloc[t] = max_nan(max_nan(mloc[t], sv[t][e]), sv[t][e + 1]);
+      // a chain of three-way maxima (a NaN score, from NaN inputs, makes the
+      // column's output NaN either way)
+      float x = max_nan(S0[t][0][0], S0[t][0][1]);
+      x = max_nan(max_nan(x, S0[t][0][2]), S0[t][0][3]);
+      x = max_nan(max_nan(x, S0[t][1][0]), S0[t][1][1]);
+      x = max_nan(max_nan(x, S0[t][1][2]), S0[t][1][3]);
+      x = max_nan(max_nan(x, S1[t][0][0]), S1[t][0][1]);
+      x = max_nan(max_nan(x, S1[t][0][2]), S1[t][0][3]);
+      x = max_nan(max_nan(x, S1[t][1][0]), S1[t][1][1]);
+      ml[t] = max_nan(max_nan(x, S1[t][1][2]), S1[t][1][3]);
+      need |= ml[t] * cs > m[t] + kPfRescale;
     }
-    // lazy max: raise it only when the stage max exceeds it by 2^8
-    bool raise[NQ];
-    bool any = false;
-#pragma unroll
-    for (int t = 0; t < NQ; ++t) {
-      mloc[t] = group_max(mloc[t]) * cs;
-      raise[t] = mloc[t] > m[t] + kPfRescale;
-      any |= raise[t];
-    }
-    if (__builtin_amdgcn_ballot_w64(any)) {
+    if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
       for (int t = 0; t < NQ; ++t) {
-        const float alpha = raise[t] ? __builtin_amdgcn_exp2f(m[t] - mloc[t]) : 1.0f;
-        m[t] = raise[t] ? mloc[t] : m[t];
+        const float mloc = group_max(ml[t]) * cs;
+        const bool raise = mloc > m[t] + kPfRescale;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m[t] - mloc) : 1.0f;
+        m[t] = raise ? mloc : m[t];
         // output rows are columns 4 grp + r of the tile; their factors sit in lanes 4 grp + r
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -541,33 +471,103 @@ void prefill_bf16_kernel(PrefillArgs a) {
         }
       }
     }
-    // (a column's masked scores are -inf, its unmasked ones finite: the
-    // fma gives -inf or a finite value for any cs >= 0 except cs = 0,
-    // where -inf * 0 is NaN; masks therefore select 0 after exp2)
+  };
+  // weights of a pair: f16 pairs (H), else bf16 high parts and residuals;
+  // operand element i < 4 is row i of the first block, i >= 4 of the second
+  // (a masked score, -inf, gives exp2(-inf) = 0)
+  auto sexp = [&](const Scores& S, uint32_t (&ph)[NQ][4], uint32_t (&pl)[NQ][4], auto h) {
+    constexpr bool H = decltype(h)::value;
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
-      float p[4 * SB];
+      float p[8];
 #pragma unroll
-      for (int e = 0; e < 4 * SB; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][e], cs, -m[t]));
-      if (edge) {
+      for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int e = 0; e < 4 * SB; ++e)
-          if (sv[t][e] == -INFINITY) p[e] = 0.f;
-      }
+        for (int r = 0; r < 4; ++r) {
+          p[4 * bb + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[t][bb][r], cs, -m[t]));
+        }
 #pragma unroll
-      for (int e = 0; e < 2 * SB; ++e) {
+      for (int i = 0; i < 4; ++i) {
         if constexpr (H)
-          phi[t][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p[2 * e], p[2 * e + 1]}), f16x2));
+          ph[t][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p[2 * i], p[2 * i + 1]}), f16x2));
         else
-          split_bf16x2(p[2 * e], p[2 * e + 1], phi[t][e], plo[t][e]);
+          split_bf16x2(p[2 * i], p[2 * i + 1], ph[t][i], pl[t][i]);
+      }
+    }
+  };
+  // O += P . V over a pair (vb: the pair's first V tile slot); each V piece
+  // is read once and used by all column tiles
+  auto pv = [&](const unsigned char* vb, const uint32_t (&ph)[NQ][4], const uint32_t (&pl)[NQ][4],
+                auto h) {
+    constexpr bool H = decltype(h)::value;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint4 vl = *reinterpret_cast<const uint4*>(vb + 1024 * j + lane * 16);
+      const uint4 vh = *reinterpret_cast<const uint4*>(vb + 2 * TILE_BYTES + 1024 * j + lane * 16);
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) {
+        if constexpr (H) {
+          const f16x8 p = __builtin_bit_cast(f16x8, make_uint4(ph[t][0], ph[t][1], ph[t][2], ph[t][3]));
+          o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p, __builtin_bit_cast(f16x8, vl), o[t][2 * j], 0, 0, 0);
+          o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p, __builtin_bit_cast(f16x8, vh), o[t][2 * j + 1], 0, 0, 0);
+        } else {
+          const bf16x8 p = __builtin_bit_cast(bf16x8, make_uint4(ph[t][0], ph[t][1], ph[t][2], ph[t][3]));
+          const bf16x8 q = __builtin_bit_cast(bf16x8, make_uint4(pl[t][0], pl[t][1], pl[t][2], pl[t][3]));
+          const bf16x8 lo = __builtin_bit_cast(bf16x8, vl), hi = __builtin_bit_cast(bf16x8, vh);
+          o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p, lo, o[t][2 * j], 0, 0, 0);
+          o[t][2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q, lo, o[t][2 * j], 0, 0, 0);
+          o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p, hi, o[t][2 * j + 1], 0, 0, 0);
+          o[t][2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q, hi, o[t][2 * j + 1], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) {
+      if constexpr (H) {
+        const f16x8 p = __builtin_bit_cast(f16x8, make_uint4(ph[t][0], ph[t][1], ph[t][2], ph[t][3]));
+        lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p, ones16, lacc[t], 0, 0, 0);
+      } else {
+        const bf16x8 p = __builtin_bit_cast(bf16x8, make_uint4(ph[t][0], ph[t][1], ph[t][2], ph[t][3]));
+        const bf16x8 q = __builtin_bit_cast(bf16x8, make_uint4(pl[t][0], pl[t][1], pl[t][2], pl[t][3]));
+        lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p, ones, lacc[t], 0, 0, 0);
+        lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q, ones, lacc[t], 0, 0, 0);
       }
     }
   };
 
-  // Pipeline: stage s is in LDS buffer s % 2.  At the top of each trip the
-  // barrier makes stage s visible and frees buffer (s + 1) % 2 (every
-  // wavefront has finished stage s - 1), which takes stage s + 1 from
-  // registers during the trip; stage s + 2's global loads go out after it.
+  // One stage, software-pipelined: the masks and max of its scores (both
+  // pairs, computed during the previous stage), then per pair its weights
+  // with the scores of the same pair of stage s + 1 issued among them (the
+  // products run on the matrix cores while the vector unit works), then its
+  // P.V, the first among the staging of stage s + 2 and the loads of stage
+  // s + 3.  S0, S1 hold the scores of stage s on entry, of stage s + 1 on exit.
+  auto stage = [&](int s, Scores& S0, Scores& S1, auto h) {
+    const unsigned char* cur = lds + (s % NBUF) * STAGE_BYTES;
+    const unsigned char* nxt = lds + ((s + 1) % NBUF) * STAGE_BYTES;
+    const int tb0 = (i0 + SB * s) * kBlock;
+    // masks are needed only where the stage reaches past the tile's first
+    // position (causal) or before its last column's window start
+    const bool edge = tb0 + SB * kBlock - 1 > p_first || (WIN && tb0 < p_last - a.window + 1);
+    uint32_t ph[NQ][4], pl[NQ][4];
+    smax(S0, S1, tb0, edge);
+    vmask(s + 2);
+    sexp(S0, ph, pl, h);
+    qk(nxt, S0);
+    pv(cur + TILE_BYTES, ph, pl, h);
+    lstore(s + 2, h);
+    gload(s + 3);
+    sexp(S1, ph, pl, h);
+    qk(nxt + 4 * TILE_BYTES, S1);
+    pv(cur + 5 * TILE_BYTES, ph, pl, h);
+  };
+
+  // Stage s is in LDS buffer s % 3.  The barrier at the top of stage s
+  // makes stage s + 1 visible (written during stage s - 1; its scores are
+  // taken during stage s) and frees buffer (s + 2) % 3
+  // (every wavefront is done with stage s - 1), which takes stage s + 2
+  // from the staging registers during the stage; stage s + 3's loads go out
+  // after it.  Stages past the end load nothing and are stored as zeros
+  // into buffers no wavefront is reading.
   auto run = [&](auto h) {
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
@@ -577,26 +577,19 @@ void prefill_bf16_kernel(PrefillArgs a) {
       lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     gload(0);
-    lwrite(0, h);
+    vmask(0);
+    lstore(0, h);
     gload(1);
-    // The second half of the wavefronts (one per SIMD) stages after its
-    // products, so that on each SIMD one wavefront's LDS stores and loads run
-    // beside the other's scores instead of every wavefront doing the same
-    // thing after the barrier (buffer (s + 1) % 2 is free from the barrier
-    // on, and stage s + 1's data is written before the next one).
-    const bool late = wave >= kPfWaves / 2;
+    vmask(1);
+    lstore(1, h);
+    gload(2);
+    __syncthreads();
+    Scores S0, S1;
+    qk(lds, S0);
+    qk(lds + 4 * TILE_BYTES, S1);
     for (int s = 0; s < nst; ++s) {
-      __syncthreads();
-      if (!late && s + 1 < nst) {
-        lwrite(s + 1, h);
-        gload(s + 2);
-      }
-      score(s, h);
-      pv(s, h);
-      if (late && s + 1 < nst) {
-        lwrite(s + 1, h);
-        gload(s + 2);
-      }
+      if (s) __syncthreads();
+      stage(s, S0, S1, h);
     }
   };
   // P.V on f16 operands: the weights lie in [0, 2^8] and round to 11
@@ -643,9 +636,9 @@ void prefill_bf16_kernel(PrefillArgs a) {
   }
 }
 
-template <int SB, bool F8>
-void launch_prefill_bf16_sb(unsigned grid, hipStream_t stream, const PrefillArgs& a,
-                            int head_dim) {
+template <bool F8>
+void launch_prefill_bf16(unsigned grid, hipStream_t stream, const PrefillArgs& a, int head_dim) {
+  constexpr int SB = kPfStageBlocks;
   const dim3 block(64 * kPfWaves);
   const bool win = a.window > 0;
   if (head_dim == 64) {
@@ -658,19 +651,6 @@ void launch_prefill_bf16_sb(unsigned grid, hipStream_t stream, const PrefillArgs
   } else {
     hipLaunchKernelGGL((prefill_bf16_kernel<128, false, SB, F8>), grid, block, 0, stream, a);
   }
-}
-
-// Blocks per pipeline stage: PKV_PF_STAGE_BLOCKS = 2 or 4 (default kPfStageBlocks)
-// for bf16 caches; FP8 caches always take 4 (a 2-block FP8 stage at head_dim
-// 64 has fewer 16-byte pieces than threads).
-void launch_prefill_bf16(unsigned grid, hipStream_t stream, const PrefillArgs& a, int head_dim,
-                         bool fp8) {
-  if (fp8)
-    launch_prefill_bf16_sb<4, true>(grid, stream, a, head_dim);
-  else if (env_int("PKV_PF_STAGE_BLOCKS", kPfStageBlocks, 2, 4) == 4)
-    launch_prefill_bf16_sb<4, false>(grid, stream, a, head_dim);
-  else
-    launch_prefill_bf16_sb<2, false>(grid, stream, a, head_dim);
 }
 
 }  // namespace
@@ -718,7 +698,10 @@ pkv_status prefill_impl(const void* q, const void* k_cache, const void* v_cache,
   const int64_t grid = tiles * num_seqs * num_kv_heads;
   if (grid > 0x7FFFFFFF) return PKV_ERR_UNSUPPORTED;
   a.tiles = static_cast<int>(tiles);
-  launch_prefill_bf16(static_cast<unsigned>(grid), stream, a, head_dim, fp8);
+  if (fp8)
+    launch_prefill_bf16<true>(static_cast<unsigned>(grid), stream, a, head_dim);
+  else
+    launch_prefill_bf16<false>(static_cast<unsigned>(grid), stream, a, head_dim);
   return launch_status();
 }
 }  // namespace
