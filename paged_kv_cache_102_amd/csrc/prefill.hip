@@ -74,6 +74,20 @@ struct PfF16 {  // a compile-time flag: the P.V operand type of a prefill pass, 
   static constexpr bool value = B;
 };
 
+// LDS through address-space-3 pointers (ds_read / ds_write)
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint4 lds_ld16(const lds_u8* p) {
+  return __builtin_bit_cast(uint4, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p));
+}
+__device__ inline void lds_st16(lds_u8* p, uint4 x) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(p) = __builtin_bit_cast(u32x4, x);
+}
+__device__ inline void lds_st8(lds_u8* p, uint32_t x, uint32_t y) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(p) = u32x2{x, y};
+}
+
 // SB: blocks per pipeline stage (two pairs: P.V takes them in pairs).  F8: the
 // cache holds FP8 E4M3 codes; each lane's 16 codes of a 1 KiB run are
 // expanded to its two bf16 pieces on the way into LDS, so everything after
@@ -258,14 +272,26 @@ void prefill_bf16_kernel(PrefillArgs a) {
   auto run_v = [&](int u) { return slot_v(u / PR); };
   auto run_blk = [&](int u) { return PR * (slot_k(u / PR) / RPT) + u % PR; };
   auto run_off = [&](int u) { return (slot_k(u / PR) % RPT) * 1024; };
+  // The block ids of the stage the next gload takes, lane j holding entry
+  // SB s + j (entries past the tile's last block read as 0 and go unused),
+  // loaded one call ahead with a vector load: a run takes its id with a lane
+  // read instead of a scalar-cache round trip (whose wait would also drain
+  // the wavefront's LDS operations in flight).  Calls go 0, 1, 2, ... from
+  // the start of each run.
+  const __amdgpu_buffer_rsrc_t rrow = tile_rsrc(row, nblk * 4);
+  auto idload = [&](int s) {
+    return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(rrow, (SB * s + (lane & (SB - 1))) * 4, 0, 0));
+  };
+  int idq = 0;
   auto gload = [&](int s) {
+    const int ids = idq;
+    idq = idload(s + 1);
 #pragma unroll
     for (int u = 0; u < PT_G; ++u) {
-      // this run's block id (wave-uniform); past the last block the read is
-      // of the last entry and the run loads nothing
+      // this run's block id (wave-uniform); a run past the last block loads nothing
       const int rel = SB * s + run_blk(u);
       const bool live = rel < nblk;
-      const int phys = load_uniform(row, live ? rel : nblk - 1);
+      const int phys = __builtin_amdgcn_readlane(ids, run_blk(u));
       const bool use = live && static_cast<unsigned>(phys) < static_cast<unsigned>(a.num_blocks);
       const int off0 = run_off(u);
       // (an unused run points at block 0 with no bytes: selects, not branches)
@@ -312,23 +338,33 @@ void prefill_bf16_kernel(PrefillArgs a) {
   // one operand of the pair's product, read as it lies.  A bf16 lane holds
   // the same piece of both blocks and writes the two chunks whole; an FP8
   // run holds one block, written as 8-byte halves.
-  auto vstore = [&](unsigned char* sb, int blk, int o, uint4 x) {
+  // This lane's address in stage buffer s % NBUF plus a wave-uniform
+  // offset, made opaque to the compiler: each access then adds its constant
+  // tile offset as the instruction's immediate (from one visible base, the
+  // three 32 KiB buffers lie beyond the immediate's 64 KiB reach and every
+  // access took a vector add of its own).
+  auto lbase = [&](int s, int extra) -> lds_u8* {
+    uint32_t v = static_cast<uint32_t>((uintptr_t)(lds_u8*)lds) + (s % NBUF) * STAGE_BYTES + lane * 16 + extra;
+    __asm__("" : "+v"(v));
+    return (lds_u8*)(uintptr_t)v;
+  };
+  auto vstore = [&](lds_u8* sb, int blk, int o, uint4 x) {
     const int lo = (4 * (blk >> 1) + 1) * TILE_BYTES + o + 8 * (blk & 1);
-    *reinterpret_cast<uint2*>(sb + lo) = make_uint2(x.x, x.y);
-    *reinterpret_cast<uint2*>(sb + lo + 2 * TILE_BYTES) = make_uint2(x.z, x.w);
+    lds_st8(sb + lo, x.x, x.y);
+    lds_st8(sb + lo + 2 * TILE_BYTES, x.z, x.w);
   };
   // stage s from the staging registers into its LDS buffer; V goes in as
   // f16 when P.V runs on f16 operands (H), where a bf16 V element with no
   // f16 equal becomes an f16 infinity or NaN
   auto lstore = [&](int s, auto h) {
     constexpr bool H = decltype(h)::value;
-    unsigned char* sb = lds + (s % NBUF) * STAGE_BYTES;
+    lds_u8* sb = lbase(s, PAIRED ? run_off(0) : 2 * run_off(0));
     if constexpr (PAIRED) {
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         uint4 x0 = st[2 * i], x1 = st[2 * i + 1];
         const int blk = run_blk(2 * i);  // the pair's first block
-        const int o = run_off(2 * i) + lane * 16;
+        const int o = run_off(2 * i) - run_off(0);
         if (slot_v(i)) {
           if constexpr (H) {
             x0 = make_uint4(bf16x2_to_f16x2(x0.x), bf16x2_to_f16x2(x0.y), bf16x2_to_f16x2(x0.z),
@@ -338,11 +374,11 @@ void prefill_bf16_kernel(PrefillArgs a) {
           }
           // the pair's operand halves: low 8 bytes of both into block 2p's
           // slot, high 8 bytes of both into block 2p + 1's
-          *reinterpret_cast<uint4*>(sb + (2 * blk + 1) * TILE_BYTES + o) = make_uint4(x0.x, x0.y, x1.x, x1.y);
-          *reinterpret_cast<uint4*>(sb + (2 * blk + 3) * TILE_BYTES + o) = make_uint4(x0.z, x0.w, x1.z, x1.w);
+          lds_st16(sb + (2 * blk + 1) * TILE_BYTES + o, make_uint4(x0.x, x0.y, x1.x, x1.y));
+          lds_st16(sb + (2 * blk + 3) * TILE_BYTES + o, make_uint4(x0.z, x0.w, x1.z, x1.w));
         } else {
-          *reinterpret_cast<uint4*>(sb + (2 * blk) * TILE_BYTES + o) = x0;
-          *reinterpret_cast<uint4*>(sb + (2 * blk + 2) * TILE_BYTES + o) = x1;
+          lds_st16(sb + (2 * blk) * TILE_BYTES + o, x0);
+          lds_st16(sb + (2 * blk + 2) * TILE_BYTES + o, x1);
         }
       }
     } else {
@@ -352,15 +388,15 @@ void prefill_bf16_kernel(PrefillArgs a) {
         // lane (E4M3 values are exact in both bf16 and f16)
         const uint4 w = st[u];
         const int blk = run_blk(u);
-        const int o = 2 * run_off(u) + lane * 16;
+        const int o = 2 * (run_off(u) - run_off(0));
         if (run_v(u)) {
           const uint4 x = H ? e4m3x8_to_f16x8(w.x, w.y) : e4m3x8_to_bf16x8(w.x, w.y);
           const uint4 y = H ? e4m3x8_to_f16x8(w.z, w.w) : e4m3x8_to_bf16x8(w.z, w.w);
           vstore(sb, blk, o, x);
           vstore(sb, blk, o + 1024, y);
         } else {
-          *reinterpret_cast<uint4*>(sb + 2 * blk * TILE_BYTES + o) = e4m3x8_to_bf16x8(w.x, w.y);
-          *reinterpret_cast<uint4*>(sb + 2 * blk * TILE_BYTES + o + 1024) = e4m3x8_to_bf16x8(w.z, w.w);
+          lds_st16(sb + 2 * blk * TILE_BYTES + o, e4m3x8_to_bf16x8(w.x, w.y));
+          lds_st16(sb + 2 * blk * TILE_BYTES + o + 1024, e4m3x8_to_bf16x8(w.z, w.w));
         }
       }
     }
@@ -401,13 +437,13 @@ void prefill_bf16_kernel(PrefillArgs a) {
   // K tiles 4q and 4q + 2 of the stage's buffer, V (in operand order)
   // tiles 4q + 1 and 4q + 3.  Its scores: S^T tiles per column tile and block.
   typedef f32x4 Scores[NQ][2];
-  auto qk = [&](const unsigned char* kb, Scores& S) {
+  auto qk = [&](const lds_u8* kb, Scores& S) {
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       bf16x8 kx[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        kx[j] = *reinterpret_cast<const bf16x8*>(kb + 2 * bb * TILE_BYTES + 1024 * j + lane * 16);
+        kx[j] = __builtin_bit_cast(bf16x8, lds_ld16(kb + 2 * bb * TILE_BYTES + 1024 * j));
 #pragma unroll
       for (int t = 0; t < NQ; ++t) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -497,13 +533,13 @@ void prefill_bf16_kernel(PrefillArgs a) {
   };
   // O += P . V over a pair (vb: the pair's first V tile slot); each V piece
   // is read once and used by all column tiles
-  auto pv = [&](const unsigned char* vb, const uint32_t (&ph)[NQ][4], const uint32_t (&pl)[NQ][4],
+  auto pv = [&](const lds_u8* vb, const uint32_t (&ph)[NQ][4], const uint32_t (&pl)[NQ][4],
                 auto h) {
     constexpr bool H = decltype(h)::value;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const uint4 vl = *reinterpret_cast<const uint4*>(vb + 1024 * j + lane * 16);
-      const uint4 vh = *reinterpret_cast<const uint4*>(vb + 2 * TILE_BYTES + 1024 * j + lane * 16);
+      const uint4 vl = lds_ld16(vb + 1024 * j);
+      const uint4 vh = lds_ld16(vb + 2 * TILE_BYTES + 1024 * j);
 #pragma unroll
       for (int t = 0; t < NQ; ++t) {
         if constexpr (H) {
@@ -542,8 +578,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
   // P.V, the first among the staging of stage s + 2 and the loads of stage
   // s + 3.  S0, S1 hold the scores of stage s on entry, of stage s + 1 on exit.
   auto stage = [&](int s, Scores& S0, Scores& S1, auto h) {
-    const unsigned char* cur = lds + (s % NBUF) * STAGE_BYTES;
-    const unsigned char* nxt = lds + ((s + 1) % NBUF) * STAGE_BYTES;
+    const lds_u8* cur = lbase(s, 0);
+    const lds_u8* nxt = lbase(s + 1, 0);
     const int tb0 = (i0 + SB * s) * kBlock;
     // masks are needed only where the stage reaches past the tile's first
     // position (causal) or before its last column's window start
@@ -576,6 +612,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
       m[t] = -1e30f;
       lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    idq = idload(0);
     gload(0);
     vmask(0);
     lstore(0, h);
@@ -585,8 +622,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
     gload(2);
     __syncthreads();
     Scores S0, S1;
-    qk(lds, S0);
-    qk(lds + 4 * TILE_BYTES, S1);
+    qk(lbase(0, 0), S0);
+    qk(lbase(0, 0) + 4 * TILE_BYTES, S1);
     for (int s = 0; s < nst; ++s) {
       if (s) __syncthreads();
       stage(s, S0, S1, h);
