@@ -571,12 +571,14 @@ void prefill_bf16_kernel(PrefillArgs a) {
     }
   };
 
-  // One stage, software-pipelined: the masks and max of its scores (both
-  // pairs, computed during the previous stage), then per pair its weights
-  // with the scores of the same pair of stage s + 1 issued among them (the
-  // products run on the matrix cores while the vector unit works), then its
-  // P.V, the first among the staging of stage s + 2 and the loads of stage
-  // s + 3.  S0, S1 hold the scores of stage s on entry, of stage s + 1 on exit.
+  // One stage, software-pipelined: stage s + 2 from the staging registers
+  // into its LDS buffer (its loads went out a stage earlier), the masks and
+  // max of stage s's scores (both pairs, computed during the previous
+  // stage), then per pair its weights with the scores of the same pair of
+  // stage s + 1 issued among them (the products run on the matrix cores
+  // while the vector unit works), then its P.V, the first among the loads of
+  // stage s + 3.  S0, S1 hold the scores of stage s on entry, of stage s + 1
+  // on exit.
   auto stage = [&](int s, Scores& S0, Scores& S1, auto h) {
     const lds_u8* cur = lbase(s, 0);
     const lds_u8* nxt = lbase(s + 1, 0);
@@ -585,12 +587,12 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // position (causal) or before its last column's window start
     const bool edge = tb0 + SB * kBlock - 1 > p_first || (WIN && tb0 < p_last - a.window + 1);
     uint32_t ph[NQ][4], pl[NQ][4];
-    smax(S0, S1, tb0, edge);
     vmask(s + 2);
+    lstore(s + 2, h);
+    smax(S0, S1, tb0, edge);
     sexp(S0, ph, pl, h);
     qk(nxt, S0);
     pv(cur + TILE_BYTES, ph, pl, h);
-    lstore(s + 2, h);
     gload(s + 3);
     sexp(S1, ph, pl, h);
     qk(nxt + 4 * TILE_BYTES, S1);
@@ -599,11 +601,11 @@ void prefill_bf16_kernel(PrefillArgs a) {
 
   // Stage s is in LDS buffer s % 3.  The barrier at the top of stage s
   // makes stage s + 1 visible (written during stage s - 1; its scores are
-  // taken during stage s) and frees buffer (s + 2) % 3
-  // (every wavefront is done with stage s - 1), which takes stage s + 2
-  // from the staging registers during the stage; stage s + 3's loads go out
-  // after it.  Stages past the end load nothing and are stored as zeros
-  // into buffers no wavefront is reading.
+  // taken during stage s) and frees buffer (s + 2) % 3 (every wavefront is
+  // done with stage s - 1), which takes stage s + 2 from the staging
+  // registers at the start of the stage; stage s + 3's loads go out after
+  // the first pair's P.V.  Stages past the end load nothing and are stored
+  // as zeros into buffers no wavefront is reading.
   auto run = [&](auto h) {
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
