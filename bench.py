@@ -386,7 +386,8 @@ def prefill_measure(dev, reps: int = 20, cache: str = "bf16"):
     return {"workload": "8 sequences x 512-token chunks on 1024..2048 cached tokens, 32 q / 8 kv heads, "
                         "head_dim 128, " + ("FP8 E4M3 cache" if f8 else "bf16"),
             "kernel": f"prefill_bf16_kernel<128,false,4{',F8' if f8 else ''}> (8 wavefronts, 256 score "
-                      "columns, 4-block K/V stages in LDS, P.V on f16" + (", codes expanded on the way in)"
+                      "columns, 4-block K/V stages in three LDS buffers, the next stage's scores issued "
+                      "among this stage's exponentials, P.V on f16" + (", codes expanded on the way in)"
                                                             if f8 else ")"),
             "ms": round(ms, 4),
             "tflops": round(tflops, 2), "bound": "mfma", "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
