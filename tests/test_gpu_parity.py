@@ -307,11 +307,48 @@ def test_prefill_chunks_vs_oracle(Hq, Hkv, D, seed):
         assert np.max(np.abs(dout[b] - got[qstart[b]])) <= 2e-3
 
 
-@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+@pytest.mark.parametrize("W", [0, 1000])
+def test_prefill_long_context_vs_oracle(W):
+    """Chunks over contexts of 5-8 K tokens (a hundred and more pipeline
+    stages per query tile, the block ids of each stage read one stage
+    ahead), chunk lengths that leave ragged last tiles, with and without a
+    sliding window that starts the walk deep into the context: every chunk
+    row against the oracle."""
+    from oracle import attention as oatt
+    from oracle.slots import plan_append
+    from tests.gpu_parity import to_device
+    Hq, Hkv, D, B = 8, 2, 128, 3
+    w = synth.small_random(171, num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           dtype="bf16", max_len=8192, min_len=5000, append=300)
+    p = _pair(w)
+    rng = np.random.default_rng(171)
+    counts = np.array([300, 65, 1], np.int64)
+    T = int(counts.sum())
+    k_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    v_new = synth.round_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    q = synth.round_bf16_bits(rng.standard_normal((T, Hq, D)).astype(np.float32))
+    slots, _, cows = plan_append(p.ora.pool, p.ora.tables, p.ora.lens, counts)
+    p.ora.cache.copy_blocks(cows)
+    p.ora.cache.write(k_new, v_new, slots)
+    p.kv.append(to_device(k_new), to_device(v_new), counts.astype(np.int32))
+    p.check_state()
+    qstart = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    print(f"[prefill long] W={W} lens={p.ora.lens.tolist()} counts={counts.tolist()}", flush=True)
+    p.kv.window = W
+    got = p.kv.prefill_attention(to_device(q), qstart, w.spec.scale).cpu().numpy()
+    exp = oatt.prefill(q, p.ora.cache, p.ora.tables, p.ora.lens, qstart, Hq, Hkv, w.spec.scale,
+                       window=W)
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got.astype(np.float64) - exp)))
+    assert err <= 2e-3, f"max abs error {err:.3e}"
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1e-39, 2.5])
 def test_scales_vs_oracle(scale):
     """The softmax scale is any real: a negative one (the prefill negates Q
-    instead), zero (every visible position weighs the same) and a large one,
-    through decode (every split form) and prefill, against the oracle."""
+    instead), zero and a subnormal one (every visible position weighs the
+    same; the prefill takes both as the smallest normal float) and a large
+    one, through decode (every split form) and prefill, against the oracle."""
     from oracle import attention as oatt
     from oracle.slots import plan_append
     from tests.gpu_parity import to_device
