@@ -30,9 +30,10 @@ namespace {
 // positions), two per SIMD.  The tile's score columns are (position,
 // head-in-group) pairs, 256 of them (32 per wavefront, as two 16-column MFMA
 // tiles), so 256 / g positions per tile.  The K and V tiles of SB consecutive
-// blocks (one stage) are loaded once per workgroup into LDS (double-buffered,
-// the next stage's global loads in flight during this stage's compute) and
-// every wavefront reads them from there:
+// blocks (one stage) are moved once per workgroup into LDS (three buffers:
+// the stage being processed, the next one, whose scores are computed during
+// this one, and the one after, being filled) and every wavefront reads them
+// from there:
 //   S^T = K . Q^T   v_mfma_f32_16x16x32_bf16, A = K piece j (16 tokens x 32
 //                   channels, the cache's lane order), B = Q^T chunk j;
 //   O  += P . V     v_mfma_f32_16x16x32_f16 over each pair of blocks (32
@@ -42,10 +43,10 @@ namespace {
 //                   tile's lane pieces of the two blocks;
 // with P and V as f16 (V converted on its way into LDS; a bf16 V element
 // beyond f16's range makes the workgroup run again with P as a bf16 high
-// part plus residual and V as bf16).  The running max
-// is raised only when a block's max exceeds it by more than 2^8 (the
-// normaliser uses the same reference, so the result is unchanged, and the
-// accumulator is rescaled rarely).
+// part plus residual and V as bf16).  The running max is raised only when a
+// stage's max exceeds it by more than 2^8 (the normaliser uses the same
+// reference, so the result is unchanged, and the accumulator is rescaled
+// rarely).
 struct PrefillArgs {
   const void* q;          // [T][Hq][D] bf16, T = qstart[B]
   const void* kc;
