@@ -45,12 +45,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the code the decode kernels are built from: their sources with
-    comments removed and whitespace runs collapsed (a change of wording in a
-    comment leaves the kernels, and their counters, as they were)."""
+def kernel_source_hash(names=("kernels.hip", "device_common.h")) -> str:
+    """Hash of the code kernels are built from (by default the decode
+    kernels'; the prefill's are prefill.hip and device_common.h): the sources
+    with comments removed and whitespace runs collapsed (a change of wording
+    in a comment leaves the kernels, and their counters, as they were)."""
     h = hashlib.sha256()
-    for name in ("kernels.hip", "device_common.h"):
+    for name in names:
         text = open(os.path.join(ROOT, "paged_kv_cache_102_amd", "csrc", name)).read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
