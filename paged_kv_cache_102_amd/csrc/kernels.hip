@@ -1737,13 +1737,25 @@ void decode_bf16_cu_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ A5: decode, fp32
-// One wave per (sequence, query head, partition); lane holds channels lane
-// and lane + 64.  Plain vector-ALU form for the fp32 cache.
+// One wave per (sequence, query head, partition), a block (16 tokens) per
+// step, the next block's id and K/V loads in flight during this one.
+// Scores: lane (t, c) = (lane % 16, lane / 16) takes token t's dot product
+// over the channel quarter c (D / 4 channels: runs of 8 in the tile order),
+// the four quarters summed across lanes.  The block's max and weight sum are
+// reductions over the 16 token lanes; the running max and normaliser are
+// the online softmax applied once per block.  P.V: lane = channel (and
+// channel + 64), its V values of the block are 4 runs of 4 tokens in the
+// tile order, each weight read from its token's lane.  Plain vector-ALU
+// form for the fp32 cache.
 template <int D>
 __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
-  constexpr int NE = D / 64;
+  constexpr int NE = D / 64;     // output channels per lane
+  constexpr int CQ = D / 4;      // channels per score lane
+  constexpr int NR = CQ / 8;     // runs of 8 channels per score lane
   constexpr int64_t TILE = int64_t(kBlock) * D;
   const int lane = threadIdx.x;
+  const int tok = lane & 15;
+  const int cq = lane >> 4;
   const int64_t wid = blockIdx.x;  // query head fastest, then sequence, then partition
   const int hq = static_cast<int>(wid % a.num_q_heads);
   const int b = static_cast<int>((wid / a.num_q_heads) % a.num_seqs);
@@ -1763,41 +1775,94 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
   const int base = wlo / kBlock * kBlock;
   const int nparts = (L - base + a.part_tokens - 1) / a.part_tokens;
   if (part >= nparts) return;
-  const int t_begin = base + part * a.part_tokens;
-  const int t_end = min(L, t_begin + a.part_tokens);
+  const int t_lo = max(base + part * a.part_tokens, wlo);  // visible positions [t_lo, t_hi)
+  const int t_hi = min(L, base + part * a.part_tokens + a.part_tokens);
+  const int blk0 = t_lo / kBlock, blk1 = (t_hi - 1) / kBlock;  // blocks visited
   const int32_t* row = a.tables + int64_t(b) * a.max_blocks;
   const float* q = static_cast<const float*>(a.q) + head * D;
   const float* kc = static_cast<const float*>(a.kc) + kvh * TILE;
   const float* vc = static_cast<const float*>(a.vc) + kvh * TILE;
   const int64_t block_stride = int64_t(a.num_kv_heads) * TILE;
-  float qv[NE], acc[NE];
+  // this lane's query channels: runs 8 (NR cq + r) .. + 8
+  float qv[CQ];
 #pragma unroll
-  for (int e = 0; e < NE; ++e) {
-    qv[e] = q[lane + 64 * e];
-    acc[e] = 0.f;
-  }
-  float m = -INFINITY, lsum = 0.f;
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[8 * r + i] = q[8 * (NR * cq + r) + i];
+  // the K and V values of a block this lane needs
+  struct Blk {
+    float k[CQ];
+    float4 v[NE][4];
+  };
   bool bad = false;
-  for (int t = max(t_begin, wlo); t < t_end; ++t) {
-    int phys = __builtin_amdgcn_readfirstlane(row[t / kBlock]);
+  auto load = [&](int blk, Blk& x) {
+    int phys = __builtin_amdgcn_readfirstlane(row[blk]);
     if (phys < 0 || phys >= a.num_blocks) {
       bad = true;
       phys = 0;
     }
     const float* kt = kc + int64_t(phys) * block_stride;
     const float* vt = vc + int64_t(phys) * block_stride;
-    const int slot = t % kBlock;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {  // K (t, d) at (d / 8) 128 + 8 t + d % 8
+      const float4* kp = reinterpret_cast<const float4*>(kt + (NR * cq + r) * 128 + tok * 8);
+      const float4 k0 = kp[0], k1 = kp[1];
+      x.k[8 * r + 0] = k0.x; x.k[8 * r + 1] = k0.y; x.k[8 * r + 2] = k0.z; x.k[8 * r + 3] = k0.w;
+      x.k[8 * r + 4] = k1.x; x.k[8 * r + 5] = k1.y; x.k[8 * r + 6] = k1.z; x.k[8 * r + 7] = k1.w;
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {  // V (t, d) at (d / 32) 512 + (t / 4) 128 + v_elem's lane part
+      const int d = lane + 64 * e;
+      const float* vd = vt + v_elem(0, d);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) x.v[e][g4] = *reinterpret_cast<const float4*>(vd + 128 * g4);
+    }
+  };
+  float acc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
+  Blk cur, nxt;
+  load(blk0, cur);
+  for (int blk = blk0; blk <= blk1; ++blk) {
+    if (blk < blk1) load(blk + 1, nxt);
     float part_dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) part_dot = fmaf(qv[e], kt[k_elem(slot, lane + 64 * e)], part_dot);
-    const float s = wave_sum(part_dot) * a.scale_log2e;
-    const float mnew = fmaxf(m, s);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    const float p = __builtin_amdgcn_exp2f(s - mnew);
-    lsum = lsum * alpha + p;
+    for (int i = 0; i < CQ; ++i) part_dot = fmaf(qv[i], cur.k[i], part_dot);
+    part_dot += __shfl_xor(part_dot, 16);
+    part_dot += __shfl_xor(part_dot, 32);
+    const int tp = blk * kBlock + tok;
+    const float sc = (tp >= t_lo && tp < t_hi) ? part_dot * a.scale_log2e : -INFINITY;
+    float bmax = sc;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) acc[e] = fmaf(p, vt[v_elem(slot, lane + 64 * e)], acc[e] * alpha);
+    for (int x = 1; x < 16; x <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, x));
+    // every visited block holds a visible position, so the block max is finite
+    const float mnew = fmaxf(m, bmax);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    const float p = __builtin_amdgcn_exp2f(sc - mnew);
+    float psum = p;
+#pragma unroll
+    for (int x = 1; x < 16; x <<= 1) psum += __shfl_xor(psum, x);
+    lsum = lsum * alpha + psum;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      float o = acc[e] * alpha;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        // invisible positions have weight 0, but their V slots may hold NaN
+        const float4 v = cur.v[e][g4];
+        const float w0 = __shfl(p, 4 * g4 + 0), w1 = __shfl(p, 4 * g4 + 1);
+        const float w2 = __shfl(p, 4 * g4 + 2), w3 = __shfl(p, 4 * g4 + 3);
+        const int t0 = blk * kBlock + 4 * g4;
+        o = (t0 + 0 >= t_lo && t0 + 0 < t_hi) ? fmaf(w0, v.x, o) : o;
+        o = (t0 + 1 >= t_lo && t0 + 1 < t_hi) ? fmaf(w1, v.y, o) : o;
+        o = (t0 + 2 >= t_lo && t0 + 2 < t_hi) ? fmaf(w2, v.z, o) : o;
+        o = (t0 + 3 >= t_lo && t0 + 3 < t_hi) ? fmaf(w3, v.w, o) : o;
+      }
+      acc[e] = o;
+    }
     m = mnew;
+    if (blk < blk1) cur = nxt;
   }
   if (nparts == 1) {
     const float inv = bad ? __builtin_nanf("") : 1.0f / lsum;
@@ -1814,13 +1879,6 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ A6: LSE reduce
-// One wave per (sequence, query head) merging its partitions:
-//   M = max_p m_p,  l = sum_p l_p 2^(m_p - M),  out = sum_p o_p 2^(m_p - M) / l
-// The maximum and the normaliser are reduced over the lanes (partition p on
-// lane p % 64); the output sum walks the partitions with lane l holding
-// channels l + 64 k, so each partition's D values are read in coalesced
-// 256-byte rows and the loads of several partitions are in flight at once.
 template <int D>
 __global__ __launch_bounds__(64) void lse_reduce_kernel(DecodeArgs a) {
   // one wavefront per (sequence, query head): lane l holds channels l + 64 k
