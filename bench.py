@@ -714,6 +714,7 @@ def main():
     bytes_total = bytes_prof = 0
     capi.pkv_profile_begin(PROFILE_EVERY)
     torch.cuda.synchronize()
+    wait0 = kv._staging.wait_s if kv._staging is not None else 0.0
     t0 = time.perf_counter()
     for i in range(steps):
         step()
@@ -722,6 +723,7 @@ def main():
         if i % PROFILE_EVERY == 0:
             bytes_prof += b
     t_issued = time.perf_counter()
+    host_wait = (kv._staging.wait_s if kv._staging is not None else 0.0) - wait0
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     nlaunch, kern_ms = capi.pkv_profile_end()
@@ -823,6 +825,10 @@ def main():
         "decode_only": dec,
         "fused_step": fused,
         "host_issue_ms_per_step": round((t_issued - t0) * 1e3 / steps, 4),
+        # of which the host waited for a staging buffer (the ring holds 16 steps'
+        # inputs, so a host ahead of the GPU waits there); the rest is planning,
+        # packing and the launches themselves
+        "host_wait_ms_per_step": round(host_wait * 1e3 / steps, 4),
         "kv_waste_fraction": round(waste, 5),
         "pool_usage_percent": round(stats["usage_percent"], 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -27,6 +27,8 @@ Every step runs in libpagedkv; this module only moves arguments.
 """
 from __future__ import annotations
 
+import time
+
 import numpy as np
 import torch
 
@@ -54,6 +56,7 @@ class _Staging:
         self.stream = None     # stream of the last release
         self.i = 0
         self.cur = None
+        self.wait_s = 0.0      # host time spent waiting for a buffer's readers
 
     def _cover(self):
         ev = torch.cuda.Event()
@@ -71,7 +74,9 @@ class _Staging:
         if k in self.pending:
             self._cover()
         if self.events[k] is not None:
+            t = time.perf_counter()
             self.events[k].synchronize()
+            self.wait_s += time.perf_counter() - t
             self.events[k] = None
         buf = self.bufs[k]
         host = buf.numpy()
