@@ -285,6 +285,51 @@ def paged_kv_append_slots(pool: Pool, block_tables: np.ndarray, context_lens: np
     return slots[:total], upd[:nu.value], cows[:nc.value]
 
 
+
+class AppendPlanner:
+    """paged_kv_append_slots bound once to a pool and to host tables and
+    lengths (int32 [B][max_blocks] and [B], updated in place and never
+    reallocated), with output buffers kept between calls: per call only the
+    counts of new tokens are converted.  Returns what paged_kv_append_slots
+    returns, as arrays of the caller's own."""
+
+    def __init__(self, pool: Pool, block_tables: np.ndarray, context_lens: np.ndarray):
+        assert block_tables.dtype == np.int32 and block_tables.flags.c_contiguous
+        assert context_lens.dtype == np.int32 and context_lens.flags.c_contiguous
+        self._pool, self._tables, self._lens = pool, block_tables, context_lens
+        self._B, self._mb = block_tables.shape
+        self._tp = block_tables.ctypes.data_as(_i32p)
+        self._lp = context_lens.ctypes.data_as(_i32p)
+        self._nn = np.ones(self._B, dtype=np.int32)
+        self._nnp = self._nn.ctypes.data_as(_i32p)
+        self._cows = np.empty((max(self._B, 1), 2), dtype=np.int32)
+        self._cp = self._cows.ctypes.data_as(_i32p)
+        self._nu, self._nc = C.c_int32(), C.c_int32()
+        self._nur, self._ncr = C.byref(self._nu), C.byref(self._nc)
+        self._fn = _lib.paged_kv_append_slots
+        self._grow(self._B)
+
+    def _grow(self, total: int):
+        self._cap = total
+        self._slots = np.empty(max(total, 1), dtype=np.int64)
+        self._sp = self._slots.ctypes.data_as(_i64p)
+        self._upd = np.empty((total + self._B, 2), dtype=np.int32)
+        self._up = self._upd.ctypes.data_as(_i32p)
+
+    def __call__(self, num_new=None):
+        if num_new is None:
+            nn_ptr, total = None, self._B
+        else:
+            self._nn[:] = num_new
+            nn_ptr, total = self._nnp, int(self._nn.sum())
+        if total > self._cap:
+            self._grow(total)
+        _check(self._fn(self._pool.handle, self._B, self._mb, self._tp, self._lp, nn_ptr, self._sp,
+                        total, self._up, self._upd.shape[0], self._nur, self._cp, self._B,
+                        self._ncr), "paged_kv_append_slots")
+        return (self._slots[:total].copy(), self._upd[:self._nu.value].copy(),
+                self._cows[:self._nc.value].copy())
+
 # --------------------------------------------------------------------------- device calls
 def _stream(stream):
     if stream is not None:

@@ -50,6 +50,11 @@ class _Staging:
     def __init__(self, nbytes: int, depth: int = 16, every: int = 8):
         assert 0 < every < depth
         self.bufs = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(depth)]
+        # each buffer seen as int64 and int32 (pieces start at multiples of 8 bytes),
+        # and as numpy bytes, made once
+        self._typed = [{np.dtype(np.int64): b.view(torch.int64), np.dtype(np.int32): b.view(torch.int32)}
+                       for b in self.bufs]
+        self._host = [b.numpy() for b in self.bufs]
         self.events = [None] * depth
         self.every = every
         self.pending = []      # released buffers no event covers yet
@@ -78,15 +83,14 @@ class _Staging:
             self.events[k].synchronize()
             self.wait_s += time.perf_counter() - t
             self.events[k] = None
-        buf = self.bufs[k]
-        host = buf.numpy()
+        host, typed = self._host[k], self._typed[k]
         views, off = [], 0
         for a in arrays:
             n = a.nbytes
             host[off:off + n] = np.ascontiguousarray(a).view(np.uint8).ravel()
-            dt = {np.dtype(np.int64): torch.int64, np.dtype(np.int32): torch.int32}[a.dtype]
-            t = buf[off:off + n].view(dt)
-            views.append(t.view(*a.shape) if a.size else t)
+            isz = a.dtype.itemsize
+            t = typed[a.dtype][off // isz:(off + n) // isz]
+            views.append(t.view(*a.shape) if a.ndim > 1 and a.size else t)
             off += (n + 7) & ~7
         self.cur = k
         return views
@@ -139,6 +143,8 @@ class PagedKV:
             self.v_cache.fill_(fill)
         self.tables = np.full((num_seqs, max_blocks_per_seq), -1, dtype=np.int32)
         self.lens = np.zeros(num_seqs, dtype=np.int32)
+        # the slot planner, bound to these two arrays (changed only in place)
+        self._plan = capi.AppendPlanner(self.pool, self.tables, self.lens)
         # device tables and lengths share one int32 buffer, so that a step's
         # length changes travel as table deltas at flat index S*mb + s; the
         # lengths have two copies, the current one and the one a fused step
@@ -149,6 +155,7 @@ class PagedKV:
         self.state_d = torch.empty(nt + 2 * num_seqs, dtype=torch.int32, device=self.device)
         self.tables_d = self.state_d[:nt].view(num_seqs, max_blocks_per_seq)
         self._cur = 0
+        self._lens_views = [self.state_d[nt + c * num_seqs:nt + (c + 1) * num_seqs] for c in (0, 1)]
         self.tables_d.copy_(torch.from_numpy(self.tables))
         self.lens_d.copy_(torch.from_numpy(self.lens))
         ws = capi.paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
@@ -162,8 +169,7 @@ class PagedKV:
     @property
     def lens_d(self):
         """The device context lengths currently in use (int32 [num_seqs])."""
-        nt = self.tables.size
-        return self.state_d[nt + self._cur * self.num_seqs:nt + (self._cur + 1) * self.num_seqs]
+        return self._lens_views[self._cur]
 
     # ------------------------------------------------------------------ host helpers
     def _stage(self, arrays):
@@ -197,7 +203,7 @@ class PagedKV:
             # (a sequence with nothing to append: its current length)
             ctx = self.lens + (nn > 0).astype(np.int32)
             rel = capi.pkv_window_release(self.pool, self.tables, ctx, self.window)
-        slots, upd, cows = capi.paged_kv_append_slots(self.pool, self.tables, self.lens, num_new)
+        slots, upd, cows = self._plan(num_new)
         if rel is not None and len(rel):
             upd = np.concatenate([rel, upd]) if len(upd) else rel
         # new lengths of the sequences that grew, as deltas into the state buffer
@@ -236,7 +242,7 @@ class PagedKV:
         rel = None
         if self.window > 0:
             rel = capi.pkv_window_release(self.pool, self.tables, self.lens + nn, self.window)
-        slots, upd, cows = capi.paged_kv_append_slots(self.pool, self.tables, self.lens, nn)
+        slots, upd, cows = self._plan(nn)
         if rel is not None and len(rel):
             upd = np.concatenate([rel, upd]) if len(upd) else rel
         slot_seq = np.full(self.num_seqs, -1, dtype=np.int64)

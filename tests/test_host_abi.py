@@ -264,3 +264,39 @@ def test_planner_errors_leave_state():
     assert e.value.status == capi.PKV_ERR_INVALID
     t[1, 0], l[1] = t0[1, 0], l0[1]
     assert np.array_equal(t, t0) and np.array_equal(l, l0) and capi.kv_pool_stats(p) == s0
+
+
+def test_append_planner_matches_wrapper():
+    """The driver's bound planner (capi.AppendPlanner) gives what the plain
+    paged_kv_append_slots call gives, errors included, on two pools fed the
+    same stream of appends and frees."""
+    rng = np.random.default_rng(5)
+    B, mb, nb = 6, 40, 200
+    pa, pb = capi.pkv_pool_create(nb, 16, None), capi.pkv_pool_create(nb, 16, None)
+    ta = np.full((B, mb), -1, np.int32)
+    la = np.zeros(B, np.int32)
+    tb, lb = ta.copy(), la.copy()
+    plan = capi.AppendPlanner(pb, tb, lb)
+    errors = 0
+    for it in range(300):
+        nn = rng.integers(0, 9, B).astype(np.int32) if it % 3 else None
+        if it % 50 == 49:
+            for s in range(B):
+                if rng.random() < 0.5:
+                    capi.kv_block_free(pa, ta[s][ta[s] >= 0])
+                    capi.kv_block_free(pb, tb[s][tb[s] >= 0])
+                    ta[s], la[s], tb[s], lb[s] = -1, 0, -1, 0
+        try:
+            ra = capi.paged_kv_append_slots(pa, ta, la, nn)
+        except capi.PkvError as e:
+            errors += 1
+            with pytest.raises(capi.PkvError) as e2:
+                plan(nn)
+            assert e2.value.args == e.args
+            continue
+        rb = plan(nn)
+        for x, y in zip(ra, rb):
+            assert x.dtype == y.dtype and x.shape == y.shape and np.array_equal(x, y)
+        np.testing.assert_array_equal(ta, tb)
+        np.testing.assert_array_equal(la, lb)
+    assert errors > 0  # the stream reaches the pool's end, so the error path is covered
